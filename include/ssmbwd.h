@@ -1,0 +1,174 @@
+/*
+ * ssmbwd.h — C ABI of the MI355X (gfx950) selective-scan backward library.
+ *
+ * Operations are those of the Mamba layer backward walked by mamba-rs 0.5.1
+ * (src/mamba_ssm/cpu/backward.rs, backward_mamba_layer_batched), with the
+ * closed-form RMSNorm backward of rlx-cpu 0.2.17 (src/training_bwd.rs,
+ * rms_norm_backward_row).  The CPU page runs them as sequential loops over one
+ * sequence; here every call is a batch of sequences on one GPU.
+ *
+ * Conventions for every entry point
+ *  - Memory: all tensor pointers are DEVICE pointers to contiguous row-major
+ *    storage owned by the caller.  The library never allocates or frees device
+ *    memory; scratch space is a caller-provided workspace whose size the
+ *    matching *_workspace_size() call returns.  Gradients are OVERWRITTEN, not
+ *    accumulated.
+ *  - Storage dtype: [batch, seqlen, *] activations and their gradients are
+ *    SSM_F32 (float) or SSM_BF16 (bfloat16, round-to-nearest-even on store).
+ *    Parameters (A_log, D, conv weight and bias, norm weight) and their
+ *    gradients are always float.  Arithmetic is float32 throughout.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream).  Calls are asynchronous on that stream: no host synchronisation,
+ *    no hidden allocation.
+ *  - Errors: arguments are checked before anything is launched; a bad call
+ *    returns a non-zero ssm_status and leaves every output untouched.  A
+ *    failed launch returns SSM_ERR_LAUNCH.  ssm_last_error() gives a message
+ *    for the calling thread's last failure.
+ *  - Results are deterministic: no atomics; every reduction has a fixed order,
+ *    so two calls with the same inputs and dims give bitwise equal outputs.
+ *  - Thread safety: calls on different streams may run concurrently as long
+ *    as they do not share a workspace.
+ */
+#ifndef SSMBWD_H
+#define SSMBWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent stride */
+  SSM_ERR_UNSUPPORTED = 2,  /* e.g. d_state outside {4, 8, 16}, misaligned bf16 rows */
+  SSM_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
+  SSM_ERR_LAUNCH = 4        /* a kernel launch failed */
+} ssm_status;
+
+typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* Shape of one selective-scan call.
+ *   u, delta, z, d_out, d_u, d_delta, d_z : [batch, seqlen, d_inner]
+ *   B, C                                   : [batch, seqlen, *] rows of stride ld_bc,
+ *                                            the d_state values of step t at row (b*seqlen+t)
+ *   d_B, d_C                               : same, row stride ld_dbc
+ *   A_log, d_A_log                         : [d_inner, d_state] (index d*d_state + n)
+ *   D, d_D                                 : [d_inner]
+ * ld_bc / ld_dbc = d_state for standalone tensors; a larger stride lets B and C
+ * (and their gradients) live inside the x_proj row [dt | B | C] as the layer
+ * keeps them.  For SSM_BF16 the B, C, d_B, d_C base pointers must be 4-byte
+ * aligned and the strides even.
+ * seg_len: length of the time segments that run in parallel and are joined by
+ * the cross-segment carries; 0 picks one from the shape.  Must be 0 or a
+ * multiple of 8.  Results do not depend on it beyond float rounding. */
+typedef struct ssm_dims {
+  int32_t batch;
+  int32_t seqlen;
+  int32_t d_inner;
+  int32_t d_state;
+  int32_t ld_bc;
+  int32_t ld_dbc;
+  int32_t seg_len;
+} ssm_dims;
+
+const char* ssm_status_string(int status);
+const char* ssm_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan_bwd — backward of the selective scan with its output gate.
+ * mamba-rs cpu/backward.rs, Phase B2 (gating backward) and Phase B3
+ * (sequential SSM BPTT), forward as implied by the saved da_exp/h_prev/h_curr:
+ *     A = -exp(A_log),  a_t = exp(delta_t A),  h_t = a_t h_{t-1} + delta_t u_t B_t,
+ *     h_{-1} = 0,  y_t = C_t . h_t + D u_t,  out_t = y_t * SiLU(z_t).
+ * Given d_out = dL/d out it writes dL/du, dL/d delta, dL/d A_log, dL/dB, dL/dC,
+ * dL/dD and dL/dz.  The forward states are recomputed in chunks; no per-step
+ * state is read from or written to memory by the caller.
+ * softplus_epilogue != 0: delta is taken to be softplus(raw) (the layer's
+ * dt_proj output) and d_delta receives dL/d raw instead, using
+ * sigmoid(raw) = 1 - exp(-delta) and passing the gradient through where
+ * delta > 20 (the page's "Softplus backward" step, threshold 20).
+ * All output pointers are required.  Workspace: ssm_scan_bwd_workspace_size().
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan_bwd_workspace_size(const ssm_dims* dims, int dtype);
+int ssm_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B,
+                 const void* C, const float* D, const void* z, const void* d_out,
+                 void* d_u, void* d_delta, float* d_A_log, void* d_B, void* d_C,
+                 float* d_D, void* d_z, int softplus_epilogue,
+                 void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype,
+                 void* stream);
+
+/* Same as ssm_scan_bwd, with stage timing: `stage_events` (nullable) points to
+ * 5 hipEvent_t handles (passed as void*, each may be null) created by the
+ * caller; event k is recorded on `stream` before stage k+1 / after stage k of
+ * the call: [0] start, [1] after the segment summaries, [2] after the carries,
+ * [3] after the main backward sweep, [4] after the final reductions.
+ * For profiling callers (the bench); results are identical to ssm_scan_bwd. */
+int ssm_scan_bwd_timed(const void* u, const void* delta, const float* A_log, const void* B,
+                       const void* C, const float* D, const void* z, const void* d_out,
+                       void* d_u, void* d_delta, float* d_A_log, void* d_B, void* d_C,
+                       float* d_D, void* d_z, int softplus_epilogue,
+                       void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype,
+                       void* stream, void* const* stage_events);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan_fwd — the forward recurrence above (the page's forward is implied
+ * by the states Phase B3 reads back).  Writes y (nullable), out = y * SiLU(z)
+ * (nullable; requires z) and, if h_ckpt is not null, the state before every
+ * ckpt_every-th step: h_ckpt[b, k, n, d] = h_{k*ckpt_every - 1} (zero for k = 0),
+ * k = 0 .. ceil(seqlen / ckpt_every) - 1, float.  ckpt_every must be a multiple
+ * of 8 when h_ckpt is given.  Workspace: ssm_scan_fwd_workspace_size().
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan_fwd_workspace_size(const ssm_dims* dims, int dtype);
+int ssm_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B,
+                 const void* C, const float* D, const void* z, void* y, void* out,
+                 float* h_ckpt, int ckpt_every, void* workspace, size_t ws_bytes,
+                 const ssm_dims* dims, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gating_bwd — Phase B2 on its own: gated = y * SiLU(z);
+ *     d_y = d_out * SiLU(z),  d_z = d_out * y * s * (1 + z (1 - s)),  s = sigmoid(z).
+ * All five tensors hold n elements of the same dtype.  No workspace.
+ * ------------------------------------------------------------------------- */
+int gating_bwd(const void* d_out, const void* y, const void* z, void* d_y, void* d_z,
+               int64_t n, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * conv1d_bwd — Phase B6: SiLU backward on the conv output, then the causal
+ * depthwise conv backward (the page's reverse loop with a shift-register
+ * carry, computed here as a stencil).  Forward (recomputed here):
+ *     c[b,t,d] = bias[d] + sum_k w[d,k] x[b, t-(d_conv-1)+k, d]   (zero before t = 0),
+ *     u = SiLU(c).
+ * d_u is dL/du.  Writes d_x[b,t,d] = sum_k g[b, t+(d_conv-1)-k, d] w[d,k] with
+ * g = d_u * SiLU'(c), d_w[d,k] = sum_{b,t} g[b,t,d] x[b,t-(d_conv-1)+k,d] and
+ * d_bias[d] = sum g.  x, d_u, d_x rows have strides ld_x, ld_du, ld_dx (>= d_inner)
+ * so that x can be the first half of the in_proj output row and d_x the first
+ * half of its gradient.  w [d_inner, d_conv] and bias are float; d_conv <= 8.
+ * Workspace: conv1d_bwd_workspace_size().
+ * ------------------------------------------------------------------------- */
+size_t conv1d_bwd_workspace_size(int batch, int seqlen, int d_inner, int d_conv);
+int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u,
+               void* d_x, float* d_w, float* d_bias, int batch, int seqlen, int d_inner,
+               int d_conv, int ld_x, int ld_du, int ld_dx, void* workspace, size_t ws_bytes,
+               int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * rmsnorm_bwd — rlx-cpu training_bwd.rs rms_norm_backward_row over `rows`
+ * rows of `dim`, without the shift term (Phase B8 of the layer passes only the
+ * norm weight), plus the residual of Phase B8:
+ *     inv_r = 1/sqrt(mean(x^2) + eps)
+ *     dx = inv_r w dy - inv_r^3 x mean(dy w x)  (+ d_residual if not null)
+ *     dw = sum over rows of dy x inv_r
+ * x, dy, d_residual, dx: [rows, dim] in dtype; w, dw: [dim] float.
+ * Workspace: rmsnorm_bwd_workspace_size().
+ * ------------------------------------------------------------------------- */
+size_t rmsnorm_bwd_workspace_size(int64_t rows, int dim);
+int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_residual,
+                void* dx, float* dw, int64_t rows, int dim, float eps, void* workspace,
+                size_t ws_bytes, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSMBWD_H */

@@ -1,0 +1,264 @@
+"""Python binding of the gfx950 selective-scan backward library (``libssmbwd.so``).
+
+Argument marshalling only: every function checks shapes, dtypes and strides,
+allocates outputs and workspace with torch on the tensors' device, and calls the
+C entry point of the same name on torch's current stream.  All arithmetic runs
+in the HIP kernels.  There is no fallback: importing this package fails if the
+library has not been built (``python -m selective_state_space_bwd_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmbwd.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "ssmbwd.h")
+
+_lib = None
+
+SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH = range(5)
+SSM_F32, SSM_BF16 = 0, 1
+
+
+class ssm_dims(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("batch", "seqlen", "d_inner", "d_state", "ld_bc", "ld_dbc", "seg_len")]
+
+
+_vp, _fp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+_dims_p = ctypes.POINTER(ssm_dims)
+
+_SIGS = {
+    "ssm_status_string": (ctypes.c_char_p, [_i]),
+    "ssm_last_error": (ctypes.c_char_p, []),
+    "ssm_scan_bwd_workspace_size": (_sz, [_dims_p, _i]),
+    "ssm_scan_bwd": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _i,
+                          _vp, _sz, _dims_p, _i, _vp]),
+    "ssm_scan_bwd_timed": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _i,
+                                _vp, _sz, _dims_p, _i, _vp, ctypes.POINTER(ctypes.c_void_p)]),
+    "ssm_scan_fwd_workspace_size": (_sz, [_dims_p, _i]),
+    "ssm_scan_fwd": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _i, _vp, _sz, _dims_p, _i, _vp]),
+    "gating_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _vp]),
+    "conv1d_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "conv1d_bwd": (_i, [_vp, _fp, _fp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
+    "rmsnorm_bwd_workspace_size": (_sz, [_i64, _i]),
+    "rmsnorm_bwd": (_i, [_vp, _fp, _vp, _vp, _vp, _fp, _i64, _i, ctypes.c_float, _vp, _sz, _i, _vp]),
+}
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m selective_state_space_bwd_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_symbols() -> list:
+    """Function names the C header declares (used to check the library's exports)."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|int)\s+(\w+)\s*\(", text, re.M)))
+
+
+class SsmError(RuntimeError):
+    def __init__(self, where: str, status: int):
+        self.status = status
+        msg = lib().ssm_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib().ssm_status_string(status).decode()} ({status}): {msg}")
+
+
+def _check(where: str, rc: int):
+    if rc != SSM_OK:
+        raise SsmError(where, rc)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"storage dtype {t.dtype} not supported (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _row_stride(x: torch.Tensor, batch: int, seqlen: int, n: int, name: str) -> int:
+    """B / C may be [B, T, N] views into a wider row (e.g. the x_proj output)."""
+    _need(x.dim() == 3 and tuple(x.shape) == (batch, seqlen, n), f"{name} must be [{batch}, {seqlen}, {n}]")
+    _need(x.stride(2) == 1, f"{name} must be contiguous in its last dim")
+    ld = x.stride(1) if seqlen > 1 else max(x.stride(1), n)
+    _need(batch <= 1 or x.stride(0) == seqlen * ld, f"{name}: rows must be evenly strided")
+    return ld
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        _need(workspace.device == device and workspace.numel() * workspace.element_size() >= nbytes,
+              f"workspace needs {nbytes} bytes on {device}")
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def scan_dims(u, B, d_state=None, seg_len=0, ld_dbc=None) -> ssm_dims:
+    batch, seqlen, d_inner = u.shape
+    n = d_state if d_state is not None else B.shape[2]
+    ld = _row_stride(B, batch, seqlen, n, "B")
+    return ssm_dims(batch, seqlen, d_inner, n, ld, ld_dbc if ld_dbc is not None else n, seg_len)
+
+
+def ssm_scan_bwd_workspace_size(dims: ssm_dims, dtype: torch.dtype) -> int:
+    return int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(dims), SSM_F32 if dtype == torch.float32 else SSM_BF16))
+
+
+def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool = False, seg_len: int = 0,
+                 out: dict | None = None, workspace: torch.Tensor | None = None, stage_events=None) -> dict:
+    """Backward of out = y * SiLU(z) through the selective scan; returns the seven gradients.
+
+    ``out`` may supply any of the output tensors (d_B / d_C may be strided views into a
+    wider row, as the layer's x_proj gradient).  See ``ssm_scan_bwd`` in include/ssmbwd.h.
+    """
+    dt = _dtype_code(u)
+    batch, seqlen, d_inner = u.shape
+    n = A_log.shape[1]
+    for name, t in (("delta", delta), ("z", z), ("d_out", d_out)):
+        _need(t.shape == u.shape and t.dtype == u.dtype and t.is_contiguous(), f"{name} must match u")
+    _need(u.is_contiguous(), "u must be contiguous")
+    _need(B.dtype == u.dtype and C.dtype == u.dtype, "B and C must have u's dtype")
+    _need(A_log.dtype == torch.float32 and D.dtype == torch.float32, "A_log and D are float32")
+    _need(A_log.shape == (d_inner, n) and A_log.is_contiguous() and D.shape == (d_inner,), "parameter shapes")
+    ld = _row_stride(B, batch, seqlen, n, "B")
+    _need(_row_stride(C, batch, seqlen, n, "C") == ld, "B and C must share a row stride")
+    o = dict(out or {})
+    dev = u.device
+    for k in ("d_u", "d_delta", "d_z"):
+        o.setdefault(k, torch.empty_like(u))
+    o.setdefault("d_A_log", torch.empty_like(A_log))
+    o.setdefault("d_D", torch.empty_like(D))
+    o.setdefault("d_B", torch.empty((batch, seqlen, n), dtype=u.dtype, device=dev))
+    o.setdefault("d_C", torch.empty((batch, seqlen, n), dtype=u.dtype, device=dev))
+    ldd = _row_stride(o["d_B"], batch, seqlen, n, "d_B")
+    _need(_row_stride(o["d_C"], batch, seqlen, n, "d_C") == ldd, "d_B and d_C must share a row stride")
+    dims = ssm_dims(batch, seqlen, d_inner, n, ld, ldd, seg_len)
+    nbytes = int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(dims), dt))
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    args = (_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(d_out),
+            _ptr(o["d_u"]), _ptr(o["d_delta"]), _ptr(o["d_A_log"]), _ptr(o["d_B"]),
+            _ptr(o["d_C"]), _ptr(o["d_D"]), _ptr(o["d_z"]), int(bool(softplus_epilogue)),
+            _ptr(ws), wsb, ctypes.byref(dims), dt, _stream(u))
+    if stage_events is None:
+        rc = lib().ssm_scan_bwd(*args)
+    else:
+        ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
+        rc = lib().ssm_scan_bwd_timed(*args, ev)
+    _check("ssm_scan_bwd", rc)
+    return o
+
+
+def ssm_scan_fwd(u, delta, A_log, B, C, D, z=None, *, want_y: bool = True, want_out: bool = True,
+                 ckpt_every: int = 0, seg_len: int = 0, workspace=None) -> dict:
+    """Forward scan: y, out = y * SiLU(z) and optional state checkpoints [B, K, N, Di] (float32)."""
+    dt = _dtype_code(u)
+    batch, seqlen, d_inner = u.shape
+    n = A_log.shape[1]
+    _need(u.is_contiguous() and delta.shape == u.shape and delta.is_contiguous(), "u / delta")
+    ld = _row_stride(B, batch, seqlen, n, "B")
+    _need(_row_stride(C, batch, seqlen, n, "C") == ld, "B and C must share a row stride")
+    res = {}
+    y = torch.empty_like(u) if want_y else None
+    o = torch.empty_like(u) if (want_out and z is not None) else None
+    ck = None
+    if ckpt_every:
+        nk = (seqlen + ckpt_every - 1) // ckpt_every
+        ck = torch.empty((batch, nk, n, d_inner), dtype=torch.float32, device=u.device)
+    dims = ssm_dims(batch, seqlen, d_inner, n, ld, n, seg_len)
+    nbytes = int(lib().ssm_scan_fwd_workspace_size(ctypes.byref(dims), dt))
+    ws, wsb = _workspace(nbytes, u.device, workspace)
+    rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _ptr(o),
+                           _ptr(ck), int(ckpt_every), _ptr(ws), wsb, ctypes.byref(dims), dt, _stream(u))
+    _check("ssm_scan_fwd", rc)
+    if y is not None:
+        res["y"] = y
+    if o is not None:
+        res["out"] = o
+    if ck is not None:
+        res["h_ckpt"] = ck
+    return res
+
+
+def gating_bwd(d_out, y, z):
+    """Phase B2 on its own: returns (d_y, d_z)."""
+    dt = _dtype_code(d_out)
+    for t in (y, z):
+        _need(t.shape == d_out.shape and t.dtype == d_out.dtype and t.is_contiguous(), "shapes/dtypes")
+    _need(d_out.is_contiguous(), "d_out must be contiguous")
+    d_y, d_z = torch.empty_like(d_out), torch.empty_like(d_out)
+    _check("gating_bwd", lib().gating_bwd(_ptr(d_out), _ptr(y), _ptr(z), _ptr(d_y), _ptr(d_z), d_out.numel(), dt,
+                                         _stream(d_out)))
+    return d_y, d_z
+
+
+def conv1d_bwd(x, w, bias, d_u, *, d_x=None, workspace=None):
+    """Causal depthwise conv + SiLU backward; x and d_u are [B, T, Di] (last-dim contiguous rows)."""
+    dt = _dtype_code(x)
+    batch, seqlen, d_inner = x.shape
+    d_conv = w.shape[1]
+    _need(w.dtype == torch.float32 and w.shape == (d_inner, d_conv) and w.is_contiguous(), "w is [Di, K] float32")
+    _need(bias is None or (bias.dtype == torch.float32 and bias.shape == (d_inner,)), "bias is [Di] float32")
+    _need(d_u.shape == x.shape and d_u.dtype == x.dtype, "d_u must match x")
+    ldx = _row_stride(x, batch, seqlen, d_inner, "x")
+    ldu = _row_stride(d_u, batch, seqlen, d_inner, "d_u")
+    if d_x is None:
+        d_x = torch.empty((batch, seqlen, d_inner), dtype=x.dtype, device=x.device)
+    ldo = _row_stride(d_x, batch, seqlen, d_inner, "d_x")
+    d_w = torch.empty_like(w)
+    d_b = torch.empty((d_inner,), dtype=torch.float32, device=x.device)
+    nbytes = int(lib().conv1d_bwd_workspace_size(batch, seqlen, d_inner, d_conv))
+    ws, wsb = _workspace(nbytes, x.device, workspace)
+    _check("conv1d_bwd", lib().conv1d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(d_u), _ptr(d_x), _ptr(d_w), _ptr(d_b),
+                                         batch, seqlen, d_inner, d_conv, ldx, ldu, ldo, _ptr(ws), wsb, dt,
+                                         _stream(x)))
+    return d_x, d_w, d_b
+
+
+def rmsnorm_bwd(x, w, dy, d_residual=None, eps: float = 1e-5, *, workspace=None):
+    """RMSNorm (weight only) backward over the last dim, plus an optional residual gradient."""
+    dt = _dtype_code(x)
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    _need(x.is_contiguous() and dy.is_contiguous() and dy.shape == x.shape and dy.dtype == x.dtype, "x / dy")
+    _need(w.dtype == torch.float32 and w.shape == (dim,), "w is [dim] float32")
+    if d_residual is not None:
+        _need(d_residual.shape == x.shape and d_residual.dtype == x.dtype and d_residual.is_contiguous(), "residual")
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    nbytes = int(lib().rmsnorm_bwd_workspace_size(rows, dim))
+    ws, wsb = _workspace(nbytes, x.device, workspace)
+    _check("rmsnorm_bwd", lib().rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(d_residual), _ptr(dx), _ptr(dw), rows,
+                                           dim, ctypes.c_float(eps), _ptr(ws), wsb, dt, _stream(x)))
+    return dx, dw

@@ -1,0 +1,139 @@
+// Shared helpers of the gfx950 kernels: storage types, bf16 conversion,
+// wave-level shuffles, error reporting for the C entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/ssmbwd.h"
+
+namespace ssm {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bfloat16 storage is a raw 16-bit pattern; conversion is exact on load and
+// round-to-nearest-even on store.
+struct bf16 {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x007fffffu)) return bf16{uint16_t((b >> 16) | 0x40u)};
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return bf16{uint16_t(b >> 16)};
+}
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, size_t i) { return to_f32(p[i]); }
+template <typename T>
+__device__ __forceinline__ void st(T* p, size_t i, float v) { p[i] = from_f32<T>(v); }
+
+// Row of NS values of a [.., NS] tensor whose address is the same in every lane
+// of the wave (B_t, C_t), so the compiler keeps it in scalar registers.
+template <int NS>
+__device__ __forceinline__ void load_row(const float* __restrict__ p, float (&v)[NS]) {
+#pragma unroll
+  for (int n = 0; n < NS; ++n) v[n] = p[n];
+}
+template <int NS>
+__device__ __forceinline__ void load_row(const bf16* __restrict__ p, float (&v)[NS]) {
+  static_assert(NS % 2 == 0, "bf16 rows are read in pairs");
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int k = 0; k < NS / 2; ++k) {
+    uint32_t w = q[k];
+    v[2 * k] = __uint_as_float(w << 16);
+    v[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
+
+// ---- cross-lane moves (DPP and the gfx950 permlane swaps) -----------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowRor8 = 0x128;        // lane l <- l ^ 8 inside a 16-lane row
+constexpr int kRowHalfMirror = 0x141;  // lane l <- 7 - l inside each 8-lane half row
+
+// Wave reduce-scatter of V values per lane (V a power of two, 1..16).  On
+// return v[0] of lane l holds the sum over all 64 lanes of the input element
+// with index l >> (6 - log2 V) (each result is repeated on 64/V lanes).
+// Steps: lane bit 5 and bit 4 halves exchange with permlane32/16 swaps, bits 3
+// and 2 with DPP; the bits left once a single value remains are summed with
+// DPP butterflies.
+template <int V>
+__device__ __forceinline__ void wave_reduce_scatter(float (&v)[V], int lane) {
+  static_assert(V == 1 || V == 2 || V == 4 || V == 8 || V == 16, "V must be a power of two <= 16");
+  if constexpr (V >= 2) {  // lane bit 5
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + V / 2]),
+                                                false, false);
+      v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  if constexpr (V >= 4) {  // lane bit 4
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + V / 4]),
+                                                false, false);
+      v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  if constexpr (V >= 8) {  // lane bit 3 (partner l ^ 8)
+    const bool hi = lane & 8;
+#pragma unroll
+    for (int i = 0; i < V / 8; ++i) {
+      float keep = hi ? v[i + V / 8] : v[i];
+      float send = hi ? v[i] : v[i + V / 8];
+      v[i] = keep + dpp<kRowRor8>(send);
+    }
+  }
+  if constexpr (V >= 16) {  // lane bit 2 (partner 7 - l within 8; flips bit 2)
+    const bool hi = lane & 4;
+    float keep = hi ? v[1] : v[0];
+    float send = hi ? v[0] : v[1];
+    v[0] = keep + dpp<kRowHalfMirror>(send);
+  }
+  // remaining low bits: all-reduce
+  if constexpr (V <= 1) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+    v[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (V <= 2) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+    v[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (V <= 4) v[0] += dpp<kRowRor8>(v[0]);
+  if constexpr (V <= 8) v[0] += dpp<kRowHalfMirror>(v[0]);
+  v[0] += dpp<kQuadXor1>(v[0]);
+  v[0] += dpp<kQuadXor2>(v[0]);
+}
+
+// ---- error reporting ---------------------------------------------------------
+void set_error(const char* fmt, ...);
+int fail(int status, const char* fmt, ...);
+int check_launch(const char* what);
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace ssm

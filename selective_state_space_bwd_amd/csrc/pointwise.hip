@@ -1,0 +1,312 @@
+// The layer's bandwidth-bound backward pieces around the scan:
+//   gating_bwd  — mamba-rs cpu/backward.rs Phase B2 on its own;
+//   conv1d_bwd  — Phase B6: SiLU backward on the conv output fused with the
+//                 causal depthwise conv backward;
+//   rmsnorm_bwd — rlx-cpu training_bwd.rs rms_norm_backward_row (no shift term)
+//                 with Phase B8's residual add.
+// Reductions over rows / steps go to fixed-order partials, no atomics.
+#include "common.hpp"
+
+namespace ssm {
+
+constexpr int kPwBlock = 256;
+
+__global__ __launch_bounds__(kPwBlock) void fill_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kPwBlock) void gating_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ y,
+                                                              const T* __restrict__ z, T* __restrict__ dy,
+                                                              T* __restrict__ dz, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kPwBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x; i < n; i += stride) {
+    const float g = ld(dout, i), yy = ld(y, i), zz = ld(z, i);
+    const float s = sigmoid(zz);
+    st(dy, i, g * zz * s);
+    st(dz, i, g * yy * s * (1.f + zz * (1.f - s)));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// conv1d: one thread per (b, chunk of kConvT steps, channel); the conv output
+// and its SiLU derivative are rebuilt from x on the fly over a window of K taps.
+constexpr int kConvT = 64;
+constexpr int kMaxTaps = 8;
+
+template <typename T, int K>
+__global__ __launch_bounds__(kPwBlock) void conv1d_bwd_kernel(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    const T* __restrict__ d_u, T* __restrict__ d_x, float* __restrict__ part, int Bt, int Tn, int Di,
+    int ld_x, int ld_du, int ld_dx, int nchunk) {
+  const int d = blockIdx.x * kPwBlock + threadIdx.x;
+  const int c = blockIdx.y, b = blockIdx.z;
+  if (d >= Di) return;
+  float wk[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) wk[k] = w[(size_t)d * K + k];
+  const float bd = bias ? bias[d] : 0.f;
+  const int t0 = c * kConvT, t1 = min(Tn, t0 + kConvT);
+  const size_t rx = (size_t)b * Tn;
+  // window xs[k] = x[t - (K-1) + k] for the current t; gs[k] = g[t - (K-1) + k]
+  float xs[K], gs[K], dw[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int tt = t0 - K + k;  // the window of step t0 - 1; x[t0] is shifted in by the loop
+    xs[k] = tt >= 0 ? ld(x, (rx + tt) * ld_x + d) : 0.f;
+    gs[k] = 0.f;
+    dw[k] = 0.f;
+  }
+  float db = 0.f;
+  const int tend = min(Tn, t1 + K - 1);
+  for (int t = t0; t < tend; ++t) {
+    // shift in x[t]
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) xs[k] = xs[k + 1];
+    xs[K - 1] = ld(x, (rx + t) * ld_x + d);
+    float cv = bd;
+#pragma unroll
+    for (int k = 0; k < K; ++k) cv = fmaf(wk[k], xs[k], cv);
+    const float s = sigmoid(cv);
+    const float g = ld(d_u, (rx + t) * ld_du + d) * s * (1.f + cv * (1.f - s));
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) gs[k] = gs[k + 1];
+    gs[K - 1] = g;
+    if (t < t1) {  // this chunk owns g[t] for the weight and bias sums
+#pragma unroll
+      for (int k = 0; k < K; ++k) dw[k] = fmaf(g, xs[k], dw[k]);
+      db += g;
+    }
+    const int to = t - (K - 1);  // d_x[to] = sum_k g[to + K-1-k] w[k] = sum_k gs[K-1-k] w[k]
+    if (to >= t0) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc = fmaf(gs[K - 1 - k], wk[k], acc);
+      st(d_x, (rx + to) * ld_dx + d, acc);
+    }
+  }
+  // the last K-1 outputs of the chunk whose g window runs past the sequence end
+  for (int to = max(t0, tend - (K - 1)); to < t1; ++to) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int tg = to + (K - 1) - k;
+      const float gv = (tg < tend) ? gs[K - 1 - (tend - 1 - tg)] : 0.f;
+      acc = fmaf(gv, wk[k], acc);
+    }
+    st(d_x, (rx + to) * ld_dx + d, acc);
+  }
+  const size_t p = ((size_t)b * nchunk + c) * (K + 1);
+#pragma unroll
+  for (int k = 0; k < K; ++k) part[(p + k) * Di + d] = dw[k];
+  part[(p + K) * Di + d] = db;
+}
+
+template <int K>
+__global__ __launch_bounds__(kPwBlock) void conv1d_bwd_finalize(const float* __restrict__ part,
+                                                                float* __restrict__ d_w,
+                                                                float* __restrict__ d_bias, int parts, int Di) {
+  const int idx = blockIdx.x * kPwBlock + threadIdx.x;
+  if (idx >= (K + 1) * Di) return;
+  const int k = idx / Di, d = idx - k * Di;
+  float acc = 0.f;
+  for (int p = 0; p < parts; ++p) acc += part[((size_t)p * (K + 1) + k) * Di + d];
+  if (k < K) d_w[(size_t)d * K + k] = acc;
+  else if (d_bias) d_bias[d] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// rmsnorm: a block takes kRmsRows rows; each thread owns columns tid + 256 j.
+constexpr int kRmsRows = 32;
+constexpr int kRmsMaxCols = 16;  // dim <= 4096
+
+__device__ __forceinline__ float2 block_sum2(float2 v, float2* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    v.x += __shfl_xor(v.x, o);
+    v.y += __shfl_xor(v.y, o);
+  }
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float2 r = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < kPwBlock / kWave; ++w) {
+    r.x += sh[w].x;
+    r.y += sh[w].y;
+  }
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_kernel(
+    const T* __restrict__ x, const float* __restrict__ w, const T* __restrict__ dy, const T* __restrict__ dres,
+    T* __restrict__ dx, float* __restrict__ part, int64_t rows, int dim, float eps) {
+  __shared__ float2 red[kPwBlock / kWave];
+  const int tid = threadIdx.x;
+  const int ncol = (dim + kPwBlock - 1) / kPwBlock;
+  float wv[kRmsMaxCols], dw[kRmsMaxCols];
+#pragma unroll
+  for (int j = 0; j < kRmsMaxCols; ++j) {
+    const int col = tid + j * kPwBlock;
+    wv[j] = (j < ncol && col < dim) ? w[col] : 0.f;
+    dw[j] = 0.f;
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * kRmsRows;
+  const int64_t r1 = min(rows, r0 + kRmsRows);
+  const float inv_dim = 1.f / (float)dim;
+  for (int64_t r = r0; r < r1; ++r) {
+    float xv[kRmsMaxCols], gv[kRmsMaxCols];
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kRmsMaxCols; ++j) {
+      const int col = tid + j * kPwBlock;
+      const bool ok = j < ncol && col < dim;
+      xv[j] = ok ? ld(x, (size_t)r * dim + col) : 0.f;
+      gv[j] = ok ? ld(dy, (size_t)r * dim + col) : 0.f;
+      acc.x = fmaf(xv[j], xv[j], acc.x);
+      acc.y = fmaf(gv[j] * wv[j], xv[j], acc.y);
+    }
+    const float2 sums = block_sum2(acc, red);
+    const float inv_r = 1.f / sqrtf(sums.x * inv_dim + eps);
+    const float dot = sums.y * inv_dim;
+    const float c3 = inv_r * inv_r * inv_r * dot;
+#pragma unroll
+    for (int j = 0; j < kRmsMaxCols; ++j) {
+      const int col = tid + j * kPwBlock;
+      if (j < ncol && col < dim) {
+        float v = inv_r * wv[j] * gv[j] - c3 * xv[j];
+        if (dres) v += ld(dres, (size_t)r * dim + col);
+        st(dx, (size_t)r * dim + col, v);
+        dw[j] = fmaf(gv[j] * xv[j], inv_r, dw[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRmsMaxCols; ++j) {
+    const int col = tid + j * kPwBlock;
+    if (j < ncol && col < dim) part[(size_t)blockIdx.x * dim + col] = dw[j];
+  }
+}
+
+__global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_finalize(const float* __restrict__ part,
+                                                                 float* __restrict__ dw, int parts, int dim) {
+  const int col = blockIdx.x * kPwBlock + threadIdx.x;
+  if (col >= dim) return;
+  float acc = 0.f;
+  for (int p = 0; p < parts; ++p) acc += part[(size_t)p * dim + col];
+  dw[col] = acc;
+}
+
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" int gating_bwd(const void* d_out, const void* y, const void* z, void* d_y, void* d_z, int64_t n,
+                          int dtype, void* stream) {
+  if (n < 0) return fail(SSM_ERR_INVALID_ARG, "n = %lld", (long long)n);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (n == 0) return SSM_OK;
+  if (!d_out || !y || !z || !d_y || !d_z) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t want = (n + kPwBlock - 1) / kPwBlock;
+  const int blocks = (int)(want < 8192 ? want : 8192);
+  if (dtype == SSM_F32)
+    hipLaunchKernelGGL(gating_bwd_kernel<float>, dim3(blocks), dim3(kPwBlock), 0, st, (const float*)d_out,
+                       (const float*)y, (const float*)z, (float*)d_y, (float*)d_z, n);
+  else
+    hipLaunchKernelGGL(gating_bwd_kernel<bf16>, dim3(blocks), dim3(kPwBlock), 0, st, (const bf16*)d_out,
+                       (const bf16*)y, (const bf16*)z, (bf16*)d_y, (bf16*)d_z, n);
+  return check_launch("gating_bwd");
+}
+
+extern "C" size_t conv1d_bwd_workspace_size(int batch, int seqlen, int d_inner, int d_conv) {
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_conv <= 0 || d_conv > kMaxTaps) return 0;
+  const size_t nchunk = (seqlen + kConvT - 1) / kConvT;
+  return align_up((size_t)batch * nchunk * (d_conv + 1) * d_inner * sizeof(float));
+}
+
+extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u, void* d_x, float* d_w,
+                          float* d_bias, int batch, int seqlen, int d_inner, int d_conv, int ld_x, int ld_du,
+                          int ld_dx, void* workspace, size_t ws_bytes, int dtype, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (batch < 0 || seqlen < 0 || d_inner <= 0 || d_conv <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "bad size (batch %d seqlen %d d_inner %d d_conv %d)", batch, seqlen, d_inner,
+                d_conv);
+  if (d_conv > kMaxTaps) return fail(SSM_ERR_UNSUPPORTED, "d_conv %d > %d", d_conv, kMaxTaps);
+  if (ld_x < d_inner || ld_du < d_inner || ld_dx < d_inner)
+    return fail(SSM_ERR_INVALID_ARG, "row strides below d_inner");
+  if (!w || !d_w) return fail(SSM_ERR_INVALID_ARG, "w and d_w are required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((size_t)batch * seqlen == 0) {  // sums over nothing
+    hipLaunchKernelGGL(fill_zero_f32, dim3((d_inner * d_conv + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0, st,
+                       d_w, (int64_t)d_inner * d_conv);
+    if (d_bias)
+      hipLaunchKernelGGL(fill_zero_f32, dim3((d_inner + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0, st, d_bias,
+                         (int64_t)d_inner);
+    return check_launch("conv1d_bwd (empty)");
+  }
+  if (!x || !d_u || !d_x) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  const size_t need = conv1d_bwd_workspace_size(batch, seqlen, d_inner, d_conv);
+  if (!workspace || ws_bytes < need)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  const int nchunk = (seqlen + kConvT - 1) / kConvT;
+  dim3 grid((d_inner + kPwBlock - 1) / kPwBlock, nchunk, batch);
+  float* part = static_cast<float*>(workspace);
+#define CONV_CASE(TY, KV)                                                                                     \
+  case KV:                                                                                                    \
+    hipLaunchKernelGGL((conv1d_bwd_kernel<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,     \
+                       (const TY*)d_u, (TY*)d_x, part, batch, seqlen, d_inner, ld_x, ld_du, ld_dx, nchunk); \
+    hipLaunchKernelGGL((conv1d_bwd_finalize<KV>), dim3(((KV + 1) * d_inner + kPwBlock - 1) / kPwBlock),      \
+                       dim3(kPwBlock), 0, st, part, d_w, d_bias, batch * nchunk, d_inner);                  \
+    break;
+  if (dtype == SSM_F32) {
+    switch (d_conv) { CONV_CASE(float, 1) CONV_CASE(float, 2) CONV_CASE(float, 3) CONV_CASE(float, 4)
+                      CONV_CASE(float, 5) CONV_CASE(float, 6) CONV_CASE(float, 7) CONV_CASE(float, 8) }
+  } else {
+    switch (d_conv) { CONV_CASE(bf16, 1) CONV_CASE(bf16, 2) CONV_CASE(bf16, 3) CONV_CASE(bf16, 4)
+                      CONV_CASE(bf16, 5) CONV_CASE(bf16, 6) CONV_CASE(bf16, 7) CONV_CASE(bf16, 8) }
+  }
+#undef CONV_CASE
+  return check_launch("conv1d_bwd");
+}
+
+extern "C" size_t rmsnorm_bwd_workspace_size(int64_t rows, int dim) {
+  if (rows <= 0 || dim <= 0 || dim > kPwBlock * kRmsMaxCols) return 0;
+  const size_t blocks = (size_t)((rows + kRmsRows - 1) / kRmsRows);
+  return align_up(blocks * dim * sizeof(float));
+}
+
+extern "C" int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_residual, void* dx,
+                           float* dw, int64_t rows, int dim, float eps, void* workspace, size_t ws_bytes, int dtype,
+                           void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (rows < 0 || dim <= 0) return fail(SSM_ERR_INVALID_ARG, "bad size (rows %lld dim %d)", (long long)rows, dim);
+  if (dim > kPwBlock * kRmsMaxCols) return fail(SSM_ERR_UNSUPPORTED, "dim %d > %d", dim, kPwBlock * kRmsMaxCols);
+  if (!(eps >= 0.f)) return fail(SSM_ERR_INVALID_ARG, "eps must be >= 0");
+  if (!dw) return fail(SSM_ERR_INVALID_ARG, "dw is required");
+  if (rows == 0) {  // sum over no rows
+    hipLaunchKernelGGL(fill_zero_f32, dim3((dim + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0,
+                       static_cast<hipStream_t>(stream), dw, (int64_t)dim);
+    return check_launch("rmsnorm_bwd (empty)");
+  }
+  if (!x || !w || !dy || !dx) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  const size_t need = rmsnorm_bwd_workspace_size(rows, dim);
+  if (!workspace || ws_bytes < need)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int blocks = (int)((rows + kRmsRows - 1) / kRmsRows);
+  float* part = static_cast<float*>(workspace);
+  if (dtype == SSM_F32)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(blocks), dim3(kPwBlock), 0, st, (const float*)x, w,
+                       (const float*)dy, (const float*)d_residual, (float*)dx, part, rows, dim, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(blocks), dim3(kPwBlock), 0, st, (const bf16*)x, w,
+                       (const bf16*)dy, (const bf16*)d_residual, (bf16*)dx, part, rows, dim, eps);
+  hipLaunchKernelGGL(rmsnorm_bwd_finalize, dim3((dim + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0, st, part, dw,
+                     blocks, dim);
+  return check_launch("rmsnorm_bwd");
+}

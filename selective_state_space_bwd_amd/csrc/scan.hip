@@ -1,0 +1,691 @@
+// Selective-scan forward and backward for gfx950.
+//
+// Method (mamba-rs 0.5.1 cpu/backward.rs, Phases B2 and B3): the page walks t
+// backwards once, reading three saved per-step state tensors (da_exp, h_prev,
+// h_curr, each [T, d_inner*d_state]).  Here nothing per step and per state
+// goes to memory.  One lane owns one channel (b, d) and keeps its d_state
+// states in registers; B_t and C_t are the same for every lane of a block and
+// sit in scalar registers.  Time is cut into segments that run in parallel,
+// and each segment into chunks of kChunk steps:
+//
+//   1. summary  (per segment, forward in t): the segment's local states from a
+//      zero start, with the state before every chunk written out
+//      (checkpoints), the local end state, and the local adjoint summary
+//      G = sum_t (prod_{r<=t} a_r) dy_t C_t that the next carry needs.
+//   2. carry    (per channel, over segments): the pair operator
+//      (a1, v1) + (a2, v2) = (a2 a1, a2 v1 + v2) joins the segments, forward for
+//      the state entering each segment and backward for the adjoint leaving it;
+//      a segment's decay is exp(A * sum of its delta).
+//   3. main     (per segment, chunks in reverse): rebuild the chunk's states
+//      from its checkpoint (corrected by the carried-in state), keep a_t h_{t-1}
+//      in registers, then walk the chunk backwards with the adjoint g.  d_B and
+//      d_C (sums over channels) are reduced inside the wave with permlane swaps
+//      and DPP, across the block's waves in LDS, and across blocks as
+//      fixed-order partials; d_A_log and d_D (sums over batch and time) are kept
+//      per lane over the segment and written as partials.
+//   4. finalize: fixed-order sums of the partials.
+// Nothing uses atomics, so results are bitwise repeatable.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.hpp"
+
+namespace ssm {
+
+constexpr int kChunk = 8;    // steps rebuilt and held in registers at a time
+constexpr int kBlock = 256;  // channels per block (4 waves)
+
+struct ScanShape {
+  int Bt, T, Di, ld_bc, ld_dbc;
+  int seg, nseg, nchunk, ntile;
+};
+
+struct ScanWs {
+  float* ckpt;     // [Bt, nchunk, N, Di]  local state before each chunk
+  float* ckpt_sd;  // [Bt, nchunk, Di]     sum of delta from the segment start
+  float* seg_h;    // [Bt, nseg, N, Di]    local end state, then the state entering the segment
+  float* seg_g;    // [Bt, nseg, N, Di]    local adjoint summary, then the adjoint leaving it
+  float* seg_sd;   // [Bt, nseg, Di]       sum of delta over the segment
+  float* part_bc;  // [ntile, Bt, T, 2N]   per-block sums of d_B | d_C
+  float* part_a;   // [Bt, nseg, N+1, Di]  per-segment sums for d_A_log | d_D
+};
+
+template <int NS>
+__device__ __forceinline__ void load_A2(const float* __restrict__ A_log, int d, float (&A2)[NS]) {
+#pragma unroll
+  for (int n = 0; n < NS; ++n) A2[n] = -expf(A_log[(size_t)d * NS + n]) * kLog2e;
+}
+
+// ---------------------------------------------------------------------------
+// 1. segment summaries.  BWD adds the chunk checkpoints and the adjoint summary.
+template <typename T, int NS, bool BWD>
+__global__ __launch_bounds__(kBlock) void scan_summary(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const T* __restrict__ z,
+    const T* __restrict__ dout, float* __restrict__ ckpt, float* __restrict__ ckpt_sd,
+    float* __restrict__ seg_h, float* __restrict__ seg_g, float* __restrict__ seg_sd, ScanShape sh) {
+  const int d = blockIdx.x * kBlock + threadIdx.x;
+  const int s = blockIdx.y, b = blockIdx.z;
+  const bool active = d < sh.Di;
+  const int dc = active ? d : sh.Di - 1;
+  const int Di = sh.Di;
+  float A2[NS];
+  load_A2<NS>(A_log, dc, A2);
+  float h[NS], P[NS], G[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) { h[n] = 0.f; P[n] = 1.f; G[n] = 0.f; }
+  float sd = 0.f;
+  const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
+  const bool need_g = BWD && s > 0;  // the first segment's adjoint summary is never used
+  const size_t row0 = (size_t)b * sh.T;
+  for (int tc = t0; tc < t1; tc += kChunk) {
+    if (BWD && tc > t0 && active) {
+      const size_t c = (size_t)b * sh.nchunk + tc / kChunk;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) ckpt[(c * NS + n) * Di + d] = h[n];
+      ckpt_sd[c * Di + d] = sd;
+    }
+    const int nv = min(kChunk, t1 - tc);
+    float dl[kChunk], uu[kChunk], dy[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        const size_t i = (row0 + tc + j) * Di + dc;
+        dl[j] = ld(delta, i);
+        uu[j] = ld(u, i);
+        if (need_g) {
+          const float zz = ld(z, i);
+          dy[j] = ld(dout, i) * zz * sigmoid(zz);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        float Bv[NS];
+        load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
+        const float du = dl[j] * uu[j];
+        if (need_g) {
+          float Cv[NS];
+          load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            const float a = fast_exp2(dl[j] * A2[n]);
+            h[n] = fmaf(a, h[n], du * Bv[n]);
+            P[n] *= a;
+            G[n] = fmaf(P[n], dy[j] * Cv[n], G[n]);
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            const float a = fast_exp2(dl[j] * A2[n]);
+            h[n] = fmaf(a, h[n], du * Bv[n]);
+          }
+        }
+        sd += dl[j];
+      }
+    }
+  }
+  if (!active) return;
+  const size_t sg = (size_t)b * sh.nseg + s;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    seg_h[(sg * NS + n) * Di + d] = h[n];
+    if (BWD) seg_g[(sg * NS + n) * Di + d] = G[n];
+  }
+  seg_sd[sg * Di + d] = sd;
+}
+
+// ---------------------------------------------------------------------------
+// 2. carries across segments, one thread per channel, in place.
+template <int NS, bool BWD>
+__global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A_log, ScanWs ws,
+                                                     ScanShape sh) {
+  const int idx = blockIdx.x * kBlock + threadIdx.x;
+  if (idx >= sh.Bt * sh.Di) return;
+  const int b = idx / sh.Di, d = idx - b * sh.Di;
+  const int Di = sh.Di;
+  float A2[NS];
+  load_A2<NS>(A_log, d, A2);
+  float H[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) H[n] = 0.f;
+  for (int s = 0; s < sh.nseg; ++s) {
+    const size_t sg = (size_t)b * sh.nseg + s;
+    const float sd = ws.seg_sd[sg * Di + d];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      float* p = ws.seg_h + (sg * NS + n) * Di + d;
+      const float loc = *p;
+      *p = H[n];
+      H[n] = fmaf(fast_exp2(A2[n] * sd), H[n], loc);
+    }
+  }
+  if (!BWD) return;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) H[n] = 0.f;
+  for (int s = sh.nseg - 1; s >= 0; --s) {
+    const size_t sg = (size_t)b * sh.nseg + s;
+    const float sd = ws.seg_sd[sg * Di + d];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      float* p = ws.seg_g + (sg * NS + n) * Di + d;
+      const float loc = *p;
+      *p = H[n];
+      H[n] = fmaf(fast_exp2(A2[n] * sd), H[n], loc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. the backward sweep of one segment.
+//
+// Per chunk, a_t h_{t-1} of the later kRegSteps steps stays in registers; for
+// d_state = 16 the earlier steps' values go to LDS (each lane reads back only
+// its own slots, so no barrier is needed), which keeps two blocks per CU.
+template <int NS>
+struct ChunkTile {
+  static constexpr int kRegSteps = (NS * kChunk <= 64) ? kChunk : 64 / NS;
+  static constexpr int kLdsSteps = kChunk - kRegSteps;
+};
+
+template <typename T, int NS, bool SOFTPLUS>
+__global__ __launch_bounds__(kBlock) void scan_bwd_main(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
+    const T* __restrict__ z, const T* __restrict__ dout, T* __restrict__ d_u,
+    T* __restrict__ d_delta, T* __restrict__ d_z, const float* __restrict__ ckpt,
+    const float* __restrict__ ckpt_sd, const float* __restrict__ seg_h, const float* __restrict__ seg_g,
+    float* __restrict__ part_bc, float* __restrict__ part_a, ScanShape sh) {
+  constexpr int kLogNS = NS == 16 ? 4 : NS == 8 ? 3 : NS == 4 ? 2 : NS == 2 ? 1 : 0;
+  constexpr int kRep = kWave / NS;  // lanes holding each reduced value
+  constexpr int kReg = ChunkTile<NS>::kRegSteps;
+  constexpr int kLds = ChunkTile<NS>::kLdsSteps;
+  static_assert(NS % 4 == 0, "a*h rows move through LDS as float4");
+  __shared__ float red[2][kBlock / kWave][kChunk][2 * NS];
+  __shared__ float4 lds_ah[kLds > 0 ? kLds : 1][NS / 4][kBlock];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int d = blockIdx.x * kBlock + tid;
+  const int s = blockIdx.y, b = blockIdx.z;
+  const bool active = d < sh.Di;
+  const int dc = active ? d : sh.Di - 1;
+  const int Di = sh.Di;
+  const size_t row0 = (size_t)b * sh.T;
+  const size_t sg = (size_t)b * sh.nseg + s;
+
+  float A2[NS];
+  load_A2<NS>(A_log, dc, A2);
+  const float Dd = Dp[dc];
+  float g[NS], dA[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    g[n] = (s == sh.nseg - 1) ? 0.f : seg_g[(sg * NS + n) * Di + dc];
+    dA[n] = 0.f;
+  }
+  float dD = 0.f;
+
+  const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
+  const int c_first = t0 / kChunk, c_last = (t1 - 1) / kChunk;
+  for (int c = c_last; c >= c_first; --c) {
+    const int tc = c * kChunk;
+    const int nv = min(kChunk, t1 - tc);
+    const int buf = c & 1;
+    // state before the chunk: local checkpoint + decayed carry-in
+    float h[NS];
+    if (c == c_first) {
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h[n] = (s == 0) ? 0.f : seg_h[(sg * NS + n) * Di + dc];
+    } else {
+      const size_t cc = (size_t)b * sh.nchunk + c;
+      const float sdv = ckpt_sd[cc * Di + dc];
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        const float hin = (s == 0) ? 0.f : seg_h[(sg * NS + n) * Di + dc];
+        h[n] = fmaf(fast_exp2(A2[n] * sdv), hin, ckpt[(cc * NS + n) * Di + dc]);
+      }
+    }
+    // per-step channel values: delta, u, dy = d_out SiLU(z), and the d_z factor
+    float dl[kChunk], uu[kChunk], dy[kChunk], dzf[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        const size_t i = (row0 + tc + j) * Di + dc;
+        dl[j] = ld(delta, i);
+        uu[j] = ld(u, i);
+        const float zz = ld(z, i), dg = ld(dout, i);
+        const float sz = sigmoid(zz);
+        dy[j] = active ? dg * zz * sz : 0.f;
+        dzf[j] = dg * sz * (1.f + zz * (1.f - sz));
+      }
+    }
+    // forward: rebuild the chunk's states, keep a_t h_{t-1}
+    float ah[kReg][NS];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        float Bv[NS], Cv[NS];
+        load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
+        load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        const float du = dl[j] * uu[j];
+        float y = Dd * uu[j];
+        float dC[NS];
+        float aj[NS];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          const float a = fast_exp2(dl[j] * A2[n]);
+          aj[n] = a * h[n];
+          h[n] = fmaf(du, Bv[n], aj[n]);
+          y = fmaf(Cv[n], h[n], y);
+          dC[n] = dy[j] * h[n];
+        }
+        if (j < kLds) {
+#pragma unroll
+          for (int q = 0; q < NS / 4; ++q)
+            lds_ah[j < kLds ? j : 0][q][tid] = make_float4(aj[4 * q], aj[4 * q + 1], aj[4 * q + 2], aj[4 * q + 3]);
+        } else {
+#pragma unroll
+          for (int n = 0; n < NS; ++n) ah[j >= kLds ? j - kLds : 0][n] = aj[n];
+        }
+        if (active) st(d_z, (row0 + tc + j) * Di + d, y * dzf[j]);
+        wave_reduce_scatter<NS>(dC, lane);
+        if ((lane & (kRep - 1)) == 0) red[buf][wave][j][NS + (lane >> (6 - kLogNS))] = dC[0];
+      }
+    }
+    // reverse: adjoint through the chunk
+#pragma unroll
+    for (int j = kChunk - 1; j >= 0; --j) {
+      if (j < nv) {
+        float Bv[NS], Cv[NS];
+        load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
+        load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        float aj[NS];
+        if (j < kLds) {
+#pragma unroll
+          for (int q = 0; q < NS / 4; ++q) {
+            const float4 v = lds_ah[j < kLds ? j : 0][q][tid];
+            aj[4 * q] = v.x;
+            aj[4 * q + 1] = v.y;
+            aj[4 * q + 2] = v.z;
+            aj[4 * q + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < NS; ++n) aj[n] = ah[j >= kLds ? j - kLds : 0][n];
+        }
+        const float du = active ? dl[j] * uu[j] : 0.f;
+        float sgb = 0.f, saw = 0.f;
+        float dB[NS];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          const float gn = fmaf(dy[j], Cv[n], g[n]);
+          const float w = gn * aj[n];
+          saw = fmaf(A2[n], w, saw);
+          dA[n] = fmaf(dl[j], w, dA[n]);
+          sgb = fmaf(gn, Bv[n], sgb);
+          dB[n] = gn * du;
+          g[n] = fast_exp2(dl[j] * A2[n]) * gn;
+        }
+        float ddl = fmaf(saw, kLn2, uu[j] * sgb);
+        if (SOFTPLUS) ddl = dl[j] > 20.f ? ddl : ddl * (1.f - fast_exp2(-dl[j] * kLog2e));
+        dD = fmaf(dy[j], uu[j], dD);
+        if (active) {
+          const size_t i = (row0 + tc + j) * Di + d;
+          st(d_u, i, fmaf(Dd, dy[j], dl[j] * sgb));
+          st(d_delta, i, ddl);
+        }
+        wave_reduce_scatter<NS>(dB, lane);
+        if ((lane & (kRep - 1)) == 0) red[buf][wave][j][lane >> (6 - kLogNS)] = dB[0];
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < kChunk * 2 * NS; q += kBlock) {
+      const int j = q / (2 * NS), k = q - j * (2 * NS);
+      if (j < nv) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kBlock / kWave; ++w) acc += red[buf][w][j][k];
+        part_bc[(((size_t)blockIdx.x * sh.Bt + b) * sh.T + tc + j) * 2 * NS + k] = acc;
+      }
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) part_a[(sg * (NS + 1) + n) * Di + d] = dA[n];
+  part_a[(sg * (NS + 1) + NS) * Di + d] = dD;
+}
+
+// ---------------------------------------------------------------------------
+// 4. fixed-order sums of the partials.
+template <typename T, int NS>
+__global__ __launch_bounds__(kBlock) void scan_bwd_finalize(
+    const float* __restrict__ A_log, T* __restrict__ d_B, T* __restrict__ d_C,
+    float* __restrict__ d_A_log, float* __restrict__ d_D, const float* __restrict__ part_bc,
+    const float* __restrict__ part_a, ScanShape sh, int nblk_bc) {
+  if ((int)blockIdx.x < nblk_bc) {
+    const size_t rows = (size_t)sh.Bt * sh.T;
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= rows * 2 * NS) return;
+    const size_t r = idx / (2 * NS);
+    const int k = (int)(idx - r * 2 * NS);
+    float acc = 0.f;
+    for (int tile = 0; tile < sh.ntile; ++tile) acc += part_bc[((size_t)tile * rows + r) * 2 * NS + k];
+    if (k < NS) st(d_B, r * sh.ld_dbc + k, acc);
+    else st(d_C, r * sh.ld_dbc + (k - NS), acc);
+  } else {
+    const int idx = (blockIdx.x - nblk_bc) * kBlock + threadIdx.x;
+    if (idx >= (NS + 1) * sh.Di) return;
+    const int n = idx / sh.Di, d = idx - n * sh.Di;
+    float acc = 0.f;
+    const int parts = sh.Bt * sh.nseg;
+    for (int p = 0; p < parts; ++p) acc += part_a[((size_t)p * (NS + 1) + n) * sh.Di + d];
+    if (n < NS) d_A_log[(size_t)d * NS + n] = -expf(A_log[(size_t)d * NS + n]) * acc;
+    else d_D[d] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// forward with true states: y, out = y*SiLU(z), optional checkpoints.
+template <typename T, int NS>
+__global__ __launch_bounds__(kBlock) void scan_fwd_main(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
+    const T* __restrict__ z, T* __restrict__ y, T* __restrict__ out, float* __restrict__ h_ckpt,
+    int ckpt_every, int nckpt, const float* __restrict__ seg_h, ScanShape sh) {
+  const int d = blockIdx.x * kBlock + threadIdx.x;
+  const int s = blockIdx.y, b = blockIdx.z;
+  if (d >= sh.Di) return;
+  const int Di = sh.Di;
+  float A2[NS];
+  load_A2<NS>(A_log, d, A2);
+  const float Dd = Dp[d];
+  const size_t row0 = (size_t)b * sh.T;
+  const size_t sg = (size_t)b * sh.nseg + s;
+  float h[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) h[n] = (s == 0) ? 0.f : seg_h[(sg * NS + n) * Di + d];
+  const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
+  for (int t = t0; t < t1; ++t) {
+    if (h_ckpt && t % ckpt_every == 0) {
+      const size_t k = (size_t)b * nckpt + t / ckpt_every;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h_ckpt[(k * NS + n) * Di + d] = h[n];
+    }
+    const size_t i = (row0 + t) * Di + d;
+    const float dl = ld(delta, i), uu = ld(u, i);
+    float Bv[NS], Cv[NS];
+    load_row<NS>(Bm + (row0 + t) * sh.ld_bc, Bv);
+    load_row<NS>(Cm + (row0 + t) * sh.ld_bc, Cv);
+    const float du = dl * uu;
+    float yy = Dd * uu;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      h[n] = fmaf(fast_exp2(dl * A2[n]), h[n], du * Bv[n]);
+      yy = fmaf(Cv[n], h[n], yy);
+    }
+    if (y) st(y, i, yy);
+    if (out) {
+      const float zz = ld(z, i);
+      st(out, i, yy * zz * sigmoid(zz));
+    }
+  }
+}
+
+__global__ void fill_zero(float* __restrict__ p, int n) {
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+namespace {
+
+struct Plan {
+  ScanShape sh;
+  size_t off[7];
+  size_t bytes;
+};
+
+int auto_seg(const ssm_dims& dm) {
+  const long ntile = (dm.d_inner + kBlock - 1) / kBlock;
+  const long per_seg = ntile * dm.batch;
+  int seg = ((dm.seqlen + kChunk - 1) / kChunk) * kChunk;
+  // enough blocks for every CU to hold two, without segments shorter than 64 steps
+  while (seg > 64 && per_seg * ((dm.seqlen + seg - 1) / seg) < 1024) seg = ((seg / 2 + kChunk - 1) / kChunk) * kChunk;
+  return seg;
+}
+
+int check_dims(const ssm_dims* dm, int dtype) {
+  if (!dm) return fail(SSM_ERR_INVALID_ARG, "dims is null");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dm->batch < 0 || dm->seqlen < 0 || dm->d_inner <= 0 || dm->d_state <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "bad size (batch %d seqlen %d d_inner %d d_state %d)", dm->batch,
+                dm->seqlen, dm->d_inner, dm->d_state);
+  if (dm->d_state != 4 && dm->d_state != 8 && dm->d_state != 16)
+    return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {4, 8, 16}", dm->d_state);
+  if (dm->ld_bc < dm->d_state || dm->ld_dbc < dm->d_state)
+    return fail(SSM_ERR_INVALID_ARG, "row strides ld_bc %d / ld_dbc %d below d_state %d", dm->ld_bc, dm->ld_dbc,
+                dm->d_state);
+  if (dm->seg_len < 0 || dm->seg_len % kChunk != 0)
+    return fail(SSM_ERR_INVALID_ARG, "seg_len %d is not 0 or a multiple of %d", dm->seg_len, kChunk);
+  if (dtype == SSM_BF16 && ((dm->ld_bc & 1) || (dm->ld_dbc & 1)))
+    return fail(SSM_ERR_UNSUPPORTED, "bf16 B/C rows need even strides (ld_bc %d, ld_dbc %d)", dm->ld_bc,
+                dm->ld_dbc);
+  const double elems = (double)dm->batch * dm->seqlen * (double)(dm->d_inner > dm->ld_bc ? dm->d_inner : dm->ld_bc);
+  if (elems > 9.0e15) return fail(SSM_ERR_INVALID_ARG, "tensor too large");
+  return SSM_OK;
+}
+
+Plan make_plan(const ssm_dims& dm, bool bwd) {
+  Plan p{};
+  ScanShape& sh = p.sh;
+  sh.Bt = dm.batch;
+  sh.T = dm.seqlen;
+  sh.Di = dm.d_inner;
+  sh.ld_bc = dm.ld_bc;
+  sh.ld_dbc = dm.ld_dbc;
+  sh.seg = dm.seg_len ? dm.seg_len : auto_seg(dm);
+  if (sh.seg <= 0) sh.seg = kChunk;
+  sh.nseg = (sh.T + sh.seg - 1) / sh.seg;
+  sh.nchunk = (sh.T + kChunk - 1) / kChunk;
+  sh.ntile = (sh.Di + kBlock - 1) / kBlock;
+  const size_t N = dm.d_state, Bt = sh.Bt, Di = sh.Di;
+  size_t sz[7] = {0, 0, 0, 0, 0, 0, 0};
+  if (bwd) {
+    sz[0] = Bt * sh.nchunk * N * Di;
+    sz[1] = Bt * sh.nchunk * Di;
+  }
+  sz[2] = Bt * sh.nseg * N * Di;
+  sz[3] = bwd ? Bt * sh.nseg * N * Di : 0;
+  sz[4] = Bt * sh.nseg * Di;
+  if (bwd) {
+    sz[5] = (size_t)sh.ntile * Bt * sh.T * 2 * N;
+    sz[6] = Bt * sh.nseg * (N + 1) * Di;
+  }
+  size_t off = 0;
+  for (int i = 0; i < 7; ++i) {
+    p.off[i] = off;
+    off += align_up(sz[i] * sizeof(float));
+  }
+  p.bytes = off;
+  return p;
+}
+
+ScanWs bind(const Plan& p, void* ws) {
+  char* base = static_cast<char*>(ws);
+  ScanWs w;
+  w.ckpt = reinterpret_cast<float*>(base + p.off[0]);
+  w.ckpt_sd = reinterpret_cast<float*>(base + p.off[1]);
+  w.seg_h = reinterpret_cast<float*>(base + p.off[2]);
+  w.seg_g = reinterpret_cast<float*>(base + p.off[3]);
+  w.seg_sd = reinterpret_cast<float*>(base + p.off[4]);
+  w.part_bc = reinterpret_cast<float*>(base + p.off[5]);
+  w.part_a = reinterpret_cast<float*>(base + p.off[6]);
+  return w;
+}
+
+template <typename T, int NS>
+int launch_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+               const float* D, const void* z, const void* d_out, void* d_u, void* d_delta,
+               float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus,
+               const Plan& p, ScanWs w, hipStream_t st, void* const* ev) {
+  auto mark = [&](int k) {
+    if (ev && ev[k]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), st);
+  };
+  const ScanShape& sh = p.sh;
+  const T* tu = static_cast<const T*>(u);
+  const T* tdl = static_cast<const T*>(delta);
+  const T* tB = static_cast<const T*>(B);
+  const T* tC = static_cast<const T*>(C);
+  const T* tz = static_cast<const T*>(z);
+  const T* tdo = static_cast<const T*>(d_out);
+  dim3 grid(sh.ntile, sh.nseg, sh.Bt);
+  mark(0);
+  hipLaunchKernelGGL((scan_summary<T, NS, true>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, tz, tdo,
+                     w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
+  mark(1);
+  if (sh.nseg > 1) {
+    const int nb = (sh.Bt * sh.Di + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((scan_carry<NS, true>), dim3(nb), dim3(kBlock), 0, st, A_log, w, sh);
+  }
+  mark(2);
+  if (softplus)
+    hipLaunchKernelGGL((scan_bwd_main<T, NS, true>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz,
+                       tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z), w.ckpt,
+                       w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);
+  else
+    hipLaunchKernelGGL((scan_bwd_main<T, NS, false>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz,
+                       tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z), w.ckpt,
+                       w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);
+  mark(3);
+  const size_t nbc = (size_t)sh.Bt * sh.T * 2 * NS;
+  const int nblk_bc = (int)((nbc + kBlock - 1) / kBlock);
+  const int nblk_a = ((NS + 1) * sh.Di + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL((scan_bwd_finalize<T, NS>), dim3(nblk_bc + nblk_a), dim3(kBlock), 0, st, A_log,
+                     static_cast<T*>(d_B), static_cast<T*>(d_C), d_A_log, d_D, w.part_bc, w.part_a, sh, nblk_bc);
+  mark(4);
+  return check_launch("ssm_scan_bwd");
+}
+
+template <typename T, int NS>
+int launch_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+               const float* D, const void* z, void* y, void* out, float* h_ckpt, int ckpt_every,
+               const Plan& p, ScanWs w, hipStream_t st) {
+  const ScanShape& sh = p.sh;
+  const T* tu = static_cast<const T*>(u);
+  const T* tdl = static_cast<const T*>(delta);
+  const T* tB = static_cast<const T*>(B);
+  const T* tC = static_cast<const T*>(C);
+  dim3 grid(sh.ntile, sh.nseg, sh.Bt);
+  if (sh.nseg > 1) {
+    hipLaunchKernelGGL((scan_summary<T, NS, false>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC,
+                       (const T*)nullptr, (const T*)nullptr, w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
+    const int nb = (sh.Bt * sh.Di + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((scan_carry<NS, false>), dim3(nb), dim3(kBlock), 0, st, A_log, w, sh);
+  }
+  const int nckpt = ckpt_every > 0 ? (sh.T + ckpt_every - 1) / ckpt_every : 0;
+  hipLaunchKernelGGL((scan_fwd_main<T, NS>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D,
+                     static_cast<const T*>(z), static_cast<T*>(y), static_cast<T*>(out), h_ckpt,
+                     ckpt_every > 0 ? ckpt_every : 1, nckpt, w.seg_h, sh);
+  return check_launch("ssm_scan_fwd");
+}
+
+int zero_params(float* d_A_log, float* d_D, int n_a, int n_d, hipStream_t st) {
+  if (n_a > 0) hipLaunchKernelGGL(fill_zero, dim3((n_a + kBlock - 1) / kBlock), dim3(kBlock), 0, st, d_A_log, n_a);
+  if (n_d > 0) hipLaunchKernelGGL(fill_zero, dim3((n_d + kBlock - 1) / kBlock), dim3(kBlock), 0, st, d_D, n_d);
+  return check_launch("ssm_scan_bwd (empty)");
+}
+
+}  // namespace
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" size_t ssm_scan_bwd_workspace_size(const ssm_dims* dims, int dtype) {
+  if (check_dims(dims, dtype) != SSM_OK) return 0;
+  if ((size_t)dims->batch * dims->seqlen * dims->d_inner == 0) return 0;
+  return make_plan(*dims, true).bytes;
+}
+
+extern "C" size_t ssm_scan_fwd_workspace_size(const ssm_dims* dims, int dtype) {
+  if (check_dims(dims, dtype) != SSM_OK) return 0;
+  if ((size_t)dims->batch * dims->seqlen * dims->d_inner == 0) return 0;
+  return make_plan(*dims, false).bytes;
+}
+
+extern "C" int ssm_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                            const float* D, const void* z, const void* d_out, void* d_u, void* d_delta,
+                            float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus_epilogue,
+                            void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream) {
+  return ssm_scan_bwd_timed(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
+                            softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, nullptr);
+}
+
+extern "C" int ssm_scan_bwd_timed(const void* u, const void* delta, const float* A_log, const void* B,
+                                  const void* C, const float* D, const void* z, const void* d_out, void* d_u,
+                                  void* d_delta, float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z,
+                                  int softplus_epilogue, void* workspace, size_t ws_bytes, const ssm_dims* dims,
+                                  int dtype, void* stream, void* const* stage_events) {
+  int rc = check_dims(dims, dtype);
+  if (rc != SSM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ssm_dims dm = *dims;
+  const int n_a = dm.d_inner * dm.d_state;
+  if (dm.d_inner > 0 && (!A_log || !D || !d_A_log || !d_D))
+    return fail(SSM_ERR_INVALID_ARG, "A_log, D, d_A_log and d_D are required");
+  if ((size_t)dm.batch * dm.seqlen * dm.d_inner == 0) return zero_params(d_A_log, d_D, n_a, dm.d_inner, st);
+  if (!u || !delta || !B || !C || !z || !d_out || !d_u || !d_delta || !d_B || !d_C || !d_z)
+    return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C) && aligned4(d_B) && aligned4(d_C)))
+    return fail(SSM_ERR_UNSUPPORTED, "bf16 B, C, d_B and d_C must be 4-byte aligned");
+  const Plan p = make_plan(dm, true);
+  if (!workspace || ws_bytes < p.bytes)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
+  const ScanWs w = bind(p, workspace);
+#define SSM_BWD_CASE(TY, NSV)                                                                                    \
+  return launch_bwd<TY, NSV>(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z, \
+                             softplus_epilogue, p, w, st, stage_events)
+  if (dtype == SSM_F32) {
+    if (dm.d_state == 16) SSM_BWD_CASE(float, 16);
+    if (dm.d_state == 8) SSM_BWD_CASE(float, 8);
+    SSM_BWD_CASE(float, 4);
+  } else {
+    if (dm.d_state == 16) SSM_BWD_CASE(bf16, 16);
+    if (dm.d_state == 8) SSM_BWD_CASE(bf16, 8);
+    SSM_BWD_CASE(bf16, 4);
+  }
+#undef SSM_BWD_CASE
+}
+
+extern "C" int ssm_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                            const float* D, const void* z, void* y, void* out, float* h_ckpt, int ckpt_every,
+                            void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream) {
+  int rc = check_dims(dims, dtype);
+  if (rc != SSM_OK) return rc;
+  const ssm_dims dm = *dims;
+  if ((size_t)dm.batch * dm.seqlen * dm.d_inner == 0) return SSM_OK;
+  if (!u || !delta || !A_log || !B || !C || !D) return fail(SSM_ERR_INVALID_ARG, "an input pointer is null");
+  if (out && !z) return fail(SSM_ERR_INVALID_ARG, "out requires z");
+  if (h_ckpt && (ckpt_every <= 0 || ckpt_every % kChunk != 0))
+    return fail(SSM_ERR_INVALID_ARG, "ckpt_every %d must be a positive multiple of %d", ckpt_every, kChunk);
+  if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C)))
+    return fail(SSM_ERR_UNSUPPORTED, "bf16 B and C must be 4-byte aligned");
+  const Plan p = make_plan(dm, false);
+  if (!workspace || ws_bytes < p.bytes)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
+  const ScanWs w = bind(p, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!h_ckpt) ckpt_every = 0;
+#define SSM_FWD_CASE(TY, NSV) \
+  return launch_fwd<TY, NSV>(u, delta, A_log, B, C, D, z, y, out, h_ckpt, ckpt_every, p, w, st)
+  if (dtype == SSM_F32) {
+    if (dm.d_state == 16) SSM_FWD_CASE(float, 16);
+    if (dm.d_state == 8) SSM_FWD_CASE(float, 8);
+    SSM_FWD_CASE(float, 4);
+  } else {
+    if (dm.d_state == 16) SSM_FWD_CASE(bf16, 16);
+    if (dm.d_state == 8) SSM_FWD_CASE(bf16, 8);
+    SSM_FWD_CASE(bf16, 4);
+  }
+#undef SSM_FWD_CASE
+}

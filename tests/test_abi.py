@@ -1,0 +1,95 @@
+"""The C ABI as seen from the host, without a GPU: the library loads, exports
+every symbol the header declares, and rejects bad arguments before launching."""
+import ctypes
+
+import pytest
+
+ssm = pytest.importorskip("selective_state_space_bwd_amd")
+L = ssm.lib()
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_exports_every_header_symbol():
+    syms = ssm.header_symbols()
+    assert {"ssm_scan_bwd", "ssm_scan_fwd", "gating_bwd", "conv1d_bwd", "rmsnorm_bwd"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings():
+    assert L.ssm_status_string(0) == b"ok"
+    for code in range(1, 5):
+        assert L.ssm_status_string(code) not in (b"ok", b"unknown status")
+    assert L.ssm_status_string(99) == b"unknown status"
+
+
+def _dims(**kw):
+    d = dict(batch=2, seqlen=64, d_inner=32, d_state=16, ld_bc=16, ld_dbc=16, seg_len=0)
+    d.update(kw)
+    return ssm.ssm_dims(**d)
+
+
+def _bwd(dims, ws_bytes=1 << 40, dtype=0, ws=FAKE, **ptrs):
+    p = [ptrs.get(k, FAKE) for k in ("u", "delta", "A_log", "B", "C", "D", "z", "d_out", "d_u", "d_delta",
+                                    "d_A_log", "d_B", "d_C", "d_D", "d_z")]
+    return L.ssm_scan_bwd(*p, 0, ws, ws_bytes, ctypes.byref(dims) if dims is not None else None, dtype, None)
+
+
+def test_workspace_size():
+    assert L.ssm_scan_bwd_workspace_size(ctypes.byref(_dims()), 0) > 0
+    assert L.ssm_scan_bwd_workspace_size(ctypes.byref(_dims(d_state=5)), 0) == 0
+    assert L.ssm_scan_bwd_workspace_size(None, 0) == 0
+    small = L.ssm_scan_bwd_workspace_size(ctypes.byref(_dims(seqlen=64)), 0)
+    big = L.ssm_scan_bwd_workspace_size(ctypes.byref(_dims(seqlen=4096)), 0)
+    assert big > small
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_state=5), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(d_state=32), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(batch=-1), ssm.SSM_ERR_INVALID_ARG),
+    (dict(d_inner=0), ssm.SSM_ERR_INVALID_ARG),
+    (dict(seg_len=12), ssm.SSM_ERR_INVALID_ARG),
+    (dict(ld_bc=8), ssm.SSM_ERR_INVALID_ARG),
+])
+def test_bwd_rejects_bad_dims(kw, code):
+    assert _bwd(_dims(**kw)) == code
+    assert L.ssm_last_error()
+
+
+def test_bwd_rejects_null_and_workspace():
+    assert _bwd(None) == ssm.SSM_ERR_INVALID_ARG
+    assert _bwd(_dims(), u=None) == ssm.SSM_ERR_INVALID_ARG
+    assert _bwd(_dims(), ws_bytes=16) == ssm.SSM_ERR_WORKSPACE
+    assert _bwd(_dims(), ws=None) == ssm.SSM_ERR_WORKSPACE
+    assert _bwd(_dims(), dtype=7) == ssm.SSM_ERR_INVALID_ARG
+    # bf16 rows must have even strides
+    assert _bwd(_dims(ld_bc=17), dtype=1) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_other_entry_points_validate():
+    assert L.gating_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.gating_bwd(None, FAKE, FAKE, FAKE, FAKE, 10, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.gating_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, None) == ssm.SSM_OK   # nothing to do
+    assert L.conv1d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 9, 4, 4, 4, FAKE, 1 << 30, 0,
+                        None) == ssm.SSM_ERR_UNSUPPORTED
+    assert L.conv1d_bwd_workspace_size(1, 8, 4, 9) == 0
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 8192, ctypes.c_float(1e-5), FAKE, 1 << 30, 0,
+                         None) == ssm.SSM_ERR_UNSUPPORTED
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 64, ctypes.c_float(-1.0), FAKE, 1 << 30, 0,
+                         None) == ssm.SSM_ERR_INVALID_ARG
+    dims = _dims()
+    assert L.ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0, FAKE, 1 << 40,
+                          ctypes.byref(dims), 0, None) == ssm.SSM_ERR_INVALID_ARG   # out needs z
+    assert L.ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 12, FAKE, 1 << 40,
+                          ctypes.byref(dims), 0, None) == ssm.SSM_ERR_INVALID_ARG   # ckpt_every % 8
+
+
+def test_binding_has_no_cpu_path():
+    """The Python functions only marshal: without a GPU they fail instead of computing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    x = torch.zeros(1, 8, 4)
+    with pytest.raises(Exception):
+        ssm.ssm_scan_bwd(x, x, torch.zeros(4, 4), torch.zeros(1, 8, 4), torch.zeros(1, 8, 4), torch.ones(4), x, x)
