@@ -109,6 +109,8 @@ def _need(cond: bool, msg: str):
 def _row_stride(x: torch.Tensor, batch: int, seqlen: int, n: int, name: str) -> int:
     """B / C may be [B, T, N] views into a wider row (e.g. the x_proj output)."""
     _need(x.dim() == 3 and tuple(x.shape) == (batch, seqlen, n), f"{name} must be [{batch}, {seqlen}, {n}]")
+    if x.numel() == 0:
+        return n
     _need(x.stride(2) == 1, f"{name} must be contiguous in its last dim")
     ld = x.stride(1) if seqlen > 1 else max(x.stride(1), n)
     _need(batch <= 1 or x.stride(0) == seqlen * ld, f"{name}: rows must be evenly strided")

@@ -207,6 +207,7 @@ def test_forward_outputs_and_checkpoints(dt):
 FULL = ["mamba130m", "mamba370m", "mamba2p8b"]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
     """Full workload on the GPU in the bench's launch configuration; the oracle
