@@ -28,12 +28,14 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ssm {
 
 constexpr int kChunk = 8;    // steps rebuilt and held in registers at a time
-constexpr int kBlock = 256;  // channels per block (4 waves)
+constexpr int kBlock = 256;  // threads (and channels) per block (4 waves)
 
 struct ScanShape {
   int Bt, T, Di, ld_bc, ld_dbc;
@@ -58,6 +60,9 @@ __device__ __forceinline__ void load_A2(const float* __restrict__ A_log, int d, 
 
 // ---------------------------------------------------------------------------
 // 1. segment summaries.  BWD adds the chunk checkpoints and the adjoint summary.
+//
+// Loads of a chunk are all issued before its arithmetic; a full chunk takes a
+// branch-free path.  Lane offsets are 32-bit from per-batch base pointers.
 template <typename T, int NS, bool BWD>
 __global__ __launch_bounds__(kBlock) void scan_summary(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
@@ -76,8 +81,16 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
   for (int n = 0; n < NS; ++n) { h[n] = 0.f; P[n] = 1.f; G[n] = 0.f; }
   float sd = 0.f;
   const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
-  const bool need_g = BWD && s > 0;  // the first segment's adjoint summary is never used
-  const size_t row0 = (size_t)b * sh.T;
+  const size_t bo = (size_t)b * sh.T * Di;
+  const T* __restrict__ ub = u + bo;
+  const T* __restrict__ db = delta + bo;
+  const T* __restrict__ zb = BWD ? z + bo : nullptr;
+  const T* __restrict__ gb = BWD ? dout + bo : nullptr;
+  const T* __restrict__ Bb = Bm + (size_t)b * sh.T * sh.ld_bc;
+  const T* __restrict__ Cb = Cm + (size_t)b * sh.T * sh.ld_bc;
+
+  // the first segment's adjoint summary is never used
+  const bool need_g = BWD && s > 0;
   for (int tc = t0; tc < t1; tc += kChunk) {
     if (BWD && tc > t0 && active) {
       const size_t c = (size_t)b * sh.nchunk + tc / kChunk;
@@ -85,47 +98,47 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
       for (int n = 0; n < NS; ++n) ckpt[(c * NS + n) * Di + d] = h[n];
       ckpt_sd[c * Di + d] = sd;
     }
+    // a ragged last chunk reads its last step again and zeroes the extra steps'
+    // delta, u and dy: a = 1 there, so the state, P and G pass through unchanged
     const int nv = min(kChunk, t1 - tc);
-    float dl[kChunk], uu[kChunk], dy[kChunk];
+    float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      if (j < nv) {
-        const size_t i = (row0 + tc + j) * Di + dc;
-        dl[j] = ld(delta, i);
-        uu[j] = ld(u, i);
-        if (need_g) {
-          const float zz = ld(z, i);
-          dy[j] = ld(dout, i) * zz * sigmoid(zz);
-        }
+      const unsigned off = (unsigned)(tc + min(j, nv - 1)) * Di + dc;
+      dl[j] = ld(db, off);
+      uu[j] = ld(ub, off);
+      if (need_g) {
+        zr[j] = ld(zb, off);
+        gr[j] = ld(gb, off);
       }
     }
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      if (j < nv) {
-        float Bv[NS];
-        load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
-        const float du = dl[j] * uu[j];
-        if (need_g) {
-          float Cv[NS];
-          load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+      const bool ok = j < nv;
+      const float dlj = ok ? dl[j] : 0.f;
+      const int t = tc + min(j, nv - 1);
+      float Bv[NS];
+      load_row<NS>(Bb + (size_t)t * sh.ld_bc, Bv);
+      const float du = ok ? dlj * uu[j] : 0.f;
+      if (need_g) {
+        float Cv[NS];
+        load_row<NS>(Cb + (size_t)t * sh.ld_bc, Cv);
+        const float dy = ok ? gr[j] * zr[j] * sigmoid(zr[j]) : 0.f;
 #pragma unroll
-          for (int n = 0; n < NS; ++n) {
-            const float a = fast_exp2(dl[j] * A2[n]);
-            h[n] = fmaf(a, h[n], du * Bv[n]);
-            P[n] *= a;
-            G[n] = fmaf(P[n], dy[j] * Cv[n], G[n]);
-          }
-        } else {
-#pragma unroll
-          for (int n = 0; n < NS; ++n) {
-            const float a = fast_exp2(dl[j] * A2[n]);
-            h[n] = fmaf(a, h[n], du * Bv[n]);
-          }
+        for (int n = 0; n < NS; ++n) {
+          const float a = fast_exp2(dlj * A2[n]);
+          h[n] = fmaf(a, h[n], du * Bv[n]);
+          P[n] *= a;
+          G[n] = fmaf(P[n], dy * Cv[n], G[n]);
         }
-        sd += dl[j];
+      } else {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = fmaf(fast_exp2(dlj * A2[n]), h[n], du * Bv[n]);
       }
+      sd += dlj;
     }
   }
+
   if (!active) return;
   const size_t sg = (size_t)b * sh.nseg + s;
 #pragma unroll
@@ -137,43 +150,37 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
 }
 
 // ---------------------------------------------------------------------------
-// 2. carries across segments, one thread per channel, in place.
+// 2. carries across segments, one thread per (b, n, d), in place.  Segment s's
+// decay is exp(A * sum of its delta); the forward carry runs over s ascending,
+// the adjoint carry descending.
 template <int NS, bool BWD>
-__global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A_log, ScanWs ws,
+__global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A_log, float* __restrict__ seg_h,
+                                                     float* __restrict__ seg_g, const float* __restrict__ seg_sd,
                                                      ScanShape sh) {
   const int idx = blockIdx.x * kBlock + threadIdx.x;
-  if (idx >= sh.Bt * sh.Di) return;
-  const int b = idx / sh.Di, d = idx - b * sh.Di;
   const int Di = sh.Di;
-  float A2[NS];
-  load_A2<NS>(A_log, d, A2);
-  float H[NS];
-#pragma unroll
-  for (int n = 0; n < NS; ++n) H[n] = 0.f;
+  if (idx >= sh.Bt * NS * Di) return;
+  const int d = idx % Di, n = (idx / Di) % NS, b = idx / (Di * NS);
+  const float A2 = -expf(A_log[(size_t)d * NS + n]) * kLog2e;
+  const size_t sd0 = (size_t)b * sh.nseg * Di + d;
+  const size_t h0 = ((size_t)b * sh.nseg * NS + n) * Di + d;
+  const size_t hs = (size_t)NS * Di;
+  float H = 0.f;
+#pragma unroll 4
   for (int s = 0; s < sh.nseg; ++s) {
-    const size_t sg = (size_t)b * sh.nseg + s;
-    const float sd = ws.seg_sd[sg * Di + d];
-#pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      float* p = ws.seg_h + (sg * NS + n) * Di + d;
-      const float loc = *p;
-      *p = H[n];
-      H[n] = fmaf(fast_exp2(A2[n] * sd), H[n], loc);
-    }
+    const float dec = fast_exp2(A2 * seg_sd[sd0 + (size_t)s * Di]);
+    const float loc = seg_h[h0 + s * hs];
+    seg_h[h0 + s * hs] = H;
+    H = fmaf(dec, H, loc);
   }
   if (!BWD) return;
-#pragma unroll
-  for (int n = 0; n < NS; ++n) H[n] = 0.f;
+  float G = 0.f;
+#pragma unroll 4
   for (int s = sh.nseg - 1; s >= 0; --s) {
-    const size_t sg = (size_t)b * sh.nseg + s;
-    const float sd = ws.seg_sd[sg * Di + d];
-#pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      float* p = ws.seg_g + (sg * NS + n) * Di + d;
-      const float loc = *p;
-      *p = H[n];
-      H[n] = fmaf(fast_exp2(A2[n] * sd), H[n], loc);
-    }
+    const float dec = fast_exp2(A2 * seg_sd[sd0 + (size_t)s * Di]);
+    const float loc = seg_g[h0 + s * hs];
+    seg_g[h0 + s * hs] = G;
+    G = fmaf(dec, G, loc);
   }
 }
 
@@ -246,17 +253,16 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
       }
     }
     // per-step channel values: delta, u, dy = d_out SiLU(z), and the d_z factor
-    float dl[kChunk], uu[kChunk], dy[kChunk], dzf[kChunk];
+    // issue the chunk's loads together; the gate math waits for them step by step
+    float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       if (j < nv) {
         const size_t i = (row0 + tc + j) * Di + dc;
         dl[j] = ld(delta, i);
         uu[j] = ld(u, i);
-        const float zz = ld(z, i), dg = ld(dout, i);
-        const float sz = sigmoid(zz);
-        dy[j] = active ? dg * zz * sz : 0.f;
-        dzf[j] = dg * sz * (1.f + zz * (1.f - sz));
+        zr[j] = ld(z, i);
+        gr[j] = ld(dout, i);
       }
     }
     // forward: rebuild the chunk's states, keep a_t h_{t-1}
@@ -267,6 +273,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
         float Bv[NS], Cv[NS];
         load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
         load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        const float sz = sigmoid(zr[j]);
+        dy[j] = active ? gr[j] * zr[j] * sz : 0.f;
+        const float dzf = gr[j] * sz * (1.f + zr[j] * (1.f - sz));
         const float du = dl[j] * uu[j];
         float y = Dd * uu[j];
         float dC[NS];
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
 #pragma unroll
           for (int n = 0; n < NS; ++n) ah[j >= kLds ? j - kLds : 0][n] = aj[n];
         }
-        if (active) st(d_z, (row0 + tc + j) * Di + d, y * dzf[j]);
+        if (active) st(d_z, (row0 + tc + j) * Di + d, y * dzf);
         wave_reduce_scatter<NS>(dC, lane);
         if ((lane & (kRep - 1)) == 0) red[buf][wave][j][NS + (lane >> (6 - kLogNS))] = dC[0];
       }
@@ -356,12 +365,16 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
 }
 
 // ---------------------------------------------------------------------------
-// 4. fixed-order sums of the partials.
+// 4. fixed-order sums of the partials.  Blocks [0, nblk_bc) sum the d_B | d_C
+// block partials over channel tiles; the rest sum the d_A_log | d_D segment
+// partials of 64 channels of one state, four thread groups taking every fourth
+// partial, combined in LDS in group order.
 template <typename T, int NS>
 __global__ __launch_bounds__(kBlock) void scan_bwd_finalize(
     const float* __restrict__ A_log, T* __restrict__ d_B, T* __restrict__ d_C,
     float* __restrict__ d_A_log, float* __restrict__ d_D, const float* __restrict__ part_bc,
     const float* __restrict__ part_a, ScanShape sh, int nblk_bc) {
+  __shared__ float grp_sum[kBlock / kWave][kWave];
   if ((int)blockIdx.x < nblk_bc) {
     const size_t rows = (size_t)sh.Bt * sh.T;
     const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
@@ -369,18 +382,31 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_finalize(
     const size_t r = idx / (2 * NS);
     const int k = (int)(idx - r * 2 * NS);
     float acc = 0.f;
+#pragma unroll 8
     for (int tile = 0; tile < sh.ntile; ++tile) acc += part_bc[((size_t)tile * rows + r) * 2 * NS + k];
     if (k < NS) st(d_B, r * sh.ld_dbc + k, acc);
     else st(d_C, r * sh.ld_dbc + (k - NS), acc);
   } else {
-    const int idx = (blockIdx.x - nblk_bc) * kBlock + threadIdx.x;
-    if (idx >= (NS + 1) * sh.Di) return;
-    const int n = idx / sh.Di, d = idx - n * sh.Di;
+    const int ndt = (sh.Di + kWave - 1) / kWave;
+    const int blk = blockIdx.x - nblk_bc;
+    const int n = blk / ndt;
+    const int lane = threadIdx.x & (kWave - 1), grp = threadIdx.x / kWave;
+    const int d = (blk - n * ndt) * kWave + lane;
     float acc = 0.f;
-    const int parts = sh.Bt * sh.nseg;
-    for (int p = 0; p < parts; ++p) acc += part_a[((size_t)p * (NS + 1) + n) * sh.Di + d];
-    if (n < NS) d_A_log[(size_t)d * NS + n] = -expf(A_log[(size_t)d * NS + n]) * acc;
-    else d_D[d] = acc;
+    if (d < sh.Di) {
+      const int parts = sh.Bt * sh.nseg;
+#pragma unroll 8
+      for (int p = grp; p < parts; p += kBlock / kWave) acc += part_a[((size_t)p * (NS + 1) + n) * sh.Di + d];
+    }
+    grp_sum[grp][lane] = acc;
+    __syncthreads();
+    if (grp == 0 && d < sh.Di) {
+      float tot = 0.f;
+#pragma unroll
+      for (int g = 0; g < kBlock / kWave; ++g) tot += grp_sum[g][lane];
+      if (n < NS) d_A_log[(size_t)d * NS + n] = -expf(A_log[(size_t)d * NS + n]) * tot;
+      else d_D[d] = tot;
+    }
   }
 }
 
@@ -545,8 +571,8 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
                      w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
   mark(1);
   if (sh.nseg > 1) {
-    const int nb = (sh.Bt * sh.Di + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL((scan_carry<NS, true>), dim3(nb), dim3(kBlock), 0, st, A_log, w, sh);
+    const int nb = (int)(((size_t)sh.Bt * NS * sh.Di + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((scan_carry<NS, true>), dim3(nb), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g, w.seg_sd, sh);
   }
   mark(2);
   if (softplus)
@@ -560,7 +586,7 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
   mark(3);
   const size_t nbc = (size_t)sh.Bt * sh.T * 2 * NS;
   const int nblk_bc = (int)((nbc + kBlock - 1) / kBlock);
-  const int nblk_a = ((NS + 1) * sh.Di + kBlock - 1) / kBlock;
+  const int nblk_a = (NS + 1) * ((sh.Di + kWave - 1) / kWave);
   hipLaunchKernelGGL((scan_bwd_finalize<T, NS>), dim3(nblk_bc + nblk_a), dim3(kBlock), 0, st, A_log,
                      static_cast<T*>(d_B), static_cast<T*>(d_C), d_A_log, d_D, w.part_bc, w.part_a, sh, nblk_bc);
   mark(4);
@@ -580,8 +606,8 @@ int launch_fwd(const void* u, const void* delta, const float* A_log, const void*
   if (sh.nseg > 1) {
     hipLaunchKernelGGL((scan_summary<T, NS, false>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC,
                        (const T*)nullptr, (const T*)nullptr, w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
-    const int nb = (sh.Bt * sh.Di + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL((scan_carry<NS, false>), dim3(nb), dim3(kBlock), 0, st, A_log, w, sh);
+    const int nb = (int)(((size_t)sh.Bt * NS * sh.Di + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((scan_carry<NS, false>), dim3(nb), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g, w.seg_sd, sh);
   }
   const int nckpt = ckpt_every > 0 ? (sh.T + ckpt_every - 1) / ckpt_every : 0;
   hipLaunchKernelGGL((scan_fwd_main<T, NS>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D,
