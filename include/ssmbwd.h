@@ -62,7 +62,10 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * aligned and the strides even.
  * seg_len: length of the time segments that run in parallel and are joined by
  * the cross-segment carries; 0 picks one from the shape.  Must be 0 or a
- * multiple of 8.  Results do not depend on it beyond float rounding. */
+ * multiple of 8.  Results do not depend on it beyond float rounding.
+ * ld_z: row stride of z and d_z (0 means d_inner), so that the gate and its
+ * gradient can be the second half of the in_proj output row [x | z].
+ * seqlen * max(d_inner, ld_z) must stay below 2^32. */
 typedef struct ssm_dims {
   int32_t batch;
   int32_t seqlen;
@@ -71,6 +74,7 @@ typedef struct ssm_dims {
   int32_t ld_bc;
   int32_t ld_dbc;
   int32_t seg_len;
+  int32_t ld_z;
 } ssm_dims;
 
 const char* ssm_status_string(int status);
@@ -167,6 +171,123 @@ size_t rmsnorm_bwd_workspace_size(int64_t rows, int dim);
 int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_residual,
                 void* dx, float* dw, int64_t rows, int dim, float eps, void* workspace,
                 size_t ws_bytes, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * linear_bwd — the weight-layer backward that mamba-rs cpu/backward.rs runs
+ * (sgemm_backward) in Phases B1 (out_proj), B4 (dt_proj, with bias), B5
+ * (x_proj) and B7 (in_proj), for Y = X W^T (+ b) with W [N, K] (out, in):
+ *     dX = dY W            [M, K]   (bf16; added to dX's contents if accumulate_dx)
+ *     dW = dY^T X          [N, K]   (float, overwritten)
+ *     db = sum over rows of dY [N] (float, overwritten)
+ * X [M, K] rows of stride ldx, dY [M, N] rows of stride lddy, dX rows of
+ * stride lddx, W contiguous; all bf16 (dtype must be SSM_BF16), products on the
+ * matrix cores with float accumulation.  dX, dW, db are each nullable (skipped);
+ * X may be null when dW is.  X, W, dY need 16-byte aligned bases and row strides
+ * that are multiples of 8.  Workspace: linear_bwd_workspace_size() (split-k
+ * partial sums; 0 bytes when no split is used).
+ * ------------------------------------------------------------------------- */
+size_t linear_bwd_workspace_size(int64_t M, int K, int N);
+int linear_bwd(const void* X, int64_t ldx, const void* W, const void* dY, int64_t lddy,
+               void* dX, int64_t lddx, int accumulate_dx, float* dW, float* db,
+               int64_t M, int K, int N, void* workspace, size_t ws_bytes, int dtype,
+               void* stream);
+
+/* linear_fwd — Y[M, N] = X[M, K] W[N, K]^T in bf16 with float accumulation (the
+ * forward products whose backward linear_bwd computes; used to build a layer's
+ * saved activations).  bias must be null.  Same alignment rules as linear_bwd.
+ * Workspace: linear_fwd_workspace_size(). */
+size_t linear_fwd_workspace_size(int64_t M, int K, int N);
+int linear_fwd(const void* X, int64_t ldx, const void* W, const float* bias, void* Y,
+               int64_t ldy, int64_t M, int K, int N, void* workspace, size_t ws_bytes,
+               int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The whole Mamba layer around the scan, as mamba-rs cpu/backward.rs
+ * backward_mamba_layer_batched walks it (Phases B1-B8); its forward is read
+ * back from those phases:
+ *     xn    = RMSNorm(x; norm_w, eps)                          (B8)
+ *     xz    = xn W_in^T,  x_b = xz[:, :d_inner], z = xz[:, d_inner:]   (B7)
+ *     u     = SiLU(causal depthwise conv(x_b; conv_w, conv_b))  (B6)
+ *     xdbl  = u W_x^T = [dt_in | B | C]  (dt_rank, d_state, d_state columns)  (B5, B3)
+ *     delta = softplus(dt_in W_dt^T + b_dt), passed through above 20        (B4, B3)
+ *     y     = selective scan(u, delta, A_log, B, C, D)          (B3)
+ *     out   = (y * SiLU(z)) W_out^T + x                         (B2, B1, B8 residual)
+ * Activations [batch, seqlen, *] are bf16 (rows of their own width, no padding);
+ * weight matrices are bf16 [out, in]; norm_w, conv_w [d_inner, d_conv], conv_b,
+ * b_dt, A_log [d_inner, d_state], D and every parameter gradient are float.
+ * d_model, d_inner, dt_rank and dt_rank + 2 d_state must be multiples of 8,
+ * d_state in {4, 8, 16}, d_conv <= 8, d_model <= 4096, all pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+typedef struct ssm_layer_dims {
+  int32_t batch;
+  int32_t seqlen;
+  int32_t d_model;
+  int32_t d_inner;
+  int32_t d_state;
+  int32_t dt_rank;
+  int32_t d_conv;
+  int32_t seg_len; /* the scan's segment length, 0 = auto (see ssm_dims) */
+  float eps;       /* RMSNorm epsilon */
+} ssm_layer_dims;
+
+typedef struct ssm_layer_weights {
+  const float* norm_w; /* [d_model] */
+  const void* W_in;    /* [2 d_inner, d_model] */
+  const float* conv_w; /* [d_inner, d_conv] */
+  const float* conv_b; /* [d_inner] */
+  const void* W_x;     /* [dt_rank + 2 d_state, d_inner] */
+  const void* W_dt;    /* [d_inner, dt_rank] */
+  const float* b_dt;   /* [d_inner] */
+  const float* A_log;  /* [d_inner, d_state] */
+  const float* D;      /* [d_inner] */
+  const void* W_out;   /* [d_model, d_inner] */
+} ssm_layer_weights;
+
+/* what the forward keeps for the backward (everything else is recomputed) */
+typedef struct ssm_layer_saved {
+  void* xz;    /* [batch, seqlen, 2 d_inner] in_proj output */
+  void* xdbl;  /* [batch, seqlen, dt_rank + 2 d_state] x_proj output */
+  void* delta; /* [batch, seqlen, d_inner] softplus output */
+  void* y;     /* [batch, seqlen, d_inner] scan output before the gate */
+} ssm_layer_saved;
+
+typedef struct ssm_layer_grads {
+  float* d_norm_w;
+  float* d_W_in;
+  float* d_conv_w;
+  float* d_conv_b;
+  float* d_W_x;
+  float* d_W_dt;
+  float* d_b_dt;
+  float* d_A_log;
+  float* d_D;
+  float* d_W_out;
+} ssm_layer_grads;
+
+/* mamba_layer_fwd — out [batch, seqlen, d_model] and the saved activations
+ * (all four buffers of `saved` are written).  Workspace:
+ * mamba_layer_fwd_workspace_size(). */
+size_t mamba_layer_fwd_workspace_size(const ssm_layer_dims* dims);
+int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* out, const ssm_layer_saved* saved,
+                    void* workspace, size_t ws_bytes, const ssm_layer_dims* dims, void* stream);
+
+/* mamba_layer_bwd — Phases B1-B8: from x, the saved activations and
+ * d_out = dL/d out, writes d_x = dL/dx (bf16, including the residual path) and
+ * every parameter gradient (float, overwritten).  Recomputes RMSNorm, the conv
+ * + SiLU output, the gate and the scan states on the way.  Workspace:
+ * mamba_layer_bwd_workspace_size().
+ * mamba_layer_bwd_timed: same, recording caller-created hipEvent_t handles
+ * (11, each nullable) around its ten stages: [0] start, then after the gate
+ * recompute, out_proj, conv recompute, scan, dt_proj, x_proj, conv, RMSNorm
+ * recompute, in_proj and RMSNorm backward. */
+size_t mamba_layer_bwd_workspace_size(const ssm_layer_dims* dims);
+int mamba_layer_bwd(const void* x, const ssm_layer_weights* w, const ssm_layer_saved* saved,
+                    const void* d_out, void* d_x, const ssm_layer_grads* grads, void* workspace,
+                    size_t ws_bytes, const ssm_layer_dims* dims, void* stream);
+int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, const ssm_layer_saved* saved,
+                          const void* d_out, void* d_x, const ssm_layer_grads* grads, void* workspace,
+                          size_t ws_bytes, const ssm_layer_dims* dims, void* stream,
+                          void* const* stage_events);
 
 #ifdef __cplusplus
 }

@@ -154,33 +154,61 @@ def layer_forward(p: dict, d_state: int, dt_rank: int, eps: float = 1e-5) -> dic
                 B=Bm, C=Cm, raw=raw, delta=delta, y=y, gated=gated, out=out)
 
 
-def layer_bwd(p: dict, d_out, d_state: int, dt_rank: int, eps: float = 1e-5) -> dict:
-    """Phases B1-B8 in order, all in fp64; returns d_x and every parameter gradient."""
-    act = layer_forward(p, d_state, dt_rank, eps)
+def softplus_inv(delta, threshold: float = 20.0):
+    """The raw dt_proj output that ``softplus_fwd`` maps to ``delta``: log(e^delta - 1),
+    and delta itself above the threshold (where the forward passed raw through)."""
+    delta = _f64(delta)
+    with np.errstate(divide="ignore"):
+        return np.where(delta > threshold, delta, np.log(np.expm1(np.minimum(delta, threshold))))
+
+
+def layer_bwd_saved(p: dict, saved: dict, d_out, d_state: int, dt_rank: int, eps: float = 1e-5) -> dict:
+    """Phases B1-B8 in order, all in fp64, from the activations a forward keeps:
+    x (in ``p``), xz, xdbl, delta and y (in ``saved``).  Everything else the
+    phases read (xn, x_b, z, the conv output c, u, dt_in, B, C, raw, gated) is
+    rebuilt from those, as the layer's forward defines it; raw comes back from
+    delta through the softplus inverse.  Returns d_x and every parameter gradient."""
+    x = _f64(p["x"])
+    di = p["D"].shape[0]
+    xz, xdbl, delta, y = (_f64(saved[k]) for k in ("xz", "xdbl", "delta", "y"))
+    xn = rmsnorm_fwd(x, p["norm_w"], eps)
+    x_b, z = xz[..., :di], xz[..., di:]
+    c = conv1d_fwd(x_b, p["conv_w"], p["conv_b"])
+    u = silu(c)
+    dt_in = xdbl[..., :dt_rank]
+    Bm = xdbl[..., dt_rank:dt_rank + d_state]
+    Cm = xdbl[..., dt_rank + d_state:dt_rank + 2 * d_state]
+    raw = softplus_inv(delta)
+    gated = y * silu(z)
     d_out = _f64(d_out)
     # B1 out_proj
-    d_gated, dW_out, _ = linear_bwd(act["gated"], p["W_out"], d_out)
+    d_gated, dW_out, _ = linear_bwd(gated, p["W_out"], d_out)
     # B2 + B3 gating and scan (the scan oracle does the gating backward itself)
-    s = ssm_scan_bwd(act["u"], act["delta"], p["A_log"], act["B"], act["C"], p["D"],
-                     act["z"], d_gated)
+    s = ssm_scan_bwd(u, delta, p["A_log"], Bm, Cm, p["D"], z, d_gated)
     # softplus backward
-    d_raw = softplus_bwd(act["raw"], s["d_delta"])
+    d_raw = softplus_bwd(raw, s["d_delta"])
     # B4 dt_proj (with bias)
-    d_dt_in, dW_dt, db_dt = linear_bwd(act["dt_in"], p["W_dt"], d_raw)
+    d_dt_in, dW_dt, db_dt = linear_bwd(dt_in, p["W_dt"], d_raw)
     d_xdbl = np.concatenate([d_dt_in, s["d_B"], s["d_C"]], axis=-1)
     # B5 x_proj; d_u collects the scan's and x_proj's contributions
-    d_u_x, dW_x, _ = linear_bwd(act["u"], p["W_x"], d_xdbl)
+    d_u_x, dW_x, _ = linear_bwd(u, p["W_x"], d_xdbl)
     d_u = s["d_u"] + d_u_x
     # B6 SiLU then conv
-    d_c = d_u * silu_grad(act["c"])
-    d_x_b, d_conv_w, d_conv_b = conv1d_bwd(act["x_b"], p["conv_w"], d_c)
+    d_c = d_u * silu_grad(c)
+    d_x_b, d_conv_w, d_conv_b = conv1d_bwd(x_b, p["conv_w"], d_c)
     # B7 in_proj on the concat [d_x_b | d_z]
     d_xz = np.concatenate([d_x_b, s["d_z"]], axis=-1)
-    d_xn, dW_in, _ = linear_bwd(act["xn"], p["W_in"], d_xz)
+    d_xn, dW_in, _ = linear_bwd(xn, p["W_in"], d_xz)
     # B8 RMSNorm + residual
-    d_x_norm, d_norm_w = rmsnorm_bwd(act["x"], p["norm_w"], d_xn, eps)
+    d_x_norm, d_norm_w = rmsnorm_bwd(x, p["norm_w"], d_xn, eps)
     return {
         "d_x": d_out + d_x_norm, "d_norm_w": d_norm_w, "d_W_in": dW_in,
         "d_conv_w": d_conv_w, "d_conv_b": d_conv_b, "d_W_x": dW_x, "d_W_dt": dW_dt,
         "d_b_dt": db_dt, "d_A_log": s["d_A_log"], "d_D": s["d_D"], "d_W_out": dW_out,
     }
+
+
+def layer_bwd(p: dict, d_out, d_state: int, dt_rank: int, eps: float = 1e-5) -> dict:
+    """The layer's gradient at p: the fp64 forward, then Phases B1-B8 from its activations."""
+    act = layer_forward(p, d_state, dt_rank, eps)
+    return layer_bwd_saved(p, act, d_out, d_state, dt_rank, eps)

@@ -26,7 +26,30 @@ SSM_F32, SSM_BF16 = 0, 1
 
 class ssm_dims(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
-                ("batch", "seqlen", "d_inner", "d_state", "ld_bc", "ld_dbc", "seg_len")]
+                ("batch", "seqlen", "d_inner", "d_state", "ld_bc", "ld_dbc", "seg_len", "ld_z")]
+
+
+class ssm_layer_dims(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("batch", "seqlen", "d_model", "d_inner", "d_state", "dt_rank", "d_conv", "seg_len")] + \
+               [("eps", ctypes.c_float)]
+
+
+LAYER_WEIGHTS = ("norm_w", "W_in", "conv_w", "conv_b", "W_x", "W_dt", "b_dt", "A_log", "D", "W_out")
+LAYER_SAVED = ("xz", "xdbl", "delta", "y")
+LAYER_GRADS = tuple("d_" + k for k in LAYER_WEIGHTS)  # same order as ssm_layer_grads
+
+
+class ssm_layer_weights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_WEIGHTS]
+
+
+class ssm_layer_saved(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_SAVED]
+
+
+class ssm_layer_grads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_GRADS]
 
 
 _vp, _fp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -47,6 +70,19 @@ _SIGS = {
     "conv1d_bwd": (_i, [_vp, _fp, _fp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
     "rmsnorm_bwd_workspace_size": (_sz, [_i64, _i]),
     "rmsnorm_bwd": (_i, [_vp, _fp, _vp, _vp, _vp, _fp, _i64, _i, ctypes.c_float, _vp, _sz, _i, _vp]),
+    "linear_bwd_workspace_size": (_sz, [_i64, _i, _i]),
+    "linear_bwd": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i, _fp, _fp, _i64, _i, _i, _vp, _sz, _i, _vp]),
+    "linear_fwd_workspace_size": (_sz, [_i64, _i, _i]),
+    "mamba_layer_fwd_workspace_size": (_sz, [ctypes.POINTER(ssm_layer_dims)]),
+    "mamba_layer_fwd": (_i, [_vp, ctypes.POINTER(ssm_layer_weights), _vp, ctypes.POINTER(ssm_layer_saved), _vp, _sz,
+                             ctypes.POINTER(ssm_layer_dims), _vp]),
+    "mamba_layer_bwd_workspace_size": (_sz, [ctypes.POINTER(ssm_layer_dims)]),
+    "mamba_layer_bwd": (_i, [_vp, ctypes.POINTER(ssm_layer_weights), ctypes.POINTER(ssm_layer_saved), _vp, _vp,
+                             ctypes.POINTER(ssm_layer_grads), _vp, _sz, ctypes.POINTER(ssm_layer_dims), _vp]),
+    "mamba_layer_bwd_timed": (_i, [_vp, ctypes.POINTER(ssm_layer_weights), ctypes.POINTER(ssm_layer_saved), _vp, _vp,
+                                   ctypes.POINTER(ssm_layer_grads), _vp, _sz, ctypes.POINTER(ssm_layer_dims), _vp,
+                                   ctypes.POINTER(ctypes.c_void_p)]),
+    "linear_fwd": (_i, [_vp, _i64, _vp, _fp, _vp, _i64, _i64, _i, _i, _vp, _sz, _i, _vp]),
 }
 
 
@@ -131,7 +167,7 @@ def scan_dims(u, B, d_state=None, seg_len=0, ld_dbc=None) -> ssm_dims:
     batch, seqlen, d_inner = u.shape
     n = d_state if d_state is not None else B.shape[2]
     ld = _row_stride(B, batch, seqlen, n, "B")
-    return ssm_dims(batch, seqlen, d_inner, n, ld, ld_dbc if ld_dbc is not None else n, seg_len)
+    return ssm_dims(batch, seqlen, d_inner, n, ld, ld_dbc if ld_dbc is not None else n, seg_len, 0)
 
 
 def ssm_scan_bwd_workspace_size(dims: ssm_dims, dtype: torch.dtype) -> int:
@@ -148,8 +184,10 @@ def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool 
     dt = _dtype_code(u)
     batch, seqlen, d_inner = u.shape
     n = A_log.shape[1]
-    for name, t in (("delta", delta), ("z", z), ("d_out", d_out)):
+    for name, t in (("delta", delta), ("d_out", d_out)):
         _need(t.shape == u.shape and t.dtype == u.dtype and t.is_contiguous(), f"{name} must match u")
+    _need(z.dtype == u.dtype, "z must have u's dtype")
+    ldz = _row_stride(z, batch, seqlen, d_inner, "z")
     _need(u.is_contiguous(), "u must be contiguous")
     _need(B.dtype == u.dtype and C.dtype == u.dtype, "B and C must have u's dtype")
     _need(A_log.dtype == torch.float32 and D.dtype == torch.float32, "A_log and D are float32")
@@ -158,15 +196,18 @@ def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool 
     _need(_row_stride(C, batch, seqlen, n, "C") == ld, "B and C must share a row stride")
     o = dict(out or {})
     dev = u.device
-    for k in ("d_u", "d_delta", "d_z"):
+    for k in ("d_u", "d_delta"):
         o.setdefault(k, torch.empty_like(u))
+    if "d_z" not in o:
+        o["d_z"] = torch.empty((batch, seqlen, ldz), dtype=u.dtype, device=dev)[..., :d_inner]
+    _need(_row_stride(o["d_z"], batch, seqlen, d_inner, "d_z") == ldz, "d_z must share z's row stride")
     o.setdefault("d_A_log", torch.empty_like(A_log))
     o.setdefault("d_D", torch.empty_like(D))
     o.setdefault("d_B", torch.empty((batch, seqlen, n), dtype=u.dtype, device=dev))
     o.setdefault("d_C", torch.empty((batch, seqlen, n), dtype=u.dtype, device=dev))
     ldd = _row_stride(o["d_B"], batch, seqlen, n, "d_B")
     _need(_row_stride(o["d_C"], batch, seqlen, n, "d_C") == ldd, "d_B and d_C must share a row stride")
-    dims = ssm_dims(batch, seqlen, d_inner, n, ld, ldd, seg_len)
+    dims = ssm_dims(batch, seqlen, d_inner, n, ld, ldd, seg_len, ldz)
     nbytes = int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(dims), dt))
     ws, wsb = _workspace(nbytes, dev, workspace)
     args = (_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(d_out),
@@ -198,7 +239,8 @@ def ssm_scan_fwd(u, delta, A_log, B, C, D, z=None, *, want_y: bool = True, want_
     if ckpt_every:
         nk = (seqlen + ckpt_every - 1) // ckpt_every
         ck = torch.empty((batch, nk, n, d_inner), dtype=torch.float32, device=u.device)
-    dims = ssm_dims(batch, seqlen, d_inner, n, ld, n, seg_len)
+    ldz = _row_stride(z, batch, seqlen, d_inner, "z") if z is not None else 0
+    dims = ssm_dims(batch, seqlen, d_inner, n, ld, n, seg_len, ldz)
     nbytes = int(lib().ssm_scan_fwd_workspace_size(ctypes.byref(dims), dt))
     ws, wsb = _workspace(nbytes, u.device, workspace)
     rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _ptr(o),
@@ -264,3 +306,158 @@ def rmsnorm_bwd(x, w, dy, d_residual=None, eps: float = 1e-5, *, workspace=None)
     _check("rmsnorm_bwd", lib().rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(d_residual), _ptr(dx), _ptr(dw), rows,
                                            dim, ctypes.c_float(eps), _ptr(ws), wsb, dt, _stream(x)))
     return dx, dw
+
+
+def _matrix(x: torch.Tensor, name: str):
+    """View [..., cols] bf16 with contiguous rows as a matrix: returns (rows, cols, row stride)."""
+    _need(x.dtype == torch.bfloat16, f"{name} must be bfloat16")
+    _need(x.dim() >= 2 and (x.stride(-1) == 1 or x.shape[-1] <= 1), f"{name} must have contiguous rows")
+    cols = x.shape[-1]
+    rows = 1
+    for s_ in x.shape[:-1]:
+        rows *= s_
+    lead = [d_ for d_ in range(x.dim() - 1) if x.shape[d_] > 1]
+    ld = x.stride(lead[-1]) if lead else cols
+    step = ld
+    for d_ in reversed(lead):  # leading dims must collapse onto rows of stride ld
+        _need(x.stride(d_) == step, f"{name}: rows must be evenly strided")
+        step *= x.shape[d_]
+    return rows, cols, ld
+
+
+def linear_bwd(X, W, dY, *, need_dx: bool = True, need_dw: bool = True, need_db: bool = False, dX=None,
+               accumulate_dx: bool = False, workspace=None):
+    """Backward of Y = X W^T (+ b): returns (dX bf16, dW float32, db float32), None where not asked.
+
+    X [..., K] and dY [..., N] may be views with strided rows (e.g. column slices of a wider
+    activation); W is [N, K] contiguous bf16.  ``dX`` may be given (and is accumulated into
+    when ``accumulate_dx``).
+    """
+    N, K = W.shape
+    _need(W.dtype == torch.bfloat16 and W.is_contiguous(), "W must be contiguous bf16 [N, K]")
+    M, n2, lddy = _matrix(dY, "dY")
+    _need(n2 == N, "dY's last dim must be W's rows")
+    ldx = 0
+    if need_dw:
+        mx, k2, ldx = _matrix(X, "X")
+        _need(mx == M and k2 == K, "X must be [M, K]")
+    dev = dY.device
+    lddx = 0
+    if need_dx:
+        if dX is None:
+            _need(not accumulate_dx, "accumulate_dx needs dX")
+            dX = torch.empty(tuple(dY.shape[:-1]) + (K,), dtype=torch.bfloat16, device=dev)
+        mx, k2, lddx = _matrix(dX, "dX")
+        _need(mx == M and k2 == K, "dX must be [M, K]")
+    else:
+        dX = None
+    dW = torch.empty((N, K), dtype=torch.float32, device=dev) if need_dw else None
+    db = torch.empty((N,), dtype=torch.float32, device=dev) if need_db else None
+    nbytes = int(lib().linear_bwd_workspace_size(M, K, N))
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    _check("linear_bwd", lib().linear_bwd(_ptr(X) if need_dw else None, ldx, _ptr(W), _ptr(dY), lddy, _ptr(dX),
+                                         lddx, int(bool(accumulate_dx)), _ptr(dW), _ptr(db), M, K, N, _ptr(ws), wsb,
+                                         SSM_BF16, _stream(dY)))
+    return dX, dW, db
+
+
+def linear_fwd(X, W, *, Y=None, workspace=None):
+    """Y = X W^T in bf16 (float accumulation); X [..., K] with contiguous rows, W [N, K]."""
+    N, K = W.shape
+    _need(W.dtype == torch.bfloat16 and W.is_contiguous(), "W must be contiguous bf16 [N, K]")
+    M, k2, ldx = _matrix(X, "X")
+    _need(k2 == K, "X's last dim must be W's columns")
+    if Y is None:
+        Y = torch.empty(tuple(X.shape[:-1]) + (N,), dtype=torch.bfloat16, device=X.device)
+    my, n2, ldy = _matrix(Y, "Y")
+    _need(my == M and n2 == N, "Y must be [M, N]")
+    nbytes = int(lib().linear_fwd_workspace_size(M, K, N))
+    ws, wsb = _workspace(nbytes, X.device, workspace)
+    _check("linear_fwd", lib().linear_fwd(_ptr(X), ldx, _ptr(W), None, _ptr(Y), ldy, M, K, N, _ptr(ws), wsb,
+                                         SSM_BF16, _stream(X)))
+    return Y
+
+
+# ---- the whole layer -------------------------------------------------------------
+_LAYER_BF16 = ("W_in", "W_x", "W_dt", "W_out")
+
+
+def layer_dims(x, weights: dict, *, eps: float = 1e-5, seg_len: int = 0) -> ssm_layer_dims:
+    batch, seqlen, d_model = x.shape
+    d_inner, d_state = weights["A_log"].shape
+    return ssm_layer_dims(batch, seqlen, d_model, d_inner, d_state, weights["W_dt"].shape[1],
+                          weights["conv_w"].shape[1], seg_len, eps)
+
+
+def _layer_weights(weights: dict, dims: ssm_layer_dims):
+    di, dm, R, N, K = dims.d_inner, dims.d_model, dims.dt_rank, dims.d_state, dims.d_conv
+    shapes = {"norm_w": (dm,), "W_in": (2 * di, dm), "conv_w": (di, K), "conv_b": (di,), "W_x": (R + 2 * N, di),
+              "W_dt": (di, R), "b_dt": (di,), "A_log": (di, N), "D": (di,), "W_out": (dm, di)}
+    for k, shp in shapes.items():
+        t = weights.get(k)
+        if t is None and k in ("conv_b", "b_dt"):
+            continue
+        _need(t is not None and tuple(t.shape) == shp and t.is_contiguous(), f"{k} must be contiguous {shp}")
+        _need(t.dtype == (torch.bfloat16 if k in _LAYER_BF16 else torch.float32),
+              f"{k} must be {'bfloat16' if k in _LAYER_BF16 else 'float32'}")
+    return ssm_layer_weights(*[ctypes.c_void_p(weights[k].data_ptr()) if weights.get(k) is not None else None
+                               for k in LAYER_WEIGHTS])
+
+
+def mamba_layer_fwd(x, weights: dict, *, eps: float = 1e-5, seg_len: int = 0, workspace=None):
+    """Layer forward on bf16 activations: returns (out, saved) with saved = {xz, xdbl, delta, y}."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.is_contiguous(), "x must be contiguous bf16 [B, T, d_model]")
+    dims = layer_dims(x, weights, eps=eps, seg_len=seg_len)
+    w = _layer_weights(weights, dims)
+    B_, T_, di, R2 = dims.batch, dims.seqlen, dims.d_inner, dims.dt_rank + 2 * dims.d_state
+    saved = {"xz": torch.empty((B_, T_, 2 * di), dtype=torch.bfloat16, device=x.device),
+             "xdbl": torch.empty((B_, T_, R2), dtype=torch.bfloat16, device=x.device),
+             "delta": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=x.device),
+             "y": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=x.device)}
+    out = torch.empty_like(x)
+    sv = ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED])
+    nbytes = int(lib().mamba_layer_fwd_workspace_size(ctypes.byref(dims)))
+    _need(nbytes > 0, "unsupported layer shape: " + (lib().ssm_last_error() or b"").decode())
+    ws, wsb = _workspace(nbytes, x.device, workspace)
+    _check("mamba_layer_fwd", lib().mamba_layer_fwd(_ptr(x), ctypes.byref(w), _ptr(out), ctypes.byref(sv), _ptr(ws),
+                                                   wsb, ctypes.byref(dims), _stream(x)))
+    return out, saved
+
+
+def mamba_layer_bwd_workspace_size(x, weights: dict, **kw) -> int:
+    return int(lib().mamba_layer_bwd_workspace_size(ctypes.byref(layer_dims(x, weights, **kw))))
+
+
+def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, seg_len: int = 0, workspace=None,
+                    out: dict | None = None, stage_events=None) -> dict:
+    """Layer backward (Phases B1-B8): returns d_x (bf16) and every parameter gradient (float32)."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.is_contiguous(), "x must be contiguous bf16 [B, T, d_model]")
+    _need(d_out.shape == x.shape and d_out.dtype == x.dtype and d_out.is_contiguous(), "d_out must match x")
+    dims = layer_dims(x, weights, eps=eps, seg_len=seg_len)
+    w = _layer_weights(weights, dims)
+    B_, T_, di, R2 = dims.batch, dims.seqlen, dims.d_inner, dims.dt_rank + 2 * dims.d_state
+    want = {"xz": (B_, T_, 2 * di), "xdbl": (B_, T_, R2), "delta": (B_, T_, di), "y": (B_, T_, di)}
+    for k, shp in want.items():
+        t = saved[k]
+        _need(tuple(t.shape) == shp and t.dtype == torch.bfloat16 and t.is_contiguous(), f"saved {k} must be {shp}")
+    sv = ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED])
+    o = dict(out or {})
+    o.setdefault("d_x", torch.empty_like(x))
+    for k in LAYER_WEIGHTS:
+        ref = weights.get(k)
+        if ref is None:
+            ref = weights["D"]
+        o.setdefault("d_" + k, torch.empty(ref.shape, dtype=torch.float32, device=x.device))
+    g = ssm_layer_grads(*[ctypes.c_void_p(o[k].data_ptr()) for k in LAYER_GRADS])
+    nbytes = int(lib().mamba_layer_bwd_workspace_size(ctypes.byref(dims)))
+    _need(nbytes > 0, "unsupported layer shape: " + (lib().ssm_last_error() or b"").decode())
+    ws, wsb = _workspace(nbytes, x.device, workspace)
+    args = (_ptr(x), ctypes.byref(w), ctypes.byref(sv), _ptr(d_out), _ptr(o["d_x"]), ctypes.byref(g), _ptr(ws), wsb,
+            ctypes.byref(dims), _stream(x))
+    if stage_events is None:
+        rc = lib().mamba_layer_bwd(*args)
+    else:
+        ev = (ctypes.c_void_p * 11)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
+        rc = lib().mamba_layer_bwd_timed(*args, ev)
+    _check("mamba_layer_bwd", rc)
+    return o

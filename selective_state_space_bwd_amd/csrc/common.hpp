@@ -135,5 +135,21 @@ int check_launch(const char* what);
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- launchers shared between translation units (arguments already checked) --
+// gemm.hip: C = opA * opB on bf16 operands (k contiguous or strided per operand)
+size_t gemm_workspace_bytes(int M, int N, int K);
+int gemm_check(const void* A, long long lda, const void* B, long long ldb, const void* C, int M, int N, int K,
+               size_t ws_bytes, const void* workspace);
+int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool b_kcontig, long long ldb, void* C,
+              long long ldc, int out_dtype, int M, int N, int K, int accumulate, void* workspace, hipStream_t st);
+// pointwise.hip: zero fill and the layer's forward pieces
+void launch_fill_zero(float* p, int64_t n, hipStream_t st);
+void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, int dim, float eps, hipStream_t st);
+void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* bias, bf16* u, int ld_u, int Bt,
+                          int Tn, int Di, int K, hipStream_t st);
+void launch_gate_fwd(const bf16* y, const bf16* z, int ld_z, bf16* g, int64_t rows, int Di, hipStream_t st);
+void launch_bias_softplus(bf16* v, const float* b, int64_t rows, int Di, hipStream_t st);
 
 }  // namespace ssm

@@ -1,0 +1,354 @@
+// bf16 GEMM on the gfx950 matrix cores for the layer's linear layers
+// (mamba-rs cpu/backward.rs, the sgemm_backward calls of Phases B1, B4, B5, B7,
+// and the matching forward products).
+//
+//   C[M, N] (+)= sum_k opA(m, k) * opB(k, n),   fp32 accumulation
+//   opA(m, k) = A[m * lda + k]  (A_K: k contiguous)  or  A[k * lda + m]
+//   opB(k, n) = B[n * ldb + k]  (B_K: k contiguous)  or  B[k * ldb + n]
+//
+// Block tile 128 x 128 x 32, four waves in a 2 x 2 grid, each wave 64 x 64 as
+// 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  Tiles are staged in LDS with k
+// contiguous (operands whose k is strided are transposed on the way in), double
+// buffered: the next tile's global loads are in flight while the matrix cores
+// work on the current one, one barrier per k step.  Split-k writes fp32 partial
+// tiles that a second kernel sums in a fixed order.
+#include "common.hpp"
+
+namespace ssm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row (16 B of padding)
+constexpr int kGemmThreads = 256;
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;          // float or bf16, row stride ldc
+  float* partial;   // split-k partials [splits, M, N] (ldc = N), or null
+  long long lda, ldb, ldc;
+  int M, N, K;
+  int k_per_split;  // multiple of kBK
+  int accumulate;   // add into C instead of overwriting (single split only)
+};
+
+// one 16-byte chunk (8 bf16) of a tile from global memory, zero outside [0, rows) x [0, cols)
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ p, long long ld, int r, int c, int rows,
+                                            int cols) {
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (r < rows) {
+    const uint16_t* q = p + (long long)r * ld + c;
+    if (c + 8 <= cols) {
+      v = *reinterpret_cast<const uint4*>(q);
+    } else {
+      uint16_t t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = (c + i < cols) ? q[i] : uint16_t(0);
+      v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16), t[4] | (uint32_t(t[5]) << 16),
+                     t[6] | (uint32_t(t[7]) << 16));
+    }
+  }
+  return v;
+}
+
+// two adjacent bf16 (tile rows r, r+1 at one k) as one dword, zero outside the matrix
+__device__ __forceinline__ uint32_t load_pair(const uint16_t* __restrict__ p, long long ld, int k, int r, int kend,
+                                              int rows) {
+  if (k >= kend || r >= rows) return 0u;
+  const uint16_t* q = p + (long long)k * ld + r;
+  if (r + 1 < rows) return *reinterpret_cast<const uint32_t*>(q);
+  return q[0];
+}
+
+// Loads of one 128 x 32 operand tile into registers, then into LDS as [row][k].
+// KC: the operand's k is contiguous in memory; a thread moves two 16-byte
+// chunks of 8 k.  Otherwise a thread holds tile rows (2p, 2p+1) at 8
+// consecutive k (eight dword loads, each wave reading 256 contiguous bytes per
+// k) and repacks them into one 16-byte LDS row segment per tile row.
+template <bool KC>
+struct TileLoader {
+  uint32_t v[8];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long long ld, int row0, int k0, int rows,
+                                       int kend, int tid) {
+    if (KC) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {  // 128 rows x 4 chunks of 8 k
+        const int c = tid + q * kGemmThreads;
+        const int r = c >> 2, kc = (c & 3) * 8;
+        const uint4 w = load_chunk(base, ld, row0 + r, k0 + kc, rows, kend);
+        v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+      }
+    } else {
+      const int r = row0 + 2 * (tid & 63), k = k0 + 8 * (tid >> 6);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = load_pair(base, ld, k + i, r, kend, rows);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* __restrict__ lds, int tid) const {
+    if (KC) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = tid + q * kGemmThreads;
+        const int r = c >> 2, kc = (c & 3) * 8;
+        *reinterpret_cast<uint4*>(lds + r * kLdsRow + kc) = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+    } else {
+      const int r = 2 * (tid & 63), kc = 8 * (tid >> 6);
+      uint4 lo, hi;  // row r takes the low halves, row r + 1 the high halves
+      lo.x = (v[0] & 0xffffu) | (v[1] << 16); hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
+      lo.y = (v[2] & 0xffffu) | (v[3] << 16); hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
+      lo.z = (v[4] & 0xffffu) | (v[5] << 16); hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
+      lo.w = (v[6] & 0xffffu) | (v[7] << 16); hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
+      *reinterpret_cast<uint4*>(lds + r * kLdsRow + kc) = lo;
+      *reinterpret_cast<uint4*>(lds + (r + 1) * kLdsRow + kc) = hi;
+    }
+  }
+};
+
+template <bool A_K, bool B_K, typename OutT>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __align__(16) uint16_t lds_a[2][kBM * kLdsRow];
+  __shared__ __align__(16) uint16_t lds_b[2][kBN * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int kb = blockIdx.z * g.k_per_split;
+  const int ke = min(g.K, kb + g.k_per_split);
+  const int nk = (ke - kb + kBK - 1) / kBK;
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  TileLoader<A_K> la;
+  TileLoader<B_K> lb;
+  la.load(g.A, g.lda, m0, kb, g.M, ke, tid);
+  lb.load(g.B, g.ldb, n0, kb, g.N, ke, tid);
+  la.store(lds_a[0], tid);
+  lb.store(lds_b[0], tid);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      la.load(g.A, g.lda, m0, kb + (kt + 1) * kBK, g.M, ke, tid);
+      lb.load(g.B, g.ldb, n0, kb + (kt + 1) * kBK, g.N, ke, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8_t fa[2], fb[2];
+      const int kofs = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&lds_a[cur][r * kLdsRow + kofs]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + (lane & 31);
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(&lds_b[cur][r * kLdsRow + kofs]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      la.store(lds_a[cur ^ 1], tid);
+      lb.store(lds_b[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+  // accumulator layout of the 32 x 32 tile: register r of lane l holds
+  // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= g.M) continue;
+        const float v = acc[i][j][r];
+        if (g.partial) {
+          g.partial[((long long)blockIdx.z * g.M + row) * g.N + col] = v;
+        } else {
+          OutT* c = static_cast<OutT*>(g.C) + (long long)row * g.ldc + col;
+          const float prev = g.accumulate ? to_f32(*c) : 0.f;
+          *c = from_f32<OutT>(prev + v);
+        }
+      }
+    }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, OutT* __restrict__ C,
+                                                     long long ldc, int M, int N, int splits, int accumulate) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)M * N) return;
+  const int row = (int)(idx / N), col = (int)(idx - (long long)row * N);
+  float acc = 0.f;
+  for (int s = 0; s < splits; ++s) acc += part[(long long)s * M * N + idx];
+  OutT* c = C + (long long)row * ldc + col;
+  *c = from_f32<OutT>((accumulate ? to_f32(*c) : 0.f) + acc);
+}
+
+// column sums of a [M, N] bf16/f32 matrix (bias gradient), fixed order: a block
+// owns 64 columns, 4 row groups, combined in LDS
+template <typename T>
+__global__ __launch_bounds__(256) void column_sum(const T* __restrict__ X, long long ldx, int M, int N,
+                                                  float* __restrict__ out) {
+  __shared__ float s[4][64];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
+  float acc = 0.f;
+  if (col < N)
+    for (int r = grp; r < M; r += 4) acc += ld(X, (size_t)r * ldx + col);
+  s[grp][lane] = acc;
+  __syncthreads();
+  if (grp == 0 && col < N) out[col] = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
+}
+
+namespace {
+
+// how many k splits: enough blocks to cover the chip, each split at least 4 k steps
+int pick_splits(int M, int N, int K) {
+  const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  int s = 1;
+  while (tiles * s * 2 <= 1024 && (K / (s * 2)) >= 4 * kBK) s *= 2;
+  return s;
+}
+
+template <bool A_K, bool B_K, typename OutT>
+int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) {
+  GemmArgs g = g0;
+  const int ksplit = max(kBK, ((g.K + splits - 1) / splits + kBK - 1) / kBK * kBK);
+  g.k_per_split = ksplit;
+  const int nsplit = (g.K + ksplit - 1) / ksplit;
+  dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM, nsplit);
+  if (nsplit > 1) {
+    g.partial = partial;
+    hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT>), grid, dim3(kGemmThreads), 0, st, g);
+    const long long n = (long long)g.M * g.N;
+    hipLaunchKernelGGL((splitk_reduce<OutT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
+                       static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
+  } else {
+    g.partial = nullptr;
+    hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT>), grid, dim3(kGemmThreads), 0, st, g);
+  }
+  return SSM_OK;
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int M, int N, int K) {
+  const int s = pick_splits(M, N, K);
+  return s > 1 ? align_up((size_t)s * M * N * sizeof(float)) : 0;
+}
+
+// argument checks of one product, before anything is launched
+int gemm_check(const void* A, long long lda, const void* B, long long ldb, const void* C, int M, int N, int K,
+               size_t ws_bytes, const void* workspace) {
+  if (M == 0 || N == 0) return SSM_OK;
+  if (!A || !B || !C) return fail(SSM_ERR_INVALID_ARG, "gemm: null operand");
+  if (!aligned16(A) || !aligned16(B) || (lda & 7) || (ldb & 7))
+    return fail(SSM_ERR_UNSUPPORTED, "gemm: operands must be 16-byte aligned with row strides multiple of 8");
+  const size_t need = K > 0 ? gemm_workspace_bytes(M, N, K) : 0;
+  if (need && (!workspace || ws_bytes < need)) return fail(SSM_ERR_WORKSPACE, "gemm: workspace too small for split-k");
+  return SSM_OK;
+}
+
+// C (f32 or bf16 per out_dtype) = opA * opB; see the file comment for the layouts.
+// The caller has run gemm_check on the same arguments.
+int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool b_kcontig, long long ldb, void* C,
+              long long ldc, int out_dtype, int M, int N, int K, int accumulate, void* workspace, hipStream_t st) {
+  if (M == 0 || N == 0) return SSM_OK;
+  GemmArgs g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, nullptr, lda, ldb, ldc, M, N, K,
+             0, accumulate};
+  const int splits = K > 0 ? pick_splits(M, N, K) : 1;
+  float* part = static_cast<float*>(workspace);
+#define GEMM_CASE(AK, BK)                                                                      \
+  if (a_kcontig == AK && b_kcontig == BK) {                                                    \
+    if (out_dtype == SSM_F32) return launch_gemm<AK, BK, float>(g, splits, part, st);          \
+    return launch_gemm<AK, BK, bf16>(g, splits, part, st);                                     \
+  }
+  GEMM_CASE(true, true)
+  GEMM_CASE(true, false)
+  GEMM_CASE(false, true)
+  GEMM_CASE(false, false)
+#undef GEMM_CASE
+  return fail(SSM_ERR_INVALID_ARG, "gemm: layout");
+}
+
+int column_sum_launch(const void* X, long long ldx, int M, int N, int dtype, float* out, hipStream_t st) {
+  const dim3 grid((N + 63) / 64);
+  if (dtype == SSM_F32)
+    hipLaunchKernelGGL(column_sum<float>, grid, dim3(256), 0, st, static_cast<const float*>(X), ldx, M, N, out);
+  else
+    hipLaunchKernelGGL(column_sum<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(X), ldx, M, N, out);
+  return SSM_OK;
+}
+
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" size_t linear_bwd_workspace_size(int64_t M, int K, int N) {
+  if (M <= 0 || K <= 0 || N <= 0 || M >= (1LL << 31)) return 0;
+  // dX = dY W   (M x K, reduction N) and dW = dY^T X (N x K, reduction M)
+  return gemm_workspace_bytes((int)M, K, N) > gemm_workspace_bytes(N, K, (int)M)
+             ? gemm_workspace_bytes((int)M, K, N)
+             : gemm_workspace_bytes(N, K, (int)M);
+}
+
+extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void* dY, int64_t lddy, void* dX,
+                          int64_t lddx, int accumulate_dx, float* dW, float* db, int64_t M, int K, int N,
+                          void* workspace, size_t ws_bytes, int dtype, void* stream) {
+  if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "linear_bwd runs on bf16 operands");
+  if (M < 0 || K <= 0 || N <= 0 || M >= (1LL << 31))
+    return fail(SSM_ERR_INVALID_ARG, "bad size (M %lld K %d N %d)", (long long)M, K, N);
+  if ((dW && ldx < K) || lddy < N || (dX && lddx < K)) return fail(SSM_ERR_INVALID_ARG, "row strides below the row length");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) {  // dX is empty; dW and db are sums over no rows
+    if (dW) launch_fill_zero(dW, (int64_t)N * K, st);
+    if (db) launch_fill_zero(db, N, st);
+    return check_launch("linear_bwd (no rows)");
+  }
+  if (!W || !dY || (dW && !X)) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  const int m = (int)M;
+  int rc = SSM_OK;
+  // dX[M, K] = dY[M, N] W[N, K]: A = dY (k = n contiguous), B(k = n, j) = W[n * K + j]
+  if (dX && (rc = gemm_check(dY, lddy, W, K, dX, m, K, N, ws_bytes, workspace)) != SSM_OK) return rc;
+  // dW[N, K] = dY^T X: A(i = n, k = m) = dY[m * lddy + n], B(k = m, j) = X[m * ldx + j]
+  if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
+  if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, accumulate_dx, workspace, st);
+  if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, 0, workspace, st);
+  if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, st);
+  return check_launch("linear_bwd");
+}
+
+extern "C" int linear_fwd(const void* X, int64_t ldx, const void* W, const float* bias, void* Y, int64_t ldy,
+                          int64_t M, int K, int N, void* workspace, size_t ws_bytes, int dtype, void* stream) {
+  if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "linear_fwd runs on bf16 operands");
+  if (M < 0 || M >= (1LL << 31) || K <= 0 || N <= 0 || ldx < K || ldy < N) return fail(SSM_ERR_INVALID_ARG, "bad size or stride");
+  if (!X || !W || !Y) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  if (bias) return fail(SSM_ERR_UNSUPPORTED, "linear_fwd bias is applied by the caller's epilogue");
+  // Y[M, N] = X[M, K] W[N, K]^T: both operands k-contiguous
+  const int rc = gemm_check(X, ldx, W, K, Y, (int)M, N, K, ws_bytes, workspace);
+  if (rc != SSM_OK) return rc;
+  gemm_bf16(X, true, ldx, W, true, K, Y, ldy, SSM_BF16, (int)M, N, K, 0, workspace, static_cast<hipStream_t>(stream));
+  return check_launch("linear_fwd");
+}
+
+extern "C" size_t linear_fwd_workspace_size(int64_t M, int K, int N) {
+  if (M <= 0 || K <= 0 || N <= 0 || M >= (1LL << 31)) return 0;
+  return gemm_workspace_bytes((int)M, N, K);
+}

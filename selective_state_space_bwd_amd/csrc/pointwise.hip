@@ -4,6 +4,9 @@
 //                 causal depthwise conv backward;
 //   rmsnorm_bwd — rlx-cpu training_bwd.rs rms_norm_backward_row (no shift term)
 //                 with Phase B8's residual add.
+// and the forward pieces a layer backward recomputes instead of storing
+// (RMSNorm output, conv + SiLU output, the gated scan output) plus the dt_proj
+// bias + softplus that turns the dt_proj product into delta.
 // Reductions over rows / steps go to fixed-order partials, no atomics.
 #include "common.hpp"
 
@@ -199,6 +202,132 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_finalize(const float* __
   float acc = 0.f;
   for (int p = 0; p < parts; ++p) acc += part[(size_t)p * dim + col];
   dw[col] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// forward pieces (bf16 storage, float arithmetic)
+
+// xn = x * w / sqrt(mean(x^2) + eps), rows of `dim` <= 4096
+__global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_kernel(const bf16* __restrict__ x, const float* __restrict__ w,
+                                                               bf16* __restrict__ xn, int64_t rows, int dim,
+                                                               float eps) {
+  __shared__ float2 red[kPwBlock / kWave];
+  const int tid = threadIdx.x;
+  const int ncol = (dim + kPwBlock - 1) / kPwBlock;
+  const int64_t r0 = (int64_t)blockIdx.x * kRmsRows;
+  const int64_t r1 = min(rows, r0 + kRmsRows);
+  const float inv_dim = 1.f / (float)dim;
+  for (int64_t r = r0; r < r1; ++r) {
+    float xv[kRmsMaxCols];
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kRmsMaxCols; ++j) {
+      const int col = tid + j * kPwBlock;
+      xv[j] = (j < ncol && col < dim) ? ld(x, (size_t)r * dim + col) : 0.f;
+      acc.x = fmaf(xv[j], xv[j], acc.x);
+    }
+    const float inv_r = 1.f / sqrtf(block_sum2(acc, red).x * inv_dim + eps);
+#pragma unroll
+    for (int j = 0; j < kRmsMaxCols; ++j) {
+      const int col = tid + j * kPwBlock;
+      if (j < ncol && col < dim) st(xn, (size_t)r * dim + col, xv[j] * inv_r * w[col]);
+    }
+  }
+}
+
+// u[b,t,d] = SiLU(bias[d] + sum_k w[d,k] x[b, t-(K-1)+k, d]); thread per (b, chunk, d)
+template <int K>
+__global__ __launch_bounds__(kPwBlock) void conv_silu_fwd_kernel(const bf16* __restrict__ x, int ld_x,
+                                                                 const float* __restrict__ w,
+                                                                 const float* __restrict__ bias, bf16* __restrict__ u,
+                                                                 int ld_u, int Tn, int Di) {
+  const int d = blockIdx.x * kPwBlock + threadIdx.x;
+  const int c = blockIdx.y, b = blockIdx.z;
+  if (d >= Di) return;
+  float wk[K], xs[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) wk[k] = w[(size_t)d * K + k];
+  const float bd = bias ? bias[d] : 0.f;
+  const int t0 = c * kConvT, t1 = min(Tn, t0 + kConvT);
+  const size_t rx = (size_t)b * Tn;
+#pragma unroll
+  for (int k = 1; k < K; ++k) {  // xs[k] holds x[t0 - K + k] before the first shift
+    const int tt = t0 - K + k;
+    xs[k] = tt >= 0 ? ld(x, (rx + tt) * ld_x + d) : 0.f;
+  }
+  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+    for (int k = 0; k + 1 < K; ++k) xs[k] = xs[k + 1];
+    xs[K - 1] = ld(x, (rx + t) * ld_x + d);
+    float c_ = bd;
+#pragma unroll
+    for (int k = 0; k < K; ++k) c_ = fmaf(wk[k], xs[k], c_);
+    st(u, (rx + t) * ld_u + d, c_ * sigmoid(c_));
+  }
+}
+
+// gated = y * SiLU(z), z rows of stride ld_z
+__global__ __launch_bounds__(kPwBlock) void gate_fwd_kernel(const bf16* __restrict__ y, const bf16* __restrict__ z,
+                                                            int ld_z, bf16* __restrict__ g, int64_t rows, int Di) {
+  const int64_t n = rows * Di;
+  const int64_t stride = (int64_t)gridDim.x * kPwBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / Di;
+    const int d = (int)(i - r * Di);
+    const float zz = ld(z, (size_t)r * ld_z + d);
+    st(g, i, ld(y, i) * zz * sigmoid(zz));
+  }
+}
+
+// delta = softplus(v + b) with v > 20 passed through, in place on [rows, Di]
+__global__ __launch_bounds__(kPwBlock) void bias_softplus_kernel(bf16* __restrict__ v, const float* __restrict__ b,
+                                                                 int64_t rows, int Di) {
+  const int64_t n = rows * Di;
+  const int64_t stride = (int64_t)gridDim.x * kPwBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x; i < n; i += stride) {
+    const int d = (int)(i % Di);
+    const float r = ld(v, i) + (b ? b[d] : 0.f);
+    st(v, i, r > 20.f ? r : log1pf(expf(r)));
+  }
+}
+
+namespace {
+int grid_for(int64_t n) {
+  const int64_t want = (n + kPwBlock - 1) / kPwBlock;
+  return (int)(want < 8192 ? want : 8192);
+}
+}  // namespace
+
+void launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)((n + kPwBlock - 1) / kPwBlock)), dim3(kPwBlock), 0, st, p, n);
+}
+
+void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, int dim, float eps, hipStream_t st) {
+  if (rows == 0) return;
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((rows + kRmsRows - 1) / kRmsRows)), dim3(kPwBlock), 0, st,
+                     x, w, xn, rows, dim, eps);
+}
+
+void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* bias, bf16* u, int ld_u, int Bt,
+                          int Tn, int Di, int K, hipStream_t st) {
+  if ((int64_t)Bt * Tn == 0) return;
+  const dim3 grid((Di + kPwBlock - 1) / kPwBlock, (Tn + kConvT - 1) / kConvT, Bt);
+#define CONV_FWD(KV)                                                                                            \
+  case KV:                                                                                                      \
+    hipLaunchKernelGGL(conv_silu_fwd_kernel<KV>, grid, dim3(kPwBlock), 0, st, x, ld_x, w, bias, u, ld_u, Tn, Di); \
+    break;
+  switch (K) { CONV_FWD(1) CONV_FWD(2) CONV_FWD(3) CONV_FWD(4) CONV_FWD(5) CONV_FWD(6) CONV_FWD(7) CONV_FWD(8) }
+#undef CONV_FWD
+}
+
+void launch_gate_fwd(const bf16* y, const bf16* z, int ld_z, bf16* g, int64_t rows, int Di, hipStream_t st) {
+  if (rows * Di == 0) return;
+  hipLaunchKernelGGL(gate_fwd_kernel, dim3(grid_for(rows * Di)), dim3(kPwBlock), 0, st, y, z, ld_z, g, rows, Di);
+}
+
+void launch_bias_softplus(bf16* v, const float* b, int64_t rows, int Di, hipStream_t st) {
+  if (rows * Di == 0) return;
+  hipLaunchKernelGGL(bias_softplus_kernel, dim3(grid_for(rows * Di)), dim3(kPwBlock), 0, st, v, b, rows, Di);
 }
 
 }  // namespace ssm

@@ -38,7 +38,7 @@ constexpr int kChunk = 8;    // steps rebuilt and held in registers at a time
 constexpr int kBlock = 256;  // threads (and channels) per block (4 waves)
 
 struct ScanShape {
-  int Bt, T, Di, ld_bc, ld_dbc;
+  int Bt, T, Di, ld_bc, ld_dbc, ld_z;
   int seg, nseg, nchunk, ntile;
 };
 
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
   const size_t bo = (size_t)b * sh.T * Di;
   const T* __restrict__ ub = u + bo;
   const T* __restrict__ db = delta + bo;
-  const T* __restrict__ zb = BWD ? z + bo : nullptr;
+  const T* __restrict__ zb = BWD ? z + (size_t)b * sh.T * sh.ld_z : nullptr;
   const T* __restrict__ gb = BWD ? dout + bo : nullptr;
   const T* __restrict__ Bb = Bm + (size_t)b * sh.T * sh.ld_bc;
   const T* __restrict__ Cb = Cm + (size_t)b * sh.T * sh.ld_bc;
@@ -104,11 +104,12 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
     float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      const unsigned off = (unsigned)(tc + min(j, nv - 1)) * Di + dc;
+      const unsigned tj = (unsigned)(tc + min(j, nv - 1));
+      const unsigned off = tj * Di + dc;
       dl[j] = ld(db, off);
       uu[j] = ld(ub, off);
       if (need_g) {
-        zr[j] = ld(zb, off);
+        zr[j] = ld(zb, tj * sh.ld_z + dc);
         gr[j] = ld(gb, off);
       }
     }
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
         const size_t i = (row0 + tc + j) * Di + dc;
         dl[j] = ld(delta, i);
         uu[j] = ld(u, i);
-        zr[j] = ld(z, i);
+        zr[j] = ld(z, (row0 + tc + j) * sh.ld_z + dc);
         gr[j] = ld(dout, i);
       }
     }
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
 #pragma unroll
           for (int n = 0; n < NS; ++n) ah[j >= kLds ? j - kLds : 0][n] = aj[n];
         }
-        if (active) st(d_z, (row0 + tc + j) * Di + d, y * dzf);
+        if (active) st(d_z, (row0 + tc + j) * sh.ld_z + d, y * dzf);
         wave_reduce_scatter<NS>(dC, lane);
         if ((lane & (kRep - 1)) == 0) red[buf][wave][j][NS + (lane >> (6 - kLogNS))] = dC[0];
       }
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_main(
     }
     if (y) st(y, i, yy);
     if (out) {
-      const float zz = ld(z, i);
+      const float zz = ld(z, (row0 + t) * sh.ld_z + d);
       st(out, i, yy * zz * sigmoid(zz));
     }
   }
@@ -492,6 +493,11 @@ int check_dims(const ssm_dims* dm, int dtype) {
   if (dm->ld_bc < dm->d_state || dm->ld_dbc < dm->d_state)
     return fail(SSM_ERR_INVALID_ARG, "row strides ld_bc %d / ld_dbc %d below d_state %d", dm->ld_bc, dm->ld_dbc,
                 dm->d_state);
+  if (dm->ld_z != 0 && dm->ld_z < dm->d_inner)
+    return fail(SSM_ERR_INVALID_ARG, "row stride ld_z %d below d_inner %d", dm->ld_z, dm->d_inner);
+  // per-sequence offsets are 32-bit in the summary pass
+  if ((double)dm->seqlen * (dm->ld_z > dm->d_inner ? dm->ld_z : dm->d_inner) >= 4294967296.0)
+    return fail(SSM_ERR_UNSUPPORTED, "seqlen x row stride above 2^32 elements");
   if (dm->seg_len < 0 || dm->seg_len % kChunk != 0)
     return fail(SSM_ERR_INVALID_ARG, "seg_len %d is not 0 or a multiple of %d", dm->seg_len, kChunk);
   if (dtype == SSM_BF16 && ((dm->ld_bc & 1) || (dm->ld_dbc & 1)))
@@ -510,6 +516,7 @@ Plan make_plan(const ssm_dims& dm, bool bwd) {
   sh.Di = dm.d_inner;
   sh.ld_bc = dm.ld_bc;
   sh.ld_dbc = dm.ld_dbc;
+  sh.ld_z = dm.ld_z ? dm.ld_z : dm.d_inner;
   sh.seg = dm.seg_len ? dm.seg_len : auto_seg(dm);
   if (sh.seg <= 0) sh.seg = kChunk;
   sh.nseg = (sh.T + sh.seg - 1) / sh.seg;

@@ -146,21 +146,22 @@ def scan_inputs(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: str 
 
 def layer_inputs(batch: int, seqlen: int, d_model: int, d_inner: int, d_state: int,
                  dt_rank: int, d_conv: int, dtype: str = "bf16", seed: int = 4,
-                 variant: str = "default") -> dict:
+                 variant: str = "default", weight_std: float = 0.02) -> dict:
     """Inputs and parameters of one full-layer backward call.
 
     Activations x, d_out [B, T, d_model] are rounded to ``dtype``; matrices are
     stored [out_features, in_features] and rounded to ``dtype``; the conv
     weight is [d_inner, d_conv]; biases, the norm weight, A_log and D are float32.
+    Weight matrices and the conv weight are N(0, weight_std).
     """
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((batch, seqlen, d_model))
     d_out = rng.standard_normal((batch, seqlen, d_model))
-    w_in = 0.02 * rng.standard_normal((2 * d_inner, d_model))
-    conv_w = 0.02 * rng.standard_normal((d_inner, d_conv))
-    w_x = 0.02 * rng.standard_normal((dt_rank + 2 * d_state, d_inner))
-    w_dt = 0.02 * rng.standard_normal((d_inner, dt_rank))
-    w_out = 0.02 * rng.standard_normal((d_model, d_inner))
+    w_in = weight_std * rng.standard_normal((2 * d_inner, d_model))
+    conv_w = weight_std * rng.standard_normal((d_inner, d_conv))
+    w_x = weight_std * rng.standard_normal((dt_rank + 2 * d_state, d_inner))
+    w_dt = weight_std * rng.standard_normal((d_inner, dt_rank))
+    w_out = weight_std * rng.standard_normal((d_model, d_inner))
     conv_b = np.zeros(d_inner)
     b_dt = np.zeros(d_inner)
     norm_w = np.ones(d_model)

@@ -24,7 +24,7 @@ def test_status_strings():
 
 
 def _dims(**kw):
-    d = dict(batch=2, seqlen=64, d_inner=32, d_state=16, ld_bc=16, ld_dbc=16, seg_len=0)
+    d = dict(batch=2, seqlen=64, d_inner=32, d_state=16, ld_bc=16, ld_dbc=16, seg_len=0, ld_z=0)
     d.update(kw)
     return ssm.ssm_dims(**d)
 
@@ -51,6 +51,8 @@ def test_workspace_size():
     (dict(d_inner=0), ssm.SSM_ERR_INVALID_ARG),
     (dict(seg_len=12), ssm.SSM_ERR_INVALID_ARG),
     (dict(ld_bc=8), ssm.SSM_ERR_INVALID_ARG),
+    (dict(ld_z=16), ssm.SSM_ERR_INVALID_ARG),
+    (dict(seqlen=1 << 20, ld_z=1 << 12), ssm.SSM_ERR_UNSUPPORTED),
 ])
 def test_bwd_rejects_bad_dims(kw, code):
     assert _bwd(_dims(**kw)) == code
@@ -83,6 +85,61 @@ def test_other_entry_points_validate():
                           ctypes.byref(dims), 0, None) == ssm.SSM_ERR_INVALID_ARG   # out needs z
     assert L.ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 12, FAKE, 1 << 40,
                           ctypes.byref(dims), 0, None) == ssm.SSM_ERR_INVALID_ARG   # ckpt_every % 8
+
+
+def test_linear_entry_points_validate():
+    ok_ws = 1 << 40
+    # bf16 only
+    assert L.linear_bwd(FAKE, 64, FAKE, FAKE, 64, FAKE, 64, 0, FAKE, FAKE, 16, 64, 64, FAKE, ok_ws, 0,
+                        None) == ssm.SSM_ERR_UNSUPPORTED
+    # negative rows, strides below the row length, null W
+    assert L.linear_bwd(FAKE, 64, FAKE, FAKE, 64, FAKE, 64, 0, FAKE, FAKE, -1, 64, 64, FAKE, ok_ws, 1,
+                        None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.linear_bwd(FAKE, 32, FAKE, FAKE, 64, FAKE, 64, 0, FAKE, FAKE, 16, 64, 64, FAKE, ok_ws, 1,
+                        None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.linear_bwd(FAKE, 64, None, FAKE, 64, FAKE, 64, 0, FAKE, FAKE, 16, 64, 64, FAKE, ok_ws, 1,
+                        None) == ssm.SSM_ERR_INVALID_ARG
+    # row strides that break 16-byte rows
+    assert L.linear_bwd(FAKE, 68, FAKE, FAKE, 64, FAKE, 64, 0, FAKE, None, 16, 64, 64, FAKE, ok_ws, 1,
+                        None) == ssm.SSM_ERR_UNSUPPORTED
+    # split-k needs its workspace
+    assert L.linear_bwd_workspace_size(16384, 96, 3072) > 0
+    assert L.linear_bwd(FAKE, 96, FAKE, FAKE, 3072, None, 0, 0, FAKE, None, 16384, 96, 3072, None, 0, 1,
+                        None) == ssm.SSM_ERR_WORKSPACE
+    assert L.linear_fwd(FAKE, 64, FAKE, FAKE, FAKE, 64, 16, 64, 64, None, 0, 1, None) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def _layer_dims(**kw):
+    d = dict(batch=8, seqlen=2048, d_model=1536, d_inner=3072, d_state=16, dt_rank=96, d_conv=4, seg_len=0, eps=1e-5)
+    d.update(kw)
+    return ssm.ssm_layer_dims(**d)
+
+
+def test_layer_entry_points_validate():
+    big = L.mamba_layer_bwd_workspace_size(ctypes.byref(_layer_dims()))
+    assert big > L.mamba_layer_bwd_workspace_size(ctypes.byref(_layer_dims(seqlen=64))) > 0
+    assert L.mamba_layer_fwd_workspace_size(ctypes.byref(_layer_dims())) > 0
+    for bad in (dict(d_state=32), dict(dt_rank=90), dict(d_conv=9), dict(d_model=8192)):
+        assert L.mamba_layer_bwd_workspace_size(ctypes.byref(_layer_dims(**bad))) == 0
+    w = ssm.ssm_layer_weights(*([FAKE.value] * 10))
+    sv = ssm.ssm_layer_saved(*([FAKE.value] * 4))
+    g = ssm.ssm_layer_grads(*([FAKE.value] * 10))
+
+    def bwd(dims, w=w, sv=sv, g=g, ws_bytes=big, x=FAKE):
+        return L.mamba_layer_bwd(x, ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE, ctypes.byref(g), FAKE, ws_bytes,
+                                 ctypes.byref(dims) if dims is not None else None, None)
+    assert bwd(None) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(_layer_dims(d_state=5)) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(_layer_dims(batch=0)) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(_layer_dims(eps=-1.0)) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(_layer_dims(), ws_bytes=1024) == ssm.SSM_ERR_WORKSPACE
+    assert bwd(_layer_dims(), x=ctypes.c_void_p(0x1002)) == ssm.SSM_ERR_INVALID_ARG   # misaligned x
+    assert bwd(_layer_dims(), w=ssm.ssm_layer_weights(*([FAKE.value] * 9 + [None]))) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(_layer_dims(), g=ssm.ssm_layer_grads(*([None] + [FAKE.value] * 9))) == ssm.SSM_ERR_INVALID_ARG
+    misaligned = ssm.ssm_layer_saved(FAKE.value, 0x1008, FAKE.value, FAKE.value)
+    assert bwd(_layer_dims(), sv=misaligned) == ssm.SSM_ERR_UNSUPPORTED
+    assert L.mamba_layer_fwd(FAKE, ctypes.byref(w), FAKE, ctypes.byref(sv), FAKE, 16, ctypes.byref(_layer_dims()),
+                             None) == ssm.SSM_ERR_WORKSPACE
 
 
 def test_binding_has_no_cpu_path():

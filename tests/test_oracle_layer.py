@@ -186,6 +186,22 @@ def test_softplus_bwd_identities():
     np.testing.assert_allclose(got[below], d[below] * (1.0 - np.exp(-delta[below])), rtol=1e-12)
     np.testing.assert_array_equal(got[~below], d[~below])
     np.testing.assert_array_equal(delta[~below], raw[~below])
+    # the backward from saved activations gets raw back from delta: an exact inverse, except
+    # on (20, softplus(20)] = (20, 20 + 2.1e-9] where delta > 20 is read as a pass-through
+    np.testing.assert_allclose(layer.softplus_inv(delta), raw, rtol=1e-12, atol=2.1e-9)
+    np.testing.assert_allclose(layer.softplus_bwd(layer.softplus_inv(delta), d), got, rtol=2.1e-9)
+
+
+def test_layer_bwd_saved_needs_only_the_saved_activations():
+    """The backward from saved activations reads x, xz, xdbl, delta and y and nothing
+    else the forward made: poisoning every other activation changes nothing."""
+    p = layer_inputs(1, 12, 8, 16, 4, 2, 4, "f32", seed=3, variant="perturbed")
+    act = layer.layer_forward(p, 4, 2)
+    ref = layer.layer_bwd_saved(p, act, p["d_out"], 4, 2)
+    poisoned = {k: (v if k in ("x", "xz", "xdbl", "delta", "y") else np.full_like(v, np.nan)) for k, v in act.items()}
+    got = layer.layer_bwd_saved(p, poisoned, p["d_out"], 4, 2)
+    for k in ref:
+        np.testing.assert_array_equal(got[k], ref[k])
 
 
 @pytest.mark.parametrize("T", [1, 2, 3])

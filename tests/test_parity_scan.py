@@ -171,6 +171,28 @@ def test_strided_B_C_inside_xdbl_rows():
     _check(gg, r, TOL["bf16"], label="strided")
 
 
+def test_gate_inside_in_proj_rows():
+    """z read from, and d_z written into, the second half of a wider [x | z] row;
+    the forward's gated output reads the same strided z."""
+    nb, T, di, N = 2, 90, 40, 16
+    p = scan_inputs(nb, T, di, N, "bf16", seed=33)
+    t = _to_dev(p, "bf16")
+    xz = torch.zeros(nb, T, 2 * di + 8, dtype=torch.bfloat16, device=DEV)
+    xz[:, :, di:2 * di] = t["z"]
+    dxz = torch.full((nb, T, 2 * di + 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    print("case: strided z / d_z bf16 B2 T90 Di40 N16", flush=True)
+    g = _ssm().ssm_scan_bwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], xz[:, :, di:2 * di],
+                            t["d_out"], out={"d_z": dxz[:, :, di:2 * di]}, seg_len=24)
+    f = _ssm().ssm_scan_fwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], xz[:, :, di:2 * di])
+    torch.cuda.synchronize()
+    assert torch.all(dxz[:, :, :di] == 7.0) and torch.all(dxz[:, :, 2 * di:] == 7.0)
+    r = oracle_bwd(p)
+    gg = {k: _np(v) for k, v in g.items()}
+    _check(gg, r, TOL["bf16"], label="strided z")
+    _, out = orc.ssm_forward(p["u"], p["delta"], p["A_log"], p["B"], p["C"], p["D"], p["z"])
+    assert norm_err(_np(f["out"]), out) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("nb,T", [(0, 16), (2, 0)])
 def test_empty_inputs(nb, T):
     p = scan_inputs(max(nb, 1), max(T, 1), 12, 8, "f32", seed=1)
