@@ -1,18 +1,26 @@
 """Benchmark of the selective-scan backward on one MI355X.
 
-One step = one ``ssm_scan_bwd`` call (segment summaries, carries, the main
-backward sweep, final reductions) over the mamba-370m-shaped workload
-(batch 8, T 2048, d_inner 2048, d_state 16, float32), inputs resident in HBM.
-Prints one JSON line.  Only one GPU is supported.
+One step of the default workload = one ``ssm_scan_bwd`` call (segment
+summaries, carries, the main backward sweep, final reductions) over the
+mamba-370m-shaped problem (batch 8, T 2048, d_inner 2048, d_state 16, float32),
+inputs resident in HBM.  ``--workload layer`` times one ``mamba_layer_bwd``
+call (the whole layer backward, bf16, batch 8, T 2048, d_model 1536, d_inner
+3072) instead.  Prints one JSON line.  Only one GPU is supported.
 
-    python bench.py [--steps K] [--warmup W] [--workload mamba370m] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload mamba370m|mamba130m|mamba2p8b|layer]
+                    [--no-cpu-baseline] [--copy-probe]
+
+``--copy-probe`` only copies a 1 GiB device buffer ``steps`` times: the plain
+copy of known size that calibrates the HBM byte counters of rocprofv3.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSM-bwd state-elements/s (B·T·d_inner·d_state) + HBM GB/s as % of MI355X peak"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 # fp32 vector peak without packed instructions: 256 CUs x 64 lanes x 2 flop (FMA) x 2.4 GHz
 VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 # algorithmic flops per state element of the backward's definition (mul, add, exp = 1 each):
@@ -30,6 +39,7 @@ VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 # adjoint  g = dy C + a g 3, w = g (a h_prev) 1, d_delta += A w 2, d_A_log += delta w 2,
 #          d_u's sum g B 2, d_B = sum_d g delta u 2, d_C = sum_d dy h 2        -> 14
 FLOPS_PER_SE = 21
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def parse():
@@ -40,11 +50,12 @@ def parse():
     ap.add_argument("--workload", default="mamba370m")
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
     return ap.parse_args()
 
 
 class HipEvents:
-    """Raw HIP events from the process's (torch's) HIP runtime."""
+    """Raw HIP events from the process's (torch's) HIP runtime, recorded by the library on its stream."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
@@ -74,7 +85,35 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline(cfg, batches: int):
+# the sources each profiled kernel is compiled from
+KERNEL_SOURCES = {"scan_bwd_main": ("scan.hip", "common.hpp")}
+
+
+def source_digest(kernel: str) -> str:
+    """Digest of a kernel's sources: recorded counter totals are only valid for the code they came from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_bwd_amd", "csrc")
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
+    taken on the current sources: lines `traffic <workload> <kernel> <bytes> <digest>`."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = source_digest(kernel)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^traffic\s+(\S+)\s+(\S+)\s+(\d+)\s+([0-9a-f]+)\s*$", line.strip())
+            if m and m.group(1) == workload and m.group(2) == kernel and m.group(4) == digest:
+                return int(m.group(3))
+    return None
+
+
+def cpu_baseline_scan(cfg, batches: int):
     """The fp64 oracle, single-threaded, on the first `batches` sequences of the workload."""
     from threadpoolctl import threadpool_limits
 
@@ -91,18 +130,46 @@ def cpu_baseline(cfg, batches: int):
                       f"{dt:.1f} s, fp64 NumPy, 1 thread)"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
-              "of this path is a design note, not a measured configuration.", file=sys.stderr)
-        sys.exit(2)
+def cpu_baseline_layer(cfg, steps: int):
+    """The fp64 oracle's whole-layer forward + backward, single-threaded, on one sequence of `steps` steps."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import layer as orc
+    from synth import layer_inputs
+    p = layer_inputs(1, steps, cfg.d_model, cfg.d_inner, cfg.d_state, cfg.dt_rank, cfg.d_conv, cfg.dtype, cfg.seed)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        orc.layer_bwd(p, p["d_out"], cfg.d_state, cfg.dt_rank)
+        dt = time.perf_counter() - t0
+    se = steps * cfg.d_inner * cfg.d_state
+    return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 sequence of {steps} steps at the workload's widths ({se} state elements, {dt:.1f} s, "
+                      "fp64 NumPy forward + backward, 1 thread)"}
+
+
+def timed(step, n_events: int, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    evs = [hip.create(n_events) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = np.array([[hip.elapsed_ms(e[i], e[i + 1]) for i in range(n_events - 1)] for e in evs])
+    hip.destroy([e for es in evs for e in es])
+    return elapsed / steps * 1e3, stages
+
+
+def run_scan(args, cfg):
     import torch
 
     import selective_state_space_bwd_amd as ssm
-    from synth import CONFIGS, scan_inputs
-
-    cfg = CONFIGS[args.workload]
+    from synth import scan_inputs
     dev = torch.device("cuda:0")
     tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     p = scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
@@ -117,25 +184,11 @@ def main():
     dims = ssm.scan_dims(t["u"], t["B"], seg_len=args.seg_len)
     ws = torch.empty(ssm.ssm_scan_bwd_workspace_size(dims, tdt), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
+    def step(ev):
         ssm.ssm_scan_bwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
                          out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    hip = HipEvents()
-    evs = [hip.create(5) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    stages = np.array([[hip.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for e in evs])
-    hip.destroy([e for es in evs for e in es])
-
-    ms_step = elapsed / args.steps * 1e3
+    ms_step, stages = timed(step, 5, args.steps, args.warmup)
     se = cfg.state_elements
     el = 4 if cfg.dtype == "f32" else 2
     rows = cfg.batch * cfg.seqlen
@@ -153,28 +206,15 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(main_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(hbm_frac, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = "scan_bwd_main"
-    roof["kernel_ms"] = round(main_ms, 4)
-    roof["hbm_frac"] = round(hbm_frac, 4)
-    roof["alu_frac"] = round(alu_frac, 4)
-
+    roof["traffic"] = recorded_traffic(args.workload, "scan_bwd_main")
+    roof.update({"kernel": "scan_bwd_main", "kernel_ms": round(main_ms, 4), "hbm_frac": round(hbm_frac, 4),
+                 "alu_frac": round(alu_frac, 4), "algorithmic_bytes": main_bytes})
     line = {
-        "metric": METRIC,
-        "value": se / (ms_step * 1e-3),
-        "unit": "state-elements/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic",
+        "metric": METRIC, "value": se / (ms_step * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_inner": cfg.d_inner,
-                   "d_state": cfg.d_state, "seg_len": args.seg_len or "auto",
-                   "storage": cfg.dtype},
+                   "d_state": cfg.d_state, "seg_len": args.seg_len or "auto", "storage": cfg.dtype},
         "hbm": {"algorithmic_bytes": alg_bytes, "effective_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "stages_ms": {"summary": round(float(stages[:, 0].mean()), 4), "carry": round(float(stages[:, 1].mean()), 4),
@@ -182,7 +222,94 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, batches=2 if cfg.seqlen * cfg.d_inner <= 2048 * 2048 else 1)
+        line["cpu_baseline"] = cpu_baseline_scan(cfg, batches=2 if cfg.seqlen * cfg.d_inner <= 2048 * 2048 else 1)
+    return line
+
+
+LAYER_STAGES = ("gate_fwd", "out_proj", "conv_silu_fwd", "scan_bwd", "dt_proj", "x_proj", "conv_bwd",
+                "rmsnorm_fwd", "in_proj", "rmsnorm_bwd")
+
+
+def run_layer(args, cfg):
+    import torch
+
+    import selective_state_space_bwd_amd as ssm
+    from synth import layer_inputs
+    dev = torch.device("cuda:0")
+    p = layer_inputs(cfg.batch, cfg.seqlen, cfg.d_model, cfg.d_inner, cfg.d_state, cfg.dt_rank, cfg.d_conv,
+                     cfg.dtype, cfg.seed)
+    bf = ("x", "d_out", "W_in", "W_x", "W_dt", "W_out")
+    t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in bf else torch.from_numpy(v)).to(dev) for k, v in p.items()}
+    del p
+    W = {k: t[k] for k in ssm.LAYER_WEIGHTS}
+    _, saved = ssm.mamba_layer_fwd(t["x"], W, seg_len=args.seg_len)
+    ws = torch.empty(ssm.mamba_layer_bwd_workspace_size(t["x"], W, seg_len=args.seg_len), dtype=torch.uint8,
+                     device=dev)
+    out = ssm.mamba_layer_bwd(t["x"], W, saved, t["d_out"], workspace=ws, seg_len=args.seg_len)
+
+    def step(ev):
+        ssm.mamba_layer_bwd(t["x"], W, saved, t["d_out"], workspace=ws, out=out, seg_len=args.seg_len,
+                            stage_events=ev)
+
+    ms_step, stages = timed(step, 11, args.steps, args.warmup)
+    st = {name: float(stages[:, i].mean()) for i, name in enumerate(LAYER_STAGES)}
+    M = cfg.batch * cfg.seqlen
+    dm, di, R2 = cfg.d_model, cfg.d_inner, cfg.dt_rank + 2 * cfg.d_state
+    gemm_flops = {"out_proj": 4 * M * dm * di, "dt_proj": 4 * M * di * cfg.dt_rank, "x_proj": 4 * M * di * R2,
+                  "in_proj": 4 * M * 2 * di * dm}
+    in_tf = gemm_flops["in_proj"] / (st["in_proj"] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(in_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(in_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "gemm_bf16_kernel, in_proj dX + dW (2 launches)", "kernel_ms": round(st["in_proj"], 4)}
+    gemm_ms = sum(st[k] for k in gemm_flops)
+    line = {
+        "metric": METRIC, "value": cfg.state_elements / (ms_step * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di,
+                   "d_state": cfg.d_state, "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv,
+                   "seg_len": args.seg_len or "auto", "storage": "bf16"},
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "gemm": {"TFLOP": round(sum(gemm_flops.values()) / 1e12, 4), "ms": round(gemm_ms, 4),
+                 "TFLOPs": round(sum(gemm_flops.values()) / (gemm_ms * 1e-3) / 1e12, 1),
+                 "per_stage_TFLOPs": {k: round(v / (st[k] * 1e-3) / 1e12, 1) for k, v in gemm_flops.items()}},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_layer(cfg, steps=512)
+    return line
+
+
+def copy_probe(args):
+    """A plain device-to-device copy of 1 GiB, `steps` times: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    return {"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "ms_per_copy": round(ms, 4),
+            "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
+              "of this path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        print(json.dumps(copy_probe(args)), flush=True)
+        return
+    from synth import CONFIGS, LayerConfig
+    cfg = CONFIGS[args.workload]
+    line = run_layer(args, cfg) if isinstance(cfg, LayerConfig) else run_scan(args, cfg)
     print(json.dumps(line), flush=True)
 
 
