@@ -201,20 +201,36 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
   *c = from_f32<OutT>((accumulate ? to_f32(*c) : 0.f) + acc);
 }
 
-// column sums of a [M, N] bf16/f32 matrix (bias gradient), fixed order: a block
-// owns 64 columns, 4 row groups, combined in LDS
+// column sums of a [M, N] matrix (bias gradient) in two fixed-order passes:
+// block (column tile of 64, row chunk) -> partial[chunk][col], then one sum
+// over the chunks per column
+constexpr int kColRows = 256;  // rows per chunk
+
 template <typename T>
-__global__ __launch_bounds__(256) void column_sum(const T* __restrict__ X, long long ldx, int M, int N,
-                                                  float* __restrict__ out) {
+__global__ __launch_bounds__(256) void column_sum_part(const T* __restrict__ X, long long ldx, int M, int N,
+                                                       float* __restrict__ part) {
   __shared__ float s[4][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + lane;
+  const int r0 = blockIdx.y * kColRows, r1 = min(M, r0 + kColRows);
   float acc = 0.f;
-  if (col < N)
-    for (int r = grp; r < M; r += 4) acc += ld(X, (size_t)r * ldx + col);
+  if (col < N) {
+#pragma unroll 8
+    for (int r = r0 + grp; r < r1; r += 4) acc += ld(X, (size_t)r * ldx + col);
+  }
   s[grp][lane] = acc;
   __syncthreads();
-  if (grp == 0 && col < N) out[col] = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
+  if (grp == 0 && col < N) part[(size_t)blockIdx.y * N + col] = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
+}
+
+__global__ __launch_bounds__(256) void column_sum_final(const float* __restrict__ part, int chunks, int N,
+                                                        float* __restrict__ out) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= N) return;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < chunks; ++c) acc += part[(size_t)c * N + col];
+  out[col] = acc;
 }
 
 namespace {
@@ -288,12 +304,21 @@ int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool 
   return fail(SSM_ERR_INVALID_ARG, "gemm: layout");
 }
 
-int column_sum_launch(const void* X, long long ldx, int M, int N, int dtype, float* out, hipStream_t st) {
-  const dim3 grid((N + 63) / 64);
+size_t column_sum_workspace_bytes(int M, int N) {
+  return align_up((size_t)((M + kColRows - 1) / kColRows) * N * sizeof(float));
+}
+
+// workspace: column_sum_workspace_bytes(M, N)
+int column_sum_launch(const void* X, long long ldx, int M, int N, int dtype, float* out, void* workspace,
+                      hipStream_t st) {
+  const int chunks = (M + kColRows - 1) / kColRows;
+  float* part = static_cast<float*>(workspace);
+  const dim3 grid((N + 63) / 64, chunks);
   if (dtype == SSM_F32)
-    hipLaunchKernelGGL(column_sum<float>, grid, dim3(256), 0, st, static_cast<const float*>(X), ldx, M, N, out);
+    hipLaunchKernelGGL(column_sum_part<float>, grid, dim3(256), 0, st, static_cast<const float*>(X), ldx, M, N, part);
   else
-    hipLaunchKernelGGL(column_sum<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(X), ldx, M, N, out);
+    hipLaunchKernelGGL(column_sum_part<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(X), ldx, M, N, part);
+  hipLaunchKernelGGL(column_sum_final, dim3((N + 255) / 256), dim3(256), 0, st, part, chunks, N, out);
   return SSM_OK;
 }
 
@@ -303,10 +328,11 @@ using namespace ssm;
 
 extern "C" size_t linear_bwd_workspace_size(int64_t M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0 || M >= (1LL << 31)) return 0;
-  // dX = dY W   (M x K, reduction N) and dW = dY^T X (N x K, reduction M)
-  return gemm_workspace_bytes((int)M, K, N) > gemm_workspace_bytes(N, K, (int)M)
-             ? gemm_workspace_bytes((int)M, K, N)
-             : gemm_workspace_bytes(N, K, (int)M);
+  // dX = dY W (M x K, reduction N), dW = dY^T X (N x K, reduction M) and the db
+  // column sums run one after another and share the space
+  const size_t a = gemm_workspace_bytes((int)M, K, N), b = gemm_workspace_bytes(N, K, (int)M);
+  const size_t c = column_sum_workspace_bytes((int)M, N);
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
 extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void* dY, int64_t lddy, void* dX,
@@ -329,9 +355,11 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   if (dX && (rc = gemm_check(dY, lddy, W, K, dX, m, K, N, ws_bytes, workspace)) != SSM_OK) return rc;
   // dW[N, K] = dY^T X: A(i = n, k = m) = dY[m * lddy + n], B(k = m, j) = X[m * ldx + j]
   if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
+  if (db && (!workspace || ws_bytes < column_sum_workspace_bytes(m, N)))
+    return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace too small for the bias sums");
   if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, accumulate_dx, workspace, st);
   if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, 0, workspace, st);
-  if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, st);
+  if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, workspace, st);
   return check_launch("linear_bwd");
 }
 

@@ -195,13 +195,183 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_kernel(
   }
 }
 
+// Wave-per-row RMSNorm for rows whose length is a multiple of the 16-byte
+// vector (8 bf16 / 4 float) and at most 64 * VEC * kRmsMaxVec: each lane holds
+// vectors lane + 64 j of the row, the two row sums reduce inside the wave, and
+// the weight-gradient sums stay in registers over the block's rows before the
+// four waves combine them in LDS.
+constexpr int kRmsMaxVec = 6;
+constexpr int kRmsWaveRows = 16;  // rows per wave (a block of 4 waves takes 64)
+
+template <typename T>
+struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+  float v[N];
+  __device__ __forceinline__ void load(const T* __restrict__ p) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    if constexpr (sizeof(T) == 4) {
+      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+    } else {
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* __restrict__ p) const {
+    uint4 w;
+    if constexpr (sizeof(T) == 4) {
+      w = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    } else {
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        u[i] = uint32_t(from_f32<bf16>(v[2 * i]).bits) | (uint32_t(from_f32<bf16>(v[2 * i + 1]).bits) << 16);
+      w = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename T, int J>
+__global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_wave(const T* __restrict__ x, const float* __restrict__ w,
+                                                             T* __restrict__ xn, int64_t rows, int dim, float eps) {
+  constexpr int V = Vec16<T>::N;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nvec = dim / V;
+  float wv[J][V];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = (lane + kWave * j) * V;
+#pragma unroll
+    for (int i = 0; i < V; ++i) wv[j][i] = (lane + kWave * j < nvec) ? w[c + i] : 0.f;
+  }
+  const float inv_dim = 1.f / (float)dim;
+  const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsWaveRows, r1 = min(rows, r0 + 4 * kRmsWaveRows);
+  for (int64_t r = r0 + wave; r < r1; r += 4) {
+    Vec16<T> xv[J];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (lane + kWave * j < nvec) {
+        xv[j].load(x + r * dim + (lane + kWave * j) * V);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv[j].v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) ss = fmaf(xv[j].v[i], xv[j].v[i], ss);
+    }
+    const float inv_r = 1.f / sqrtf(wave_sum(ss) * inv_dim + eps);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (lane + kWave * j < nvec) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv[j].v[i] = xv[j].v[i] * inv_r * wv[j][i];
+        xv[j].store(xn + r * dim + (lane + kWave * j) * V);
+      }
+    }
+  }
+}
+
+template <typename T, int J>
+__global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_wave(const T* __restrict__ x, const float* __restrict__ w,
+                                                             const T* __restrict__ dy, const T* __restrict__ dres,
+                                                             T* __restrict__ dx, float* __restrict__ part,
+                                                             int64_t rows, int dim, float eps) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ float red[4][J * V * kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nvec = dim / V;
+  float wv[J][V], dw[J][V];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = (lane + kWave * j) * V;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      wv[j][i] = (lane + kWave * j < nvec) ? w[c + i] : 0.f;
+      dw[j][i] = 0.f;
+    }
+  }
+  const float inv_dim = 1.f / (float)dim;
+  const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsWaveRows, r1 = min(rows, r0 + 4 * kRmsWaveRows);
+  for (int64_t r = r0 + wave; r < r1; r += 4) {
+    Vec16<T> xv[J], gv[J];
+    float ss = 0.f, sd = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (lane + kWave * j < nvec) {
+        xv[j].load(x + r * dim + (lane + kWave * j) * V);
+        gv[j].load(dy + r * dim + (lane + kWave * j) * V);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv[j].v[i] = gv[j].v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        ss = fmaf(xv[j].v[i], xv[j].v[i], ss);
+        sd = fmaf(gv[j].v[i] * wv[j][i], xv[j].v[i], sd);
+      }
+    }
+    const float inv_r = 1.f / sqrtf(wave_sum(ss) * inv_dim + eps);
+    const float c3 = inv_r * inv_r * inv_r * (wave_sum(sd) * inv_dim);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (lane + kWave * j < nvec) {
+        Vec16<T> res, o;
+        if (dres) res.load(dres + r * dim + (lane + kWave * j) * V);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          o.v[i] = inv_r * wv[j][i] * gv[j].v[i] - c3 * xv[j].v[i] + (dres ? res.v[i] : 0.f);
+          dw[j][i] = fmaf(gv[j].v[i] * xv[j].v[i], inv_r, dw[j][i]);
+        }
+        o.store(dx + r * dim + (lane + kWave * j) * V);
+      }
+    }
+  }
+  // combine the four waves' column sums in a fixed order
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int i = 0; i < V; ++i) red[wave][(j * V + i) * kWave + lane] = dw[j][i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (lane + kWave * j < nvec) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int k = (j * V + i) * kWave + lane;
+          part[(size_t)blockIdx.x * dim + (lane + kWave * j) * V + i] = red[0][k] + red[1][k] + red[2][k] + red[3][k];
+        }
+      }
+    }
+  }
+}
+
+// dw[col] = sum over parts, in a fixed order: a block owns 64 columns, its four
+// waves take every fourth part and combine in LDS
 __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_finalize(const float* __restrict__ part,
                                                                  float* __restrict__ dw, int parts, int dim) {
-  const int col = blockIdx.x * kPwBlock + threadIdx.x;
-  if (col >= dim) return;
+  __shared__ float s[4][kWave];
+  const int lane = threadIdx.x & (kWave - 1), grp = threadIdx.x / kWave;
+  const int col = blockIdx.x * kWave + lane;
   float acc = 0.f;
-  for (int p = 0; p < parts; ++p) acc += part[(size_t)p * dim + col];
-  dw[col] = acc;
+  if (col < dim) {
+#pragma unroll 8
+    for (int p = grp; p < parts; p += 4) acc += part[(size_t)p * dim + col];
+  }
+  s[grp][lane] = acc;
+  __syncthreads();
+  if (grp == 0 && col < dim) dw[col] = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
 }
 
 // ---------------------------------------------------------------------------
@@ -302,10 +472,29 @@ void launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   if (n > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)((n + kPwBlock - 1) / kPwBlock)), dim3(kPwBlock), 0, st, p, n);
 }
 
+// vectors of 16 bytes per lane the wave-per-row kernels need for a row, 0 if they do not apply
+template <typename T>
+int rms_wave_vecs(const void* a, const void* b, const void* c, const void* d, int dim) {
+  constexpr int V = 16 / sizeof(T);
+  const auto al = [](const void* p) { return p == nullptr || aligned16(p); };
+  if (dim % V != 0 || !al(a) || !al(b) || !al(c) || !al(d)) return 0;
+  const int j = (dim / V + kWave - 1) / kWave;
+  return j <= kRmsMaxVec ? j : 0;
+}
+
 void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, int dim, float eps, hipStream_t st) {
   if (rows == 0) return;
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((rows + kRmsRows - 1) / kRmsRows)), dim3(kPwBlock), 0, st,
-                     x, w, xn, rows, dim, eps);
+  const int j = rms_wave_vecs<bf16>(x, xn, nullptr, nullptr, dim);
+  const dim3 grid((unsigned)((rows + 4 * kRmsWaveRows - 1) / (4 * kRmsWaveRows)));
+  switch (j) {
+#define RMS_FWD(J) \
+  case J: hipLaunchKernelGGL((rmsnorm_fwd_wave<bf16, J>), grid, dim3(kPwBlock), 0, st, x, w, xn, rows, dim, eps); return;
+    RMS_FWD(1) RMS_FWD(2) RMS_FWD(3) RMS_FWD(4) RMS_FWD(5) RMS_FWD(6)
+#undef RMS_FWD
+    default:
+      hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((rows + kRmsRows - 1) / kRmsRows)), dim3(kPwBlock), 0,
+                         st, x, w, xn, rows, dim, eps);
+  }
 }
 
 void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* bias, bf16* u, int ld_u, int Bt,
@@ -427,15 +616,35 @@ extern "C" int rmsnorm_bwd(const void* x, const float* w, const void* dy, const 
   if (!workspace || ws_bytes < need)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int blocks = (int)((rows + kRmsRows - 1) / kRmsRows);
   float* part = static_cast<float*>(workspace);
-  if (dtype == SSM_F32)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(blocks), dim3(kPwBlock), 0, st, (const float*)x, w,
-                       (const float*)dy, (const float*)d_residual, (float*)dx, part, rows, dim, eps);
-  else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(blocks), dim3(kPwBlock), 0, st, (const bf16*)x, w,
-                       (const bf16*)dy, (const bf16*)d_residual, (bf16*)dx, part, rows, dim, eps);
-  hipLaunchKernelGGL(rmsnorm_bwd_finalize, dim3((dim + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0, st, part, dw,
+  int blocks = 0;
+  const int jw = dtype == SSM_F32 ? rms_wave_vecs<float>(x, dy, d_residual, dx, dim)
+                                  : rms_wave_vecs<bf16>(x, dy, d_residual, dx, dim);
+  if (jw > 0) {
+    blocks = (int)((rows + 4 * kRmsWaveRows - 1) / (4 * kRmsWaveRows));
+#define RMS_BWD(TY, J)                                                                                          \
+  case J:                                                                                                       \
+    hipLaunchKernelGGL((rmsnorm_bwd_wave<TY, J>), dim3(blocks), dim3(kPwBlock), 0, st, (const TY*)x, w,         \
+                       (const TY*)dy, (const TY*)d_residual, (TY*)dx, part, rows, dim, eps);                   \
+    break;
+    if (dtype == SSM_F32) {
+      switch (jw) { RMS_BWD(float, 1) RMS_BWD(float, 2) RMS_BWD(float, 3) RMS_BWD(float, 4) RMS_BWD(float, 5)
+                    RMS_BWD(float, 6) }
+    } else {
+      switch (jw) { RMS_BWD(bf16, 1) RMS_BWD(bf16, 2) RMS_BWD(bf16, 3) RMS_BWD(bf16, 4) RMS_BWD(bf16, 5)
+                    RMS_BWD(bf16, 6) }
+    }
+#undef RMS_BWD
+  } else {
+    blocks = (int)((rows + kRmsRows - 1) / kRmsRows);
+    if (dtype == SSM_F32)
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(blocks), dim3(kPwBlock), 0, st, (const float*)x, w,
+                         (const float*)dy, (const float*)d_residual, (float*)dx, part, rows, dim, eps);
+    else
+      hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, dim3(blocks), dim3(kPwBlock), 0, st, (const bf16*)x, w,
+                         (const bf16*)dy, (const bf16*)d_residual, (bf16*)dx, part, rows, dim, eps);
+  }
+  hipLaunchKernelGGL(rmsnorm_bwd_finalize, dim3((dim + kWave - 1) / kWave), dim3(kPwBlock), 0, st, part, dw,
                      blocks, dim);
   return check_launch("rmsnorm_bwd");
 }

@@ -71,8 +71,11 @@ def test_conv1d_bwd(case):
     assert norm_err(_np(db), rdb) < TOL[dt]
 
 
+# rows of 16-byte vectors up to 6 per lane take the wave-per-row kernels (f32 dim 12, 100, 1536;
+# bf16 dim 1000, 1536, 2048, 3072); the rest the block-per-rows kernels (f32 4096, bf16 36, 4096)
 RMS = [(5, 12, "f32", False), (300, 1536, "f32", True), (64, 1536, "bf16", True), (33, 4096, "f32", False),
-       (1, 100, "f32", True)]
+       (1, 100, "f32", True), (70, 1000, "bf16", False), (17, 36, "bf16", True), (130, 4096, "bf16", True),
+       (1000, 2048, "bf16", True), (200, 3072, "bf16", False)]
 
 
 @pytest.mark.parametrize("case", RMS, ids=[f"R{c[0]}D{c[1]}-{c[2]}-res{int(c[3])}" for c in RMS])
