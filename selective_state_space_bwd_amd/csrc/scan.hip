@@ -58,11 +58,35 @@ __device__ __forceinline__ void load_A2(const float* __restrict__ A_log, int d, 
   for (int n = 0; n < NS; ++n) A2[n] = -expf(A_log[(size_t)d * NS + n]) * kLog2e;
 }
 
+// The B | C rows of one 8-step chunk, staged in LDS for the whole block: thread
+// i < 8 * 2N holds element (step i / 2N, column i % 2N), B in columns [0, N)
+// and C in [N, 2N).  Steps past the chunk's valid length repeat its last row
+// (clamp) so every read stays inside the tensors.
+template <typename T, int NS>
+__device__ __forceinline__ float bc_element(const T* __restrict__ Bb, const T* __restrict__ Cb, int ld_bc, int tc,
+                                            int nv, int tid) {
+  const int j = tid / (2 * NS), k = tid - j * (2 * NS);
+  if (tid >= kChunk * 2 * NS) return 0.f;
+  const size_t row = (size_t)(tc + min(j, nv - 1)) * ld_bc;
+  return k < NS ? ld(Bb, row + k) : ld(Cb, row + (k - NS));
+}
+
+template <int NS>
+__device__ __forceinline__ void bc_row(const float (&bcs)[kChunk][2 * NS], int j, float (&Bv)[NS], float (&Cv)[NS]) {
+  const float4* p = reinterpret_cast<const float4*>(&bcs[j][0]);
+#pragma unroll
+  for (int q = 0; q < NS / 4; ++q) {
+    const float4 b = p[q], c = p[NS / 4 + q];
+    Bv[4 * q] = b.x; Bv[4 * q + 1] = b.y; Bv[4 * q + 2] = b.z; Bv[4 * q + 3] = b.w;
+    Cv[4 * q] = c.x; Cv[4 * q + 1] = c.y; Cv[4 * q + 2] = c.z; Cv[4 * q + 3] = c.w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 1. segment summaries.  BWD adds the chunk checkpoints and the adjoint summary.
 //
-// Loads of a chunk are all issued before its arithmetic; a full chunk takes a
-// branch-free path.  Lane offsets are 32-bit from per-batch base pointers.
+// Every chunk takes one branch-free path.  Lane offsets are 32-bit from
+// per-batch base pointers.
 template <typename T, int NS, bool BWD>
 __global__ __launch_bounds__(kBlock) void scan_summary(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
@@ -91,40 +115,71 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
 
   // the first segment's adjoint summary is never used
   const bool need_g = BWD && s > 0;
-  for (int tc = t0; tc < t1; tc += kChunk) {
+  // float prefetches the next chunk's channel values and stages B | C in LDS;
+  // bf16 (whose loads are half as wide) keeps three waves per SIMD instead:
+  // it loads each chunk's values at its start and B | C with scalar loads
+  constexpr bool kPipe = sizeof(T) == 4;
+  // per-step channel values of one chunk; a ragged last chunk reads its last
+  // step again and zeroes the extra steps' delta, u and dy below: a = 1 there,
+  // so the state, P and G pass through unchanged
+  struct Raw {
+    float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk];
+  };
+  const auto load_raw = [&](int tc, Raw& r) {
+    const int nv = min(kChunk, t1 - tc);
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const unsigned tj = (unsigned)(tc + min(j, nv - 1));
+      const unsigned off = tj * Di + dc;
+      r.dl[j] = ld(db, off);
+      r.uu[j] = ld(ub, off);
+      if (need_g) {
+        r.zr[j] = ld(zb, tj * sh.ld_z + dc);
+        r.gr[j] = ld(gb, off);
+      }
+    }
+  };
+  __shared__ __align__(16) float bcs[2][kChunk][2 * NS];
+  const int tid = threadIdx.x;
+  Raw cur;
+  if (kPipe) {
+    load_raw(t0, cur);
+    if (tid < kChunk * 2 * NS)
+      (&bcs[0][0][0])[tid] = bc_element<T, NS>(Bb, Cb, sh.ld_bc, t0, min(kChunk, t1 - t0), tid);
+    __syncthreads();
+  }
+  int buf = 0;
+  for (int tc = t0; tc < t1; tc += kChunk, buf ^= 1) {
+    const bool more = tc + kChunk < t1;
+    Raw nxt;
+    float bc_next = 0.f;
+    if (kPipe && more) {
+      load_raw(tc + kChunk, nxt);
+      bc_next = bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc + kChunk, min(kChunk, t1 - tc - kChunk), tid);
+    }
     if (BWD && tc > t0 && active) {
       const size_t c = (size_t)b * sh.nchunk + tc / kChunk;
 #pragma unroll
       for (int n = 0; n < NS; ++n) ckpt[(c * NS + n) * Di + d] = h[n];
       ckpt_sd[c * Di + d] = sd;
     }
-    // a ragged last chunk reads its last step again and zeroes the extra steps'
-    // delta, u and dy: a = 1 there, so the state, P and G pass through unchanged
+    if (!kPipe) load_raw(tc, cur);
     const int nv = min(kChunk, t1 - tc);
-    float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk];
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const unsigned tj = (unsigned)(tc + min(j, nv - 1));
-      const unsigned off = tj * Di + dc;
-      dl[j] = ld(db, off);
-      uu[j] = ld(ub, off);
-      if (need_g) {
-        zr[j] = ld(zb, tj * sh.ld_z + dc);
-        gr[j] = ld(gb, off);
-      }
-    }
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       const bool ok = j < nv;
-      const float dlj = ok ? dl[j] : 0.f;
-      const int t = tc + min(j, nv - 1);
-      float Bv[NS];
-      load_row<NS>(Bb + (size_t)t * sh.ld_bc, Bv);
-      const float du = ok ? dlj * uu[j] : 0.f;
+      const float dlj = ok ? cur.dl[j] : 0.f;
+      float Bv[NS], Cv[NS];
+      if (kPipe) {
+        bc_row<NS>(bcs[buf], j, Bv, Cv);
+      } else {
+        const size_t row = (size_t)(tc + min(j, nv - 1)) * sh.ld_bc;
+        load_row<NS>(Bb + row, Bv);
+        if (need_g) load_row<NS>(Cb + row, Cv);
+      }
+      const float du = ok ? dlj * cur.uu[j] : 0.f;
       if (need_g) {
-        float Cv[NS];
-        load_row<NS>(Cb + (size_t)t * sh.ld_bc, Cv);
-        const float dy = ok ? gr[j] * zr[j] * sigmoid(zr[j]) : 0.f;
+        const float dy = ok ? cur.gr[j] * cur.zr[j] * sigmoid(cur.zr[j]) : 0.f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           const float a = fast_exp2(dlj * A2[n]);
@@ -137,6 +192,12 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
         for (int n = 0; n < NS; ++n) h[n] = fmaf(fast_exp2(dlj * A2[n]), h[n], du * Bv[n]);
       }
       sd += dlj;
+    }
+    if (kPipe) {
+      // the buffer written here was last read before the previous chunk's barrier
+      if (more && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
+      __syncthreads();
+      if (more) cur = nxt;
     }
   }
 
@@ -197,8 +258,11 @@ struct ChunkTile {
   static constexpr int kLdsSteps = kChunk - kRegSteps;
 };
 
+// float asks for two waves per SIMD (B | C staged in LDS take VGPRs the
+// compiler would otherwise spend at the cost of occupancy); bf16 leaves the
+// choice to the compiler.
 template <typename T, int NS, bool SOFTPLUS>
-__global__ __launch_bounds__(kBlock) void scan_bwd_main(
+__global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
     const T* __restrict__ z, const T* __restrict__ dout, T* __restrict__ d_u,
@@ -212,6 +276,7 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
   static_assert(NS % 4 == 0, "a*h rows move through LDS as float4");
   __shared__ float red[2][kBlock / kWave][kChunk][2 * NS];
   __shared__ float4 lds_ah[kLds > 0 ? kLds : 1][NS / 4][kBlock];
+  __shared__ __align__(16) float bcs[2][kChunk][2 * NS];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int d = blockIdx.x * kBlock + tid;
@@ -235,10 +300,23 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
 
   const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
   const int c_first = t0 / kChunk, c_last = (t1 - 1) / kChunk;
+  const T* __restrict__ Bb = Bm + row0 * sh.ld_bc;
+  const T* __restrict__ Cb = Cm + row0 * sh.ld_bc;
+  // float: the last chunk's B | C rows go to LDS before the sweep, and each chunk
+  // fetches the next one's while it computes.  bf16 reads them per step with
+  // scalar loads (its VGPR budget has no room for the staged rows).
+  constexpr bool kStage = sizeof(T) == 4;
+  if (kStage) {
+    if (tid < kChunk * 2 * NS)
+      (&bcs[c_last & 1][0][0])[tid] =
+          bc_element<T, NS>(Bb, Cb, sh.ld_bc, c_last * kChunk, min(kChunk, t1 - c_last * kChunk), tid);
+    __syncthreads();
+  }
   for (int c = c_last; c >= c_first; --c) {
     const int tc = c * kChunk;
     const int nv = min(kChunk, t1 - tc);
     const int buf = c & 1;
+    const float bc_next = kStage && c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
     // state before the chunk: local checkpoint + decayed carry-in
     float h[NS];
     if (c == c_first) {
@@ -272,8 +350,12 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
     for (int j = 0; j < kChunk; ++j) {
       if (j < nv) {
         float Bv[NS], Cv[NS];
-        load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
-        load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        if (kStage) {
+          bc_row<NS>(bcs[buf], j, Bv, Cv);
+        } else {
+          load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
+          load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        }
         const float sz = sigmoid(zr[j]);
         dy[j] = active ? gr[j] * zr[j] * sz : 0.f;
         const float dzf = gr[j] * sz * (1.f + zr[j] * (1.f - sz));
@@ -307,8 +389,12 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
     for (int j = kChunk - 1; j >= 0; --j) {
       if (j < nv) {
         float Bv[NS], Cv[NS];
-        load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
-        load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        if (kStage) {
+          bc_row<NS>(bcs[buf], j, Bv, Cv);
+        } else {
+          load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
+          load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
+        }
         float aj[NS];
         if (j < kLds) {
 #pragma unroll
@@ -348,6 +434,8 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_main(
         if ((lane & (kRep - 1)) == 0) red[buf][wave][j][lane >> (6 - kLogNS)] = dB[0];
       }
     }
+    // the buffer written here was last read before the previous chunk's barrier
+    if (kStage && c > c_first && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
     __syncthreads();
     for (int q = tid; q < kChunk * 2 * NS; q += kBlock) {
       const int j = q / (2 * NS), k = q - j * (2 * NS);
@@ -473,14 +561,48 @@ struct Plan {
   size_t bytes;
 };
 
-int auto_seg(const ssm_dims& dm) {
-  const long ntile = (dm.d_inner + kBlock - 1) / kBlock;
-  const long per_seg = ntile * dm.batch;
-  int seg = ((dm.seqlen + kChunk - 1) / kChunk) * kChunk;
-  // enough blocks for every CU to hold two, without segments shorter than 64 steps
-  while (seg > 64 && per_seg * ((dm.seqlen + seg - 1) / seg) < 1024) seg = ((seg / 2 + kChunk - 1) / kChunk) * kChunk;
-  return seg;
+// Segment length: the segments of all batch elements and channel tiles run as
+// independent blocks of the summary and the main kernel, so a pass takes about
+// (rounds of resident blocks) x (segment length + a fixed set-up cost) in each,
+// the main kernel's steps weighing about three summary steps.  Picks the length,
+// a multiple of 8 and at least 64 steps (or the whole sequence), that minimises
+// the sum; ties go to the longer segment (fewer carries, less workspace).
+int auto_seg(const ssm_dims& dm, long cap_summary, long cap_main) {
+  constexpr int kSegOverhead = 16;  // steps' worth of checkpoint restore and carry work
+  constexpr long kMainWeight = 3;
+  const long rows = (long)((dm.d_inner + kBlock - 1) / kBlock) * dm.batch;
+  const int tmax = (dm.seqlen + kChunk - 1) / kChunk * kChunk;
+  const int smin = tmax < 64 ? tmax : 64;
+  long best_cost = -1;
+  int best = tmax;
+  for (int seg = tmax; seg >= smin && seg > 0; seg -= kChunk) {
+    const long blocks = rows * ((dm.seqlen + seg - 1) / seg);
+    const long rounds = (blocks + cap_summary - 1) / cap_summary + kMainWeight * ((blocks + cap_main - 1) / cap_main);
+    const long cost = rounds * (seg + kSegOverhead);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = seg;
+    }
+  }
+  return best;
 }
+
+// CUs of the current device (256 if it cannot be queried)
+long device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  return cus;
+}
+
+// 256-lane blocks one CU holds at once, from the kernels' register use: the main
+// sweep runs two waves per SIMD, the summary two in float and three in bf16
+// (its float variant holds the next chunk's values in registers)
+long summary_blocks_per_cu(int dtype) { return dtype == SSM_F32 ? 2 : 3; }
+constexpr long kMainBlocksPerCU = 2;
 
 int check_dims(const ssm_dims* dm, int dtype) {
   if (!dm) return fail(SSM_ERR_INVALID_ARG, "dims is null");
@@ -508,7 +630,7 @@ int check_dims(const ssm_dims* dm, int dtype) {
   return SSM_OK;
 }
 
-Plan make_plan(const ssm_dims& dm, bool bwd) {
+Plan make_plan(const ssm_dims& dm, int dtype, bool bwd) {
   Plan p{};
   ScanShape& sh = p.sh;
   sh.Bt = dm.batch;
@@ -517,7 +639,8 @@ Plan make_plan(const ssm_dims& dm, bool bwd) {
   sh.ld_bc = dm.ld_bc;
   sh.ld_dbc = dm.ld_dbc;
   sh.ld_z = dm.ld_z ? dm.ld_z : dm.d_inner;
-  sh.seg = dm.seg_len ? dm.seg_len : auto_seg(dm);
+  const long cus = dm.seg_len ? 0 : device_cus();
+  sh.seg = dm.seg_len ? dm.seg_len : auto_seg(dm, cus * summary_blocks_per_cu(dtype), cus * kMainBlocksPerCU);
   if (sh.seg <= 0) sh.seg = kChunk;
   sh.nseg = (sh.T + sh.seg - 1) / sh.seg;
   sh.nchunk = (sh.T + kChunk - 1) / kChunk;
@@ -637,13 +760,13 @@ using namespace ssm;
 extern "C" size_t ssm_scan_bwd_workspace_size(const ssm_dims* dims, int dtype) {
   if (check_dims(dims, dtype) != SSM_OK) return 0;
   if ((size_t)dims->batch * dims->seqlen * dims->d_inner == 0) return 0;
-  return make_plan(*dims, true).bytes;
+  return make_plan(*dims, dtype, true).bytes;
 }
 
 extern "C" size_t ssm_scan_fwd_workspace_size(const ssm_dims* dims, int dtype) {
   if (check_dims(dims, dtype) != SSM_OK) return 0;
   if ((size_t)dims->batch * dims->seqlen * dims->d_inner == 0) return 0;
-  return make_plan(*dims, false).bytes;
+  return make_plan(*dims, dtype, false).bytes;
 }
 
 extern "C" int ssm_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
@@ -671,7 +794,7 @@ extern "C" int ssm_scan_bwd_timed(const void* u, const void* delta, const float*
     return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
   if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C) && aligned4(d_B) && aligned4(d_C)))
     return fail(SSM_ERR_UNSUPPORTED, "bf16 B, C, d_B and d_C must be 4-byte aligned");
-  const Plan p = make_plan(dm, true);
+  const Plan p = make_plan(dm, dtype, true);
   if (!workspace || ws_bytes < p.bytes)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
   const ScanWs w = bind(p, workspace);
@@ -703,7 +826,7 @@ extern "C" int ssm_scan_fwd(const void* u, const void* delta, const float* A_log
     return fail(SSM_ERR_INVALID_ARG, "ckpt_every %d must be a positive multiple of %d", ckpt_every, kChunk);
   if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C)))
     return fail(SSM_ERR_UNSUPPORTED, "bf16 B and C must be 4-byte aligned");
-  const Plan p = make_plan(dm, false);
+  const Plan p = make_plan(dm, dtype, false);
   if (!workspace || ws_bytes < p.bytes)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
   const ScanWs w = bind(p, workspace);
