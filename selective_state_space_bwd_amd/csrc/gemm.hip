@@ -6,21 +6,25 @@
 //   opA(m, k) = A[m * lda + k]  (A_K: k contiguous)  or  A[k * lda + m]
 //   opB(k, n) = B[n * ldb + k]  (B_K: k contiguous)  or  B[k * ldb + n]
 //
-// Block tile 128 x 128 x 32, four waves in a 2 x 2 grid, each wave 64 x 64 as
-// 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  Tiles are staged in LDS with k
-// contiguous (operands whose k is strided are transposed on the way in), double
-// buffered: the next tile's global loads are in flight while the matrix cores
-// work on the current one, one barrier per k step.  Split-k writes fp32 partial
-// tiles that a second kernel sums in a fixed order.
+// Block tile BM x BN x 32 (256 x 128 for large products, 128 x 128 otherwise),
+// four waves in a 2 x 2 grid, each wave (BM/2) x (BN/2) as
+// v_mfma_f32_32x32x16_bf16 tiles.  Every operand tile sits in LDS in the layout
+// it has in memory, so global loads and LDS stores are 16 bytes either way:
+// [row][k] when k is contiguous, read as MFMA operands with ds_read_b128, or
+// [k][row] when k is the row index, read with the gfx950 transposing
+// ds_read_b64_tr_b16 (two per operand).  Double buffered: the next tile's
+// global loads are in flight while the matrix cores work on the current one,
+// one barrier per k step.  Split-k writes fp32 partial tiles that a second
+// kernel sums in a fixed order.
 #include "common.hpp"
 
 namespace ssm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row (16 B of padding)
+constexpr int kBK = 32;
 constexpr int kGemmThreads = 256;
 
 struct GemmArgs {
@@ -34,7 +38,7 @@ struct GemmArgs {
   int accumulate;   // add into C instead of overwriting (single split only)
 };
 
-// one 16-byte chunk (8 bf16) of a tile from global memory, zero outside [0, rows) x [0, cols)
+// one 16-byte chunk (8 bf16) of a matrix row, zero outside [0, rows) x [0, cols)
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ p, long long ld, int r, int c, int rows,
                                             int cols) {
   uint4 v = make_uint4(0, 0, 0, 0);
@@ -53,82 +57,85 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ p, long
   return v;
 }
 
-// two adjacent bf16 (tile rows r, r+1 at one k) as one dword, zero outside the matrix
-__device__ __forceinline__ uint32_t load_pair(const uint16_t* __restrict__ p, long long ld, int k, int r, int kend,
-                                              int rows) {
-  if (k >= kend || r >= rows) return 0u;
-  const uint16_t* q = p + (long long)k * ld + r;
-  if (r + 1 < rows) return *reinterpret_cast<const uint32_t*>(q);
-  return q[0];
-}
+// One operand's R x 32 tile: its global -> register -> LDS moves and its MFMA
+// operand reads.  KC: k contiguous, LDS [row][k] with rows of 40 bf16; else
+// LDS [k][row] with rows of R + 16 bf16 (the padding spreads the four k rows a
+// transposing read touches over different banks).
+template <bool KC, int R>
+struct OperandTile {
+  static constexpr int kLd = KC ? kBK + 8 : R + 16;
+  static constexpr int kElems = KC ? R * kLd : kBK * kLd;
+  static constexpr int kPer = R * kBK / 8 / kGemmThreads;  // 16-byte chunks per thread
+  static_assert(kPer >= 1 && R % 32 == 0, "tile shape");
+  uint4 v[kPer];
 
-// Loads of one 128 x 32 operand tile into registers, then into LDS as [row][k].
-// KC: the operand's k is contiguous in memory; a thread moves two 16-byte
-// chunks of 8 k.  Otherwise a thread holds tile rows (2p, 2p+1) at 8
-// consecutive k (eight dword loads, each wave reading 256 contiguous bytes per
-// k) and repacks them into one 16-byte LDS row segment per tile row.
-template <bool KC>
-struct TileLoader {
-  uint32_t v[8];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long long ld, int row0, int k0, int rows,
                                        int kend, int tid) {
-    if (KC) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {  // 128 rows x 4 chunks of 8 k
-        const int c = tid + q * kGemmThreads;
-        const int r = c >> 2, kc = (c & 3) * 8;
-        const uint4 w = load_chunk(base, ld, row0 + r, k0 + kc, rows, kend);
-        v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    for (int q = 0; q < kPer; ++q) {
+      const int c = tid + q * kGemmThreads;
+      if (KC) {  // R rows x 4 chunks of 8 k
+        v[q] = load_chunk(base, ld, row0 + (c >> 2), k0 + (c & 3) * 8, rows, kend);
+      } else {   // 32 k rows x R / 8 chunks of 8 tile rows
+        v[q] = load_chunk(base, ld, k0 + c / (R / 8), row0 + (c % (R / 8)) * 8, kend, rows);
       }
-    } else {
-      const int r = row0 + 2 * (tid & 63), k = k0 + 8 * (tid >> 6);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = load_pair(base, ld, k + i, r, kend, rows);
     }
   }
   __device__ __forceinline__ void store(uint16_t* __restrict__ lds, int tid) const {
-    if (KC) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = tid + q * kGemmThreads;
-        const int r = c >> 2, kc = (c & 3) * 8;
-        *reinterpret_cast<uint4*>(lds + r * kLdsRow + kc) = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      }
+    for (int q = 0; q < kPer; ++q) {
+      const int c = tid + q * kGemmThreads;
+      const int off = KC ? (c >> 2) * kLd + (c & 3) * 8 : (c / (R / 8)) * kLd + (c % (R / 8)) * 8;
+      *reinterpret_cast<uint4*>(lds + off) = v[q];
+    }
+  }
+  // MFMA operand of rows rt * 32 .. + 31 and k ks * 16 .. + 15: lane l holds row
+  // l % 32 and k 8 (l / 32) .. + 7
+  static __device__ __forceinline__ bf16x8_t frag(const uint16_t* __restrict__ lds, int rt, int ks, int lane) {
+    if (KC) {
+      return *reinterpret_cast<const bf16x8_t*>(&lds[(rt * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8]);
     } else {
-      const int r = 2 * (tid & 63), kc = 8 * (tid >> 6);
-      uint4 lo, hi;  // row r takes the low halves, row r + 1 the high halves
-      lo.x = (v[0] & 0xffffu) | (v[1] << 16); hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
-      lo.y = (v[2] & 0xffffu) | (v[3] << 16); hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
-      lo.z = (v[4] & 0xffffu) | (v[5] << 16); hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
-      lo.w = (v[6] & 0xffffu) | (v[7] << 16); hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
-      *reinterpret_cast<uint4*>(lds + r * kLdsRow + kc) = lo;
-      *reinterpret_cast<uint4*>(lds + (r + 1) * kLdsRow + kc) = hi;
+      // within a 16-lane group, lane i of the transposing read returns element
+      // i % 4 of the 8-byte rows addressed by lanes 4r + i / 4, r = 0..3: lane j
+      // addresses k row (j / 4) and rows 4 (j % 4) .. + 3, so lane i gets tile row
+      // i at four consecutive k
+      const int grp = lane >> 4, j = lane & 15;
+      const int k = ks * 16 + 8 * (grp >> 1) + (j >> 2);
+      const int r = rt * 32 + 16 * (grp & 1) + 4 * (j & 3);
+      typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(lds + k * kLd + r));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(lds + (k + 4) * kLd + r));
+      const v4i16_t lohi[2] = {lo, hi};
+      return *reinterpret_cast<const bf16x8_t*>(lohi);
     }
   }
 };
 
-template <bool A_K, bool B_K, typename OutT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __align__(16) uint16_t lds_a[2][kBM * kLdsRow];
-  __shared__ __align__(16) uint16_t lds_b[2][kBN * kLdsRow];
+template <bool A_K, bool B_K, typename OutT, int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
+  using TA = OperandTile<A_K, BM>;
+  using TB = OperandTile<B_K, BN>;
+  constexpr int TM = BM / 64, TN = BN / 64;  // 32 x 32 tiles per wave
+  __shared__ __align__(16) uint16_t lds_a[2][TA::kElems];
+  __shared__ __align__(16) uint16_t lds_b[2][TB::kElems];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int kb = blockIdx.z * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
   const int nk = (ke - kb + kBK - 1) / kBK;
 
-  floatx16 acc[2][2];
+  floatx16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  TileLoader<A_K> la;
-  TileLoader<B_K> lb;
+  TA la;
+  TB lb;
   la.load(g.A, g.lda, m0, kb, g.M, ke, tid);
   lb.load(g.B, g.ldb, n0, kb, g.N, ke, tid);
   la.store(lds_a[0], tid);
@@ -142,22 +149,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t fa[2], fb[2];
-      const int kofs = ks * 16 + (lane >> 5) * 8;
+      bf16x8_t fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(&lds_a[cur][r * kLdsRow + kofs]);
-      }
+      for (int i = 0; i < TM; ++i) fa[i] = TA::frag(lds_a[cur], wm * TM + i, ks, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + (lane & 31);
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(&lds_b[cur][r * kLdsRow + kofs]);
-      }
+      for (int j = 0; j < TN; ++j) fb[j] = TB::frag(lds_b[cur], wn * TN + j, ks, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) {
       la.store(lds_a[cur ^ 1], tid);
@@ -165,17 +165,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
-  // accumulator layout of the 32 x 32 tile: register r of lane l holds
+  // accumulator layout of a 32 x 32 tile: register r of lane l holds
   // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + (wn * TN + j) * 32 + (lane & 31);
       if (col >= g.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = m0 + (wm * TM + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= g.M) continue;
         const float v = acc[i][j][r];
         if (g.partial) {
@@ -235,9 +235,17 @@ __global__ __launch_bounds__(256) void column_sum_final(const float* __restrict_
 
 namespace {
 
+// the block tile: 256 rows when the product has enough rows that the grid still
+// covers the chip, else 128
+int pick_bm(int M, int N) {
+  const long long big = (long long)((M + 255) / 256) * ((N + 127) / 128);
+  return (M >= 1024 && big >= 256) ? 256 : 128;
+}
+
 // how many k splits: enough blocks to cover the chip, each split at least 4 k steps
 int pick_splits(int M, int N, int K) {
-  const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int bm = pick_bm(M, N);
+  const long long tiles = (long long)((M + bm - 1) / bm) * ((N + 127) / 128);
   int s = 1;
   while (tiles * s * 2 <= 1024 && (K / (s * 2)) >= 4 * kBK) s *= 2;
   return s;
@@ -249,16 +257,17 @@ int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) 
   const int ksplit = max(kBK, ((g.K + splits - 1) / splits + kBK - 1) / kBK * kBK);
   g.k_per_split = ksplit;
   const int nsplit = (g.K + ksplit - 1) / ksplit;
-  dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM, nsplit);
+  const int bm = pick_bm(g.M, g.N);
+  dim3 grid((g.N + 127) / 128, (g.M + bm - 1) / bm, nsplit);
+  g.partial = nsplit > 1 ? partial : nullptr;
+  if (bm == 256)
+    hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT, 256, 128>), grid, dim3(kGemmThreads), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT, 128, 128>), grid, dim3(kGemmThreads), 0, st, g);
   if (nsplit > 1) {
-    g.partial = partial;
-    hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT>), grid, dim3(kGemmThreads), 0, st, g);
     const long long n = (long long)g.M * g.N;
     hipLaunchKernelGGL((splitk_reduce<OutT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
                        static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
-  } else {
-    g.partial = nullptr;
-    hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT>), grid, dim3(kGemmThreads), 0, st, g);
   }
   return SSM_OK;
 }
