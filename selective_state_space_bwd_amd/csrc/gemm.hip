@@ -58,17 +58,41 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ p, long
 }
 
 // One operand's R x 32 tile: its global -> register -> LDS moves and its MFMA
-// operand reads.  KC: k contiguous, LDS [row][k] with rows of 40 bf16; else
-// LDS [k][row] with rows of R + 16 bf16 (the padding spreads the four k rows a
-// transposing read touches over different banks).
+// operand reads.
+// KC (k contiguous): LDS [row][k], rows of 32 bf16 = four 16-byte chunks, chunk
+// c of row r stored at c ^ ((r >> 1) & 3).  Eight lanes of a 16-byte access then
+// fall in eight different 16-byte bank groups both when a store writes two rows'
+// four chunks and when a fragment read takes one chunk of eight rows.
+// Otherwise: LDS [k][row], rows of R + 16 bf16 (the padding spreads the four k
+// rows a transposing read touches over different banks).
 template <bool KC, int R>
 struct OperandTile {
-  static constexpr int kLd = KC ? kBK + 8 : R + 16;
+  static constexpr int kLd = KC ? kBK : R + 16;
   static constexpr int kElems = KC ? R * kLd : kBK * kLd;
   static constexpr int kPer = R * kBK / 8 / kGemmThreads;  // 16-byte chunks per thread
   static_assert(kPer >= 1 && R % 32 == 0, "tile shape");
   uint4 v[kPer];
 
+  static __device__ __forceinline__ int kc_offset(int r, int chunk) {
+    return r * kLd + ((chunk ^ ((r >> 1) & 3)) << 3);
+  }
+  // Interior tiles: each thread's chunks sit at fixed byte offsets from the
+  // tile's first element, so a k step only moves a wave-uniform base.
+  unsigned off[kPer];
+  __device__ __forceinline__ void init(long long ld, int tid) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int c = tid + q * kGemmThreads;
+      off[q] = KC ? (unsigned)(((c >> 2) * ld + (c & 3) * 8) * 2)
+                  : (unsigned)(((c / (R / 8)) * ld + (c % (R / 8)) * 8) * 2);
+    }
+  }
+  // tile at rows row0.., k k0.., every chunk inside the matrix
+  __device__ __forceinline__ void load_full(const uint16_t* __restrict__ base, long long ld, int row0, int k0) {
+    const char* t = reinterpret_cast<const char*>(KC ? base + row0 * ld + k0 : base + k0 * ld + row0);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) v[q] = *reinterpret_cast<const uint4*>(t + off[q]);
+  }
   __device__ __forceinline__ void load(const uint16_t* __restrict__ base, long long ld, int row0, int k0, int rows,
                                        int kend, int tid) {
 #pragma unroll
@@ -85,7 +109,7 @@ struct OperandTile {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int c = tid + q * kGemmThreads;
-      const int off = KC ? (c >> 2) * kLd + (c & 3) * 8 : (c / (R / 8)) * kLd + (c % (R / 8)) * 8;
+      const int off = KC ? kc_offset(c >> 2, c & 3) : (c / (R / 8)) * kLd + (c % (R / 8)) * 8;
       *reinterpret_cast<uint4*>(lds + off) = v[q];
     }
   }
@@ -93,7 +117,7 @@ struct OperandTile {
   // l % 32 and k 8 (l / 32) .. + 7
   static __device__ __forceinline__ bf16x8_t frag(const uint16_t* __restrict__ lds, int rt, int ks, int lane) {
     if (KC) {
-      return *reinterpret_cast<const bf16x8_t*>(&lds[(rt * 32 + (lane & 31)) * kLd + ks * 16 + (lane >> 5) * 8]);
+      return *reinterpret_cast<const bf16x8_t*>(&lds[kc_offset(rt * 32 + (lane & 31), ks * 2 + (lane >> 5))]);
     } else {
       // within a 16-lane group, lane i of the transposing read returns element
       // i % 4 of the 8-byte rows addressed by lanes 4r + i / 4, r = 0..3: lane j
@@ -134,36 +158,60 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  TA la;
-  TB lb;
-  la.load(g.A, g.lda, m0, kb, g.M, ke, tid);
-  lb.load(g.B, g.ldb, n0, kb, g.N, ke, tid);
-  la.store(lds_a[0], tid);
-  lb.store(lds_b[0], tid);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(g.A, g.lda, m0, kb + (kt + 1) * kBK, g.M, ke, tid);
-      lb.load(g.B, g.ldb, n0, kb + (kt + 1) * kBK, g.N, ke, tid);
+  // two register sets carry tiles kt + 1 and kt + 2 while the matrix cores work
+  // on tile kt from LDS: the global loads of a tile get two k steps to land
+  TA la0, la1;
+  TB lb0, lb1;
+  // a k step whose whole A and B tiles lie inside the matrices takes unchecked
+  // 16-byte loads at fixed per-thread offsets; edge tiles check every element
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+  la0.init(g.lda, tid);
+  la1.init(g.lda, tid);
+  lb0.init(g.ldb, tid);
+  lb1.init(g.ldb, tid);
+  const auto load_tile = [&](TA& a, TB& b, int k0) {
+    if (interior && k0 + kBK <= ke) {
+      a.load_full(g.A, g.lda, m0, k0);
+      b.load_full(g.B, g.ldb, n0, k0);
+    } else {
+      a.load(g.A, g.lda, m0, k0, g.M, ke, tid);
+      b.load(g.B, g.ldb, n0, k0, g.N, ke, tid);
     }
+  };
+  load_tile(la0, lb0, kb);
+  if (nk > 1) load_tile(la1, lb1, kb + kBK);
+  la0.store(lds_a[0], tid);
+  lb0.store(lds_b[0], tid);
+  __syncthreads();
+  // one k step on LDS buffer `cur`; `nxt_a/b` hold tile kt + 1, `free_a/b` take tile kt + 2
+  const auto step = [&](int kt, int cur, TA& free_a, TB& free_b, const TA& nxt_a, const TB& nxt_b) {
+    if (kt + 2 < nk) load_tile(free_a, free_b, kb + (kt + 2) * kBK);
+    // all operand reads of the k step first, so the second half's reads are in
+    // flight while the first half's products run
+    bf16x8_t fa[kBK / 16][TM], fb[kBK / 16][TN];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = TA::frag(lds_a[cur], wm * TM + i, ks, lane);
+      for (int i = 0; i < TM; ++i) fa[ks][i] = TA::frag(lds_a[cur], wm * TM + i, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = TB::frag(lds_b[cur], wn * TN + j, ks, lane);
+      for (int j = 0; j < TN; ++j) fb[ks][j] = TB::frag(lds_b[cur], wn * TN + j, ks, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
     if (kt + 1 < nk) {
-      la.store(lds_a[cur ^ 1], tid);
-      lb.store(lds_b[cur ^ 1], tid);
+      nxt_a.store(lds_a[cur ^ 1], tid);
+      nxt_b.store(lds_b[cur ^ 1], tid);
     }
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, 0, la0, lb0, la1, lb1);
+    if (kt + 1 < nk) step(kt + 1, 1, la1, lb1, la0, lb0);
   }
   // accumulator layout of a 32 x 32 tile: register r of lane l holds
   // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
