@@ -36,6 +36,7 @@ struct GemmArgs {
   int M, N, K;
   int k_per_split;  // multiple of kBK
   int accumulate;   // add into C instead of overwriting (single split only)
+  int vec_out;      // C rows allow 16-byte vectors (aligned base, ldc a multiple of the vector)
 };
 
 // one 16-byte chunk (8 bf16) of a matrix row, zero outside [0, rows) x [0, cols)
@@ -135,13 +136,65 @@ struct OperandTile {
   }
 };
 
+constexpr int kStageLd = 36;  // floats per staged row (16-byte aligned rows)
+
+// 16 consecutive outputs of one row starting at column col (< n): 16-byte
+// vectors when the row allows it, element by element at the right edge
+template <typename T>
+__device__ __forceinline__ void write_row16(T* __restrict__ rowp, int col, int n, const float (&v)[16], bool accumulate,
+                                            bool vec_ok) {
+  constexpr int V = 16 / sizeof(T);  // elements per vector
+  if (vec_ok && col + 16 <= n) {
+#pragma unroll
+    for (int q = 0; q < 16 / V; ++q) {
+      T* p = rowp + col + q * V;
+      if constexpr (sizeof(T) == 4) {
+        float4 o = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        if (accumulate) {
+          const float4 prev = *reinterpret_cast<const float4*>(p);
+          o.x += prev.x; o.y += prev.y; o.z += prev.z; o.w += prev.w;
+        }
+        *reinterpret_cast<float4*>(p) = o;
+      } else {
+        uint4 prev = make_uint4(0, 0, 0, 0);
+        if (accumulate) prev = *reinterpret_cast<const uint4*>(p);
+        const uint32_t pw[4] = {prev.x, prev.y, prev.z, prev.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float lo = v[8 * q + 2 * e], hi = v[8 * q + 2 * e + 1];
+          if (accumulate) {
+            lo += __uint_as_float(pw[e] << 16);
+            hi += __uint_as_float(pw[e] & 0xffff0000u);
+          }
+          ow[e] = uint32_t(from_f32<bf16>(lo).bits) | (uint32_t(from_f32<bf16>(hi).bits) << 16);
+        }
+        *reinterpret_cast<uint4*>(p) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (col + e < n) {
+        T* p = rowp + col + e;
+        *p = from_f32<T>((accumulate ? to_f32(*p) : 0.f) + v[e]);
+      }
+    }
+  }
+}
+
 template <bool A_K, bool B_K, typename OutT, int BM, int BN>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
   using TA = OperandTile<A_K, BM>;
   using TB = OperandTile<B_K, BN>;
   constexpr int TM = BM / 64, TN = BN / 64;  // 32 x 32 tiles per wave
-  __shared__ __align__(16) uint16_t lds_a[2][TA::kElems];
-  __shared__ __align__(16) uint16_t lds_b[2][TB::kElems];
+  // double-buffered A and B tiles; after the k loop the same space stages the
+  // output tiles (4 waves x 32 rows x kStageLd floats)
+  constexpr int kLdsElems = 2 * (TA::kElems + TB::kElems);
+  static_assert(4 * 32 * kStageLd * 2 <= kLdsElems, "epilogue staging must fit in the tile buffers");
+  __shared__ __align__(16) uint16_t lds[kLdsElems];
+  uint16_t(*lds_a)[TA::kElems] = reinterpret_cast<uint16_t(*)[TA::kElems]>(lds);
+  uint16_t(*lds_b)[TB::kElems] = reinterpret_cast<uint16_t(*)[TB::kElems]>(lds + 2 * TA::kElems);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -213,26 +266,38 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
     step(kt, 0, la0, lb0, la1, lb1);
     if (kt + 1 < nk) step(kt + 1, 1, la1, lb1, la0, lb0);
   }
-  // accumulator layout of a 32 x 32 tile: register r of lane l holds
-  // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  // Epilogue.  Accumulator layout of a 32 x 32 tile: register r of lane l holds
+  // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  Each tile goes through a
+  // per-wave LDS area so that lane l then owns row l / 2, columns 16 (l % 2) ..
+  // + 15, written (or read, added and written) as 16-byte vectors.
+  // the k loop ended with a barrier: no wave reads the tile buffers any more
+  float(*stage)[32][kStageLd] = reinterpret_cast<float(*)[32][kStageLd]>(lds);
+  float* out_f = g.partial ? g.partial + (long long)blockIdx.z * g.M * g.N : nullptr;
+  const long long ldo = g.partial ? g.N : g.ldc;
+  const bool vec_ok = g.partial ? (g.N % 4 == 0) : g.vec_out;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n0 + (wn * TN + j) * 32 + (lane & 31);
-      if (col >= g.N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + (wm * TM + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= g.M) continue;
-        const float v = acc[i][j][r];
-        if (g.partial) {
-          g.partial[((long long)blockIdx.z * g.M + row) * g.N + col] = v;
-        } else {
-          OutT* c = static_cast<OutT*>(g.C) + (long long)row * g.ldc + col;
-          const float prev = g.accumulate ? to_f32(*c) : 0.f;
-          *c = from_f32<OutT>(prev + v);
-        }
+      for (int r = 0; r < 16; ++r) stage[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(&stage[wave][lane >> 1][16 * (lane & 1) + 4 * q]);
+        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int row = m0 + (wm * TM + i) * 32 + (lane >> 1);
+      const int col = n0 + (wn * TN + j) * 32 + 16 * (lane & 1);
+      if (row >= g.M) continue;
+      if (out_f) {
+        write_row16<float>(out_f + (long long)row * ldo, col, g.N, v, false, vec_ok);
+      } else {
+        write_row16<OutT>(static_cast<OutT*>(g.C) + (long long)row * ldo, col, g.N, v, g.accumulate != 0, vec_ok);
       }
     }
 }
@@ -344,8 +409,9 @@ int gemm_check(const void* A, long long lda, const void* B, long long ldb, const
 int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool b_kcontig, long long ldb, void* C,
               long long ldc, int out_dtype, int M, int N, int K, int accumulate, void* workspace, hipStream_t st) {
   if (M == 0 || N == 0) return SSM_OK;
+  const long long vec = out_dtype == SSM_F32 ? 4 : 8;  // elements per 16-byte vector of C
   GemmArgs g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, nullptr, lda, ldb, ldc, M, N, K,
-             0, accumulate};
+             0, accumulate, aligned16(C) && ldc % vec == 0};
   const int splits = K > 0 ? pick_splits(M, N, K) : 1;
   float* part = static_cast<float*>(workspace);
 #define GEMM_CASE(AK, BK)                                                                      \
