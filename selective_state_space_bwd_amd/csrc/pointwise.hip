@@ -14,6 +14,45 @@ namespace ssm {
 
 constexpr int kPwBlock = 256;
 
+// 16 bytes of a row (8 bf16 or 4 float channels) held as float
+template <typename T>
+struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+  float v[N];
+  __device__ __forceinline__ void load(const T* __restrict__ p) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    if constexpr (sizeof(T) == 4) {
+      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+    } else {
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* __restrict__ p) const {
+    uint4 w;
+    if constexpr (sizeof(T) == 4) {
+      w = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    } else {
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        u[i] = uint32_t(from_f32<bf16>(v[2 * i]).bits) | (uint32_t(from_f32<bf16>(v[2 * i + 1]).bits) << 16);
+      w = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 __global__ __launch_bounds__(kPwBlock) void fill_zero_f32(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -107,17 +146,187 @@ __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_kernel(
   part[(p + K) * Di + d] = db;
 }
 
+// Vector form for rows of 16-byte vectors (d_inner, the strides and the bases
+// multiples of 16 bytes): a block's four waves take one vector of channels per
+// lane and four consecutive chunks of kConvTV steps, one chunk per wave.  Each
+// wave issues the loads of kConvLoad steps together, then runs them; the waves'
+// weight and bias sums combine in LDS in a fixed order into one partial per
+// block.  The K-1 steps after a chunk, needed for its last d_x outputs, are
+// recomputed by the wave (with zero gradient past the sequence end).
+constexpr int kConvTV = 32;
+constexpr int kConvWaves = kPwBlock / kWave;
+constexpr int kConvLoad = 4;
+constexpr int kConvBlockSteps = kConvTV * kConvWaves;
+
+template <typename T, int K>
+struct ConvWindow {
+  static constexpr int V = Vec16<T>::N;
+  float wk[K][V], bd[V], xs[K][V], gs[K][V];
+
+  __device__ __forceinline__ void init(const float* __restrict__ w, const float* __restrict__ bias, int d0) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        wk[k][i] = w[(size_t)(d0 + i) * K + k];
+        gs[k][i] = 0.f;
+      }
+      bd[i] = bias ? bias[d0 + i] : 0.f;
+    }
+  }
+  // shift x[t] in; returns the conv output per channel
+  __device__ __forceinline__ void push_x(const Vec16<T>& xv, float (&cv)[V]) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+#pragma unroll
+      for (int k = 0; k + 1 < K; ++k) xs[k][i] = xs[k + 1][i];
+      xs[K - 1][i] = xv.v[i];
+      float c = bd[i];
+#pragma unroll
+      for (int k = 0; k < K; ++k) c = fmaf(wk[k][i], xs[k][i], c);
+      cv[i] = c;
+    }
+  }
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(kPwBlock) void conv1d_bwd_vec(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    const T* __restrict__ d_u, T* __restrict__ d_x, float* __restrict__ part, int Tn, int Di,
+    int ld_x, int ld_du, int ld_dx) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ float red[kConvWaves - 1][(K + 1) * V][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int d0 = (blockIdx.x * kWave + lane) * V;
+  const bool on = d0 < Di;
+  const int t0 = (blockIdx.y * kConvWaves + wave) * kConvTV;
+  const int t1 = min(Tn, t0 + kConvTV);
+  const size_t rx = (size_t)blockIdx.z * Tn;
+  float dw[K + 1][V];  // K weight sums, then the bias sum
+#pragma unroll
+  for (int k = 0; k <= K; ++k)
+#pragma unroll
+    for (int i = 0; i < V; ++i) dw[k][i] = 0.f;
+
+  if (on && t0 < Tn) {
+    ConvWindow<T, K> win;
+    win.init(w, bias, d0);
+#pragma unroll
+    for (int k = 1; k < K; ++k) {  // x[t0 - K + k]; slot 0 is shifted out by the first step
+      const int tt = t0 - K + k;
+      Vec16<T> xv;
+      if (tt >= 0) {
+        xv.load(x + (rx + tt) * ld_x + d0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv.v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) win.xs[k][i] = xv.v[i];
+    }
+    // one step t: g[t] = d_u[t] SiLU'(conv[t]) (zero past the end); the weight
+    // and bias sums if the chunk owns t; d_x[t - (K-1)] once its window is full
+    const auto step = [&](int t, const Vec16<T>& xv, const Vec16<T>& uv, bool valid, bool own) {
+      float cv[V];
+      win.push_x(xv, cv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float s = sigmoid(cv[i]);
+        const float g = valid ? uv.v[i] * s * (1.f + cv[i] * (1.f - s)) : 0.f;
+#pragma unroll
+        for (int k = 0; k + 1 < K; ++k) win.gs[k][i] = win.gs[k + 1][i];
+        win.gs[K - 1][i] = g;
+        if (own) {
+#pragma unroll
+          for (int k = 0; k < K; ++k) dw[k][i] = fmaf(g, win.xs[k][i], dw[k][i]);
+          dw[K][i] += g;
+        }
+      }
+      const int to = t - (K - 1);
+      if (to >= t0) {
+        Vec16<T> o;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) acc = fmaf(win.gs[K - 1 - k][i], win.wk[k][i], acc);
+          o.v[i] = acc;
+        }
+        o.store(d_x + (rx + to) * ld_dx + d0);
+      }
+    };
+    for (int tb = t0; tb < t1; tb += kConvLoad) {
+      Vec16<T> xv[kConvLoad], uv[kConvLoad];
+#pragma unroll
+      for (int s = 0; s < kConvLoad; ++s) {  // clamped rows keep the loads unconditional
+        const int t = min(tb + s, t1 - 1);
+        xv[s].load(x + (rx + t) * ld_x + d0);
+        uv[s].load(d_u + (rx + t) * ld_du + d0);
+      }
+#pragma unroll
+      for (int s = 0; s < kConvLoad; ++s)
+        if (tb + s < t1) step(tb + s, xv[s], uv[s], true, true);
+    }
+    if constexpr (K > 1) {
+      Vec16<T> xv[K - 1], uv[K - 1];
+#pragma unroll
+      for (int s = 0; s < K - 1; ++s) {
+        const int t = min(t1 + s, Tn - 1);
+        xv[s].load(x + (rx + t) * ld_x + d0);
+        uv[s].load(d_u + (rx + t) * ld_du + d0);
+      }
+#pragma unroll
+      for (int s = 0; s < K - 1; ++s) step(t1 + s, xv[s], uv[s], t1 + s < Tn, false);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int k = 0; k <= K; ++k)
+#pragma unroll
+      for (int i = 0; i < V; ++i) red[wave - 1][k * V + i][lane] = dw[k][i];
+  }
+  __syncthreads();
+  if (wave == 0 && on) {
+    float* dst = part + (((size_t)blockIdx.z * gridDim.y + blockIdx.y) * (K + 1)) * Di + d0;
+#pragma unroll
+    for (int k = 0; k <= K; ++k) {
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        float4 o;
+        o.x = dw[k][i] + red[0][k * V + i][lane] + red[1][k * V + i][lane] + red[2][k * V + i][lane];
+        o.y = dw[k][i + 1] + red[0][k * V + i + 1][lane] + red[1][k * V + i + 1][lane] + red[2][k * V + i + 1][lane];
+        o.z = dw[k][i + 2] + red[0][k * V + i + 2][lane] + red[1][k * V + i + 2][lane] + red[2][k * V + i + 2][lane];
+        o.w = dw[k][i + 3] + red[0][k * V + i + 3][lane] + red[1][k * V + i + 3][lane] + red[2][k * V + i + 3][lane];
+        *reinterpret_cast<float4*>(dst + (size_t)k * Di + i) = o;
+      }
+    }
+  }
+}
+
+// d_w[d, k] and d_bias[d]: sums over the parts [parts][K + 1][Di] in a fixed
+// order; a block owns 64 of the (K + 1) Di columns, its four waves take every
+// fourth part and combine in LDS
 template <int K>
 __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_finalize(const float* __restrict__ part,
                                                                 float* __restrict__ d_w,
                                                                 float* __restrict__ d_bias, int parts, int Di) {
-  const int idx = blockIdx.x * kPwBlock + threadIdx.x;
-  if (idx >= (K + 1) * Di) return;
-  const int k = idx / Di, d = idx - k * Di;
+  __shared__ float s[4][kWave];
+  const int lane = threadIdx.x & (kWave - 1), grp = threadIdx.x / kWave;
+  const int ncol = (K + 1) * Di;
+  const int col = blockIdx.x * kWave + lane;
   float acc = 0.f;
-  for (int p = 0; p < parts; ++p) acc += part[((size_t)p * (K + 1) + k) * Di + d];
-  if (k < K) d_w[(size_t)d * K + k] = acc;
-  else if (d_bias) d_bias[d] = acc;
+  if (col < ncol) {
+#pragma unroll 8
+    for (int p = grp; p < parts; p += 4) acc += part[(size_t)p * ncol + col];
+  }
+  s[grp][lane] = acc;
+  __syncthreads();
+  if (grp == 0 && col < ncol) {
+    const float v = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
+    const int k = col / Di, d = col - k * Di;
+    if (k < K) d_w[(size_t)d * K + k] = v;
+    else if (d_bias) d_bias[d] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -202,44 +411,6 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_kernel(
 // four waves combine them in LDS.
 constexpr int kRmsMaxVec = 6;
 constexpr int kRmsWaveRows = 16;  // rows per wave (a block of 4 waves takes 64)
-
-template <typename T>
-struct Vec16 {
-  static constexpr int N = 16 / sizeof(T);
-  float v[N];
-  __device__ __forceinline__ void load(const T* __restrict__ p) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    if constexpr (sizeof(T) == 4) {
-      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
-    } else {
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(u[i] << 16);
-        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(T* __restrict__ p) const {
-    uint4 w;
-    if constexpr (sizeof(T) == 4) {
-      w = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
-    } else {
-      uint32_t u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        u[i] = uint32_t(from_f32<bf16>(v[2 * i]).bits) | (uint32_t(from_f32<bf16>(v[2 * i + 1]).bits) << 16);
-      w = make_uint4(u[0], u[1], u[2], u[3]);
-    }
-    *reinterpret_cast<uint4*>(p) = w;
-  }
-};
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 template <typename T, int J>
 __global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_wave(const T* __restrict__ x, const float* __restrict__ w,
@@ -405,47 +576,69 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_kernel(const bf16* __res
   }
 }
 
-// u[b,t,d] = SiLU(bias[d] + sum_k w[d,k] x[b, t-(K-1)+k, d]); thread per (b, chunk, d)
+// u[b,t,d] = SiLU(bias[d] + sum_k w[d,k] x[b, t-(K-1)+k, d]), on 8-channel
+// vectors: a lane per vector and a wave per chunk of kConvTV steps, as in the
+// vector conv backward
 template <int K>
-__global__ __launch_bounds__(kPwBlock) void conv_silu_fwd_kernel(const bf16* __restrict__ x, int ld_x,
-                                                                 const float* __restrict__ w,
-                                                                 const float* __restrict__ bias, bf16* __restrict__ u,
-                                                                 int ld_u, int Tn, int Di) {
-  const int d = blockIdx.x * kPwBlock + threadIdx.x;
-  const int c = blockIdx.y, b = blockIdx.z;
-  if (d >= Di) return;
-  float wk[K], xs[K];
+__global__ __launch_bounds__(kPwBlock) void conv_silu_fwd_vec(const bf16* __restrict__ x, int ld_x,
+                                                              const float* __restrict__ w,
+                                                              const float* __restrict__ bias, bf16* __restrict__ u,
+                                                              int ld_u, int Tn, int Di) {
+  constexpr int V = Vec16<bf16>::N;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int d0 = (blockIdx.x * kWave + lane) * V;
+  const int t0 = (blockIdx.y * kConvWaves + wave) * kConvTV;
+  if (d0 >= Di || t0 >= Tn) return;
+  const int t1 = min(Tn, t0 + kConvTV);
+  const size_t rx = (size_t)blockIdx.z * Tn;
+  ConvWindow<bf16, K> win;
+  win.init(w, bias, d0);
 #pragma unroll
-  for (int k = 0; k < K; ++k) wk[k] = w[(size_t)d * K + k];
-  const float bd = bias ? bias[d] : 0.f;
-  const int t0 = c * kConvT, t1 = min(Tn, t0 + kConvT);
-  const size_t rx = (size_t)b * Tn;
-#pragma unroll
-  for (int k = 1; k < K; ++k) {  // xs[k] holds x[t0 - K + k] before the first shift
+  for (int k = 1; k < K; ++k) {
     const int tt = t0 - K + k;
-    xs[k] = tt >= 0 ? ld(x, (rx + tt) * ld_x + d) : 0.f;
+    Vec16<bf16> xv;
+    if (tt >= 0) {
+      xv.load(x + (rx + tt) * ld_x + d0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) xv.v[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) win.xs[k][i] = xv.v[i];
   }
-  for (int t = t0; t < t1; ++t) {
+  for (int tb = t0; tb < t1; tb += kConvLoad) {
+    Vec16<bf16> xv[kConvLoad];
 #pragma unroll
-    for (int k = 0; k + 1 < K; ++k) xs[k] = xs[k + 1];
-    xs[K - 1] = ld(x, (rx + t) * ld_x + d);
-    float c_ = bd;
+    for (int s = 0; s < kConvLoad; ++s) xv[s].load(x + (rx + min(tb + s, t1 - 1)) * ld_x + d0);
 #pragma unroll
-    for (int k = 0; k < K; ++k) c_ = fmaf(wk[k], xs[k], c_);
-    st(u, (rx + t) * ld_u + d, c_ * sigmoid(c_));
+    for (int s = 0; s < kConvLoad; ++s) {
+      if (tb + s < t1) {
+        float cv[V];
+        win.push_x(xv[s], cv);
+        Vec16<bf16> o;
+#pragma unroll
+        for (int i = 0; i < V; ++i) o.v[i] = cv[i] * sigmoid(cv[i]);
+        o.store(u + (rx + tb + s) * ld_u + d0);
+      }
+    }
   }
 }
 
-// gated = y * SiLU(z), z rows of stride ld_z
-__global__ __launch_bounds__(kPwBlock) void gate_fwd_kernel(const bf16* __restrict__ y, const bf16* __restrict__ z,
-                                                            int ld_z, bf16* __restrict__ g, int64_t rows, int Di) {
-  const int64_t n = rows * Di;
+// gated = y * SiLU(z) on 8-channel vectors, z rows of stride ld_z
+__global__ __launch_bounds__(kPwBlock) void gate_fwd_vec(const bf16* __restrict__ y, const bf16* __restrict__ z,
+                                                         int ld_z, bf16* __restrict__ g, int64_t rows, int nvec) {
+  constexpr int V = Vec16<bf16>::N;
+  const int64_t n = rows * nvec;
   const int64_t stride = (int64_t)gridDim.x * kPwBlock;
   for (int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x; i < n; i += stride) {
-    const int64_t r = i / Di;
-    const int d = (int)(i - r * Di);
-    const float zz = ld(z, (size_t)r * ld_z + d);
-    st(g, i, ld(y, i) * zz * sigmoid(zz));
+    const int64_t r = i / nvec;
+    const int dv = (int)(i - r * nvec);
+    Vec16<bf16> yv, zv;
+    yv.load(y + i * V);
+    zv.load(z + (size_t)r * ld_z + (size_t)dv * V);
+#pragma unroll
+    for (int k = 0; k < V; ++k) yv.v[k] = yv.v[k] * zv.v[k] * sigmoid(zv.v[k]);
+    yv.store(g + i * V);
   }
 }
 
@@ -500,10 +693,10 @@ void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, i
 void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* bias, bf16* u, int ld_u, int Bt,
                           int Tn, int Di, int K, hipStream_t st) {
   if ((int64_t)Bt * Tn == 0) return;
-  const dim3 grid((Di + kPwBlock - 1) / kPwBlock, (Tn + kConvT - 1) / kConvT, Bt);
-#define CONV_FWD(KV)                                                                                            \
-  case KV:                                                                                                      \
-    hipLaunchKernelGGL(conv_silu_fwd_kernel<KV>, grid, dim3(kPwBlock), 0, st, x, ld_x, w, bias, u, ld_u, Tn, Di); \
+  const dim3 grid((Di / 8 + kWave - 1) / kWave, (Tn + kConvBlockSteps - 1) / kConvBlockSteps, Bt);
+#define CONV_FWD(KV)                                                                                         \
+  case KV:                                                                                                   \
+    hipLaunchKernelGGL(conv_silu_fwd_vec<KV>, grid, dim3(kPwBlock), 0, st, x, ld_x, w, bias, u, ld_u, Tn, Di); \
     break;
   switch (K) { CONV_FWD(1) CONV_FWD(2) CONV_FWD(3) CONV_FWD(4) CONV_FWD(5) CONV_FWD(6) CONV_FWD(7) CONV_FWD(8) }
 #undef CONV_FWD
@@ -511,7 +704,7 @@ void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* 
 
 void launch_gate_fwd(const bf16* y, const bf16* z, int ld_z, bf16* g, int64_t rows, int Di, hipStream_t st) {
   if (rows * Di == 0) return;
-  hipLaunchKernelGGL(gate_fwd_kernel, dim3(grid_for(rows * Di)), dim3(kPwBlock), 0, st, y, z, ld_z, g, rows, Di);
+  hipLaunchKernelGGL(gate_fwd_vec, dim3(grid_for(rows * Di / 8)), dim3(kPwBlock), 0, st, y, z, ld_z, g, rows, Di / 8);
 }
 
 void launch_bias_softplus(bf16* v, const float* b, int64_t rows, int Di, hipStream_t st) {
@@ -571,15 +764,24 @@ extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, cons
   const size_t need = conv1d_bwd_workspace_size(batch, seqlen, d_inner, d_conv);
   if (!workspace || ws_bytes < need)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
-  const int nchunk = (seqlen + kConvT - 1) / kConvT;
-  dim3 grid((d_inner + kPwBlock - 1) / kPwBlock, nchunk, batch);
   float* part = static_cast<float*>(workspace);
-#define CONV_CASE(TY, KV)                                                                                     \
-  case KV:                                                                                                    \
-    hipLaunchKernelGGL((conv1d_bwd_kernel<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,     \
-                       (const TY*)d_u, (TY*)d_x, part, batch, seqlen, d_inner, ld_x, ld_du, ld_dx, nchunk); \
-    hipLaunchKernelGGL((conv1d_bwd_finalize<KV>), dim3(((KV + 1) * d_inner + kPwBlock - 1) / kPwBlock),      \
-                       dim3(kPwBlock), 0, st, part, d_w, d_bias, batch * nchunk, d_inner);                  \
+  const int V = dtype == SSM_F32 ? 4 : 8;
+  const bool vec = d_inner % V == 0 && ld_x % V == 0 && ld_du % V == 0 && ld_dx % V == 0 && aligned16(x) &&
+                   aligned16(d_u) && aligned16(d_x) && aligned16(workspace);
+  const int nchunk = vec ? (seqlen + kConvBlockSteps - 1) / kConvBlockSteps : (seqlen + kConvT - 1) / kConvT;
+  const dim3 grid = vec ? dim3((d_inner / V + kWave - 1) / kWave, nchunk, batch)
+                        : dim3((d_inner + kPwBlock - 1) / kPwBlock, nchunk, batch);
+  const dim3 fgrid(((d_conv + 1) * d_inner + kWave - 1) / kWave);
+#define CONV_CASE(TY, KV)                                                                                      \
+  case KV:                                                                                                     \
+    if (vec)                                                                                                   \
+      hipLaunchKernelGGL((conv1d_bwd_vec<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,        \
+                         (const TY*)d_u, (TY*)d_x, part, seqlen, d_inner, ld_x, ld_du, ld_dx);                \
+    else                                                                                                       \
+      hipLaunchKernelGGL((conv1d_bwd_kernel<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,     \
+                         (const TY*)d_u, (TY*)d_x, part, batch, seqlen, d_inner, ld_x, ld_du, ld_dx, nchunk); \
+    hipLaunchKernelGGL((conv1d_bwd_finalize<KV>), fgrid, dim3(kPwBlock), 0, st, part, d_w, d_bias,            \
+                       batch * nchunk, d_inner);                                                              \
     break;
   if (dtype == SSM_F32) {
     switch (d_conv) { CONV_CASE(float, 1) CONV_CASE(float, 2) CONV_CASE(float, 3) CONV_CASE(float, 4)

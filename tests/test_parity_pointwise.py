@@ -40,13 +40,20 @@ def test_gating_bwd(dt, n):
     assert norm_err(_np(d_z), rz) < TOL[dt]
 
 
-CONV = [  # batch, seqlen, d_inner, d_conv, dtype, row stride of x (>= d_inner)
+# batch, seqlen, d_inner, d_conv, dtype, row stride of x (>= d_inner).  Rows of whole
+# 16-byte vectors (f32 d_inner and stride multiples of 4, bf16 of 8) take the vector
+# kernel (128-step blocks, ragged here), the others the one-channel-per-thread kernel.
+CONV = [
     (2, 150, 70, 4, "f32", 70),
     (1, 3, 9, 4, "f32", 9),
     (3, 64, 33, 2, "f32", 40),
     (2, 129, 256, 4, "bf16", 512),
     (1, 200, 16, 1, "f32", 16),
     (2, 65, 20, 8, "f32", 20),
+    (2, 300, 136, 3, "bf16", 136),
+    (1, 77, 36, 4, "bf16", 36),
+    (1, 140, 64, 8, "bf16", 64),
+    (2, 260, 64, 4, "f32", 96),
 ]
 
 
