@@ -19,8 +19,8 @@ template <typename T>
 struct Vec16 {
   static constexpr int N = 16 / sizeof(T);
   float v[N];
-  __device__ __forceinline__ void load(const T* __restrict__ p) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
+  __device__ __forceinline__ void load(const T* __restrict__ p) { set(*reinterpret_cast<const uint4*>(p)); }
+  __device__ __forceinline__ void set(const uint4 w) {
     if constexpr (sizeof(T) == 4) {
       v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
     } else {
@@ -255,28 +255,37 @@ __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_vec(
         o.store(d_x + (rx + to) * ld_dx + d0);
       }
     };
-    for (int tb = t0; tb < t1; tb += kConvLoad) {
-      Vec16<T> xv[kConvLoad], uv[kConvLoad];
+    // steps t0 .. t1 + K - 2 in groups of kConvLoad; the rows of the next group
+    // are loaded (raw) before the current group runs.  Rows are clamped to the
+    // last one the wave reads, so every load is in bounds and unconditional.
+    const int te = t1 + K - 1, tlast = min(te, Tn) - 1;
+    uint4 xr[kConvLoad], ur[kConvLoad];
 #pragma unroll
-      for (int s = 0; s < kConvLoad; ++s) {  // clamped rows keep the loads unconditional
-        const int t = min(tb + s, t1 - 1);
-        xv[s].load(x + (rx + t) * ld_x + d0);
-        uv[s].load(d_u + (rx + t) * ld_du + d0);
-      }
-#pragma unroll
-      for (int s = 0; s < kConvLoad; ++s)
-        if (tb + s < t1) step(tb + s, xv[s], uv[s], true, true);
+    for (int s = 0; s < kConvLoad; ++s) {
+      const int t = min(t0 + s, tlast);
+      xr[s] = *reinterpret_cast<const uint4*>(x + (rx + t) * ld_x + d0);
+      ur[s] = *reinterpret_cast<const uint4*>(d_u + (rx + t) * ld_du + d0);
     }
-    if constexpr (K > 1) {
-      Vec16<T> xv[K - 1], uv[K - 1];
+    for (int tb = t0; tb < te; tb += kConvLoad) {
+      uint4 xn[kConvLoad], un[kConvLoad];
 #pragma unroll
-      for (int s = 0; s < K - 1; ++s) {
-        const int t = min(t1 + s, Tn - 1);
-        xv[s].load(x + (rx + t) * ld_x + d0);
-        uv[s].load(d_u + (rx + t) * ld_du + d0);
+      for (int s = 0; s < kConvLoad; ++s) {
+        const int t = min(tb + kConvLoad + s, tlast);
+        xn[s] = *reinterpret_cast<const uint4*>(x + (rx + t) * ld_x + d0);
+        un[s] = *reinterpret_cast<const uint4*>(d_u + (rx + t) * ld_du + d0);
       }
 #pragma unroll
-      for (int s = 0; s < K - 1; ++s) step(t1 + s, xv[s], uv[s], t1 + s < Tn, false);
+      for (int s = 0; s < kConvLoad; ++s) {
+        const int t = tb + s;
+        if (t < te) {
+          Vec16<T> xv, uv;
+          xv.set(xr[s]);
+          uv.set(ur[s]);
+          step(t, xv, uv, t < Tn, t < t1);
+        }
+        xr[s] = xn[s];
+        ur[s] = un[s];
+      }
     }
   }
   if (wave > 0) {
@@ -410,7 +419,10 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_kernel(
 // the weight-gradient sums stay in registers over the block's rows before the
 // four waves combine them in LDS.
 constexpr int kRmsMaxVec = 6;
-constexpr int kRmsWaveRows = 16;  // rows per wave (a block of 4 waves takes 64)
+// rows per wave: few, so that a layer's 16k rows make thousands of blocks and
+// several waves per SIMD hide the load -> row sum -> store chain of each row
+constexpr int kRmsFwdWaveRows = 2;
+constexpr int kRmsBwdWaveRows = 4;  // also sets the number of weight-sum partials
 
 template <typename T, int J>
 __global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_wave(const T* __restrict__ x, const float* __restrict__ w,
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_wave(const T* __restrict
     for (int i = 0; i < V; ++i) wv[j][i] = (lane + kWave * j < nvec) ? w[c + i] : 0.f;
   }
   const float inv_dim = 1.f / (float)dim;
-  const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsWaveRows, r1 = min(rows, r0 + 4 * kRmsWaveRows);
+  const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsFwdWaveRows, r1 = min(rows, r0 + 4 * kRmsFwdWaveRows);
   for (int64_t r = r0 + wave; r < r1; r += 4) {
     Vec16<T> xv[J];
     float ss = 0.f;
@@ -473,7 +485,7 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_wave(const T* __restrict
     }
   }
   const float inv_dim = 1.f / (float)dim;
-  const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsWaveRows, r1 = min(rows, r0 + 4 * kRmsWaveRows);
+  const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsBwdWaveRows, r1 = min(rows, r0 + 4 * kRmsBwdWaveRows);
   for (int64_t r = r0 + wave; r < r1; r += 4) {
     Vec16<T> xv[J], gv[J];
     float ss = 0.f, sd = 0.f;
@@ -606,20 +618,28 @@ __global__ __launch_bounds__(kPwBlock) void conv_silu_fwd_vec(const bf16* __rest
 #pragma unroll
     for (int i = 0; i < V; ++i) win.xs[k][i] = xv.v[i];
   }
-  for (int tb = t0; tb < t1; tb += kConvLoad) {
-    Vec16<bf16> xv[kConvLoad];
+  uint4 xr[kConvLoad];
 #pragma unroll
-    for (int s = 0; s < kConvLoad; ++s) xv[s].load(x + (rx + min(tb + s, t1 - 1)) * ld_x + d0);
+  for (int s = 0; s < kConvLoad; ++s)
+    xr[s] = *reinterpret_cast<const uint4*>(x + (rx + min(t0 + s, t1 - 1)) * ld_x + d0);
+  for (int tb = t0; tb < t1; tb += kConvLoad) {
+    uint4 xn[kConvLoad];
+#pragma unroll
+    for (int s = 0; s < kConvLoad; ++s)
+      xn[s] = *reinterpret_cast<const uint4*>(x + (rx + min(tb + kConvLoad + s, t1 - 1)) * ld_x + d0);
 #pragma unroll
     for (int s = 0; s < kConvLoad; ++s) {
       if (tb + s < t1) {
+        Vec16<bf16> xv;
+        xv.set(xr[s]);
         float cv[V];
-        win.push_x(xv[s], cv);
+        win.push_x(xv, cv);
         Vec16<bf16> o;
 #pragma unroll
         for (int i = 0; i < V; ++i) o.v[i] = cv[i] * sigmoid(cv[i]);
         o.store(u + (rx + tb + s) * ld_u + d0);
       }
+      xr[s] = xn[s];
     }
   }
 }
@@ -678,7 +698,7 @@ int rms_wave_vecs(const void* a, const void* b, const void* c, const void* d, in
 void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, int dim, float eps, hipStream_t st) {
   if (rows == 0) return;
   const int j = rms_wave_vecs<bf16>(x, xn, nullptr, nullptr, dim);
-  const dim3 grid((unsigned)((rows + 4 * kRmsWaveRows - 1) / (4 * kRmsWaveRows)));
+  const dim3 grid((unsigned)((rows + 4 * kRmsFwdWaveRows - 1) / (4 * kRmsFwdWaveRows)));
   switch (j) {
 #define RMS_FWD(J) \
   case J: hipLaunchKernelGGL((rmsnorm_fwd_wave<bf16, J>), grid, dim3(kPwBlock), 0, st, x, w, xn, rows, dim, eps); return;
@@ -796,7 +816,9 @@ extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, cons
 
 extern "C" size_t rmsnorm_bwd_workspace_size(int64_t rows, int dim) {
   if (rows <= 0 || dim <= 0 || dim > kPwBlock * kRmsMaxCols) return 0;
-  const size_t blocks = (size_t)((rows + kRmsRows - 1) / kRmsRows);
+  // one partial row per block of either kernel
+  constexpr int rows_per_block = kRmsRows < 4 * kRmsBwdWaveRows ? kRmsRows : 4 * kRmsBwdWaveRows;
+  const size_t blocks = (size_t)((rows + rows_per_block - 1) / rows_per_block);
   return align_up(blocks * dim * sizeof(float));
 }
 
@@ -823,7 +845,7 @@ extern "C" int rmsnorm_bwd(const void* x, const float* w, const void* dy, const 
   const int jw = dtype == SSM_F32 ? rms_wave_vecs<float>(x, dy, d_residual, dx, dim)
                                   : rms_wave_vecs<bf16>(x, dy, d_residual, dx, dim);
   if (jw > 0) {
-    blocks = (int)((rows + 4 * kRmsWaveRows - 1) / (4 * kRmsWaveRows));
+    blocks = (int)((rows + 4 * kRmsBwdWaveRows - 1) / (4 * kRmsBwdWaveRows));
 #define RMS_BWD(TY, J)                                                                                          \
   case J:                                                                                                       \
     hipLaunchKernelGGL((rmsnorm_bwd_wave<TY, J>), dim3(blocks), dim3(kPwBlock), 0, st, (const TY*)x, w,         \
