@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--ckpt", action="store_true",
+                    help="scan workloads: time ssm_scan_bwd_ckpt, the backward that takes the forward's state "
+                         "before every 8-step chunk (made once by ssm_scan_fwd before the timed steps)")
     return ap.parse_args()
 
 
@@ -182,20 +185,33 @@ def run_scan(args, cfg):
     out["d_A_log"] = torch.empty_like(t["A_log"])
     out["d_D"] = torch.empty_like(t["D"])
     dims = ssm.scan_dims(t["u"], t["B"], seg_len=args.seg_len)
-    ws = torch.empty(ssm.ssm_scan_bwd_workspace_size(dims, tdt), dtype=torch.uint8, device=dev)
+    if args.ckpt:
+        h_ckpt = ssm.ssm_scan_fwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], want_y=False,
+                                  want_out=False, ckpt_every=8)["h_ckpt"]
+        ws = torch.empty(ssm.ssm_scan_bwd_ckpt_workspace_size(dims, tdt), dtype=torch.uint8, device=dev)
 
-    def step(ev):
-        ssm.ssm_scan_bwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
-                         out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
+        def step(ev):
+            ssm.ssm_scan_bwd_ckpt(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
+                                  h_ckpt, out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
+    else:
+        ws = torch.empty(ssm.ssm_scan_bwd_workspace_size(dims, tdt), dtype=torch.uint8, device=dev)
+
+        def step(ev):
+            ssm.ssm_scan_bwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
+                             out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
 
     ms_step, stages = timed(step, 5, args.steps, args.warmup)
     se = cfg.state_elements
     el = 4 if cfg.dtype == "f32" else 2
     rows = cfg.batch * cfg.seqlen
-    alg_bytes = (7 * rows * cfg.d_inner + 4 * rows * cfg.d_state) * el + (2 * cfg.d_inner * (cfg.d_state + 1)) * 4
+    # with given chunk states, the float32 states before every 8-step chunk are one more input
+    ckpt_bytes = 4 * cfg.batch * ((cfg.seqlen + 7) // 8) * cfg.d_state * cfg.d_inner if args.ckpt else 0
+    alg_bytes = ((7 * rows * cfg.d_inner + 4 * rows * cfg.d_state) * el + (2 * cfg.d_inner * (cfg.d_state + 1)) * 4
+                 + ckpt_bytes)
     main_ms = float(stages[:, 2].mean())
-    # the main sweep reads u, delta, z, d_out, B, C and writes d_u, d_delta, d_z (d_B, d_C go out as partials)
-    main_bytes = (7 * rows * cfg.d_inner + 2 * rows * cfg.d_state) * el
+    # the main sweep reads u, delta, z, d_out, B, C (and the given chunk states) and writes d_u, d_delta, d_z
+    # (d_B, d_C go out as partials)
+    main_bytes = (7 * rows * cfg.d_inner + 2 * rows * cfg.d_state) * el + ckpt_bytes
     main_gbps = main_bytes / (main_ms * 1e-3) / 1e9
     main_tflops = FLOPS_PER_SE * se / (main_ms * 1e-3) / 1e12
     hbm_frac = main_gbps / HBM_PEAK_GBPS
@@ -206,7 +222,7 @@ def run_scan(args, cfg):
     else:
         roof = {"bound": "hbm", "achieved": round(main_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(hbm_frac, 4)}
-    roof["traffic"] = recorded_traffic(args.workload, "scan_bwd_main")
+    roof["traffic"] = None if args.ckpt else recorded_traffic(args.workload, "scan_bwd_main")
     roof.update({"kernel": "scan_bwd_main", "kernel_ms": round(main_ms, 4), "hbm_frac": round(hbm_frac, 4),
                  "alu_frac": round(alu_frac, 4), "algorithmic_bytes": main_bytes})
     line = {
@@ -214,7 +230,8 @@ def run_scan(args, cfg):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_inner": cfg.d_inner,
-                   "d_state": cfg.d_state, "seg_len": args.seg_len or "auto", "storage": cfg.dtype},
+                   "d_state": cfg.d_state, "seg_len": args.seg_len or "auto", "storage": cfg.dtype,
+                   "chunk_states": "given by the forward" if args.ckpt else "rebuilt"},
         "hbm": {"algorithmic_bytes": alg_bytes, "effective_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "stages_ms": {"summary": round(float(stages[:, 0].mean()), 4), "carry": round(float(stages[:, 1].mean()), 4),

@@ -117,6 +117,29 @@ int ssm_scan_bwd_timed(const void* u, const void* delta, const float* A_log, con
                        void* stream, void* const* stage_events);
 
 /* ---------------------------------------------------------------------------
+ * ssm_scan_bwd_ckpt — ssm_scan_bwd for a caller whose forward kept the state
+ * before every 8-step chunk, as ssm_scan_fwd writes it with ckpt_every = 8:
+ * h_ckpt[b, k, n, d] = h_{8k - 1} (zero for k = 0), k = 0 .. ceil(seqlen / 8) - 1,
+ * float, [batch, ceil(seqlen / 8), d_state, d_inner] contiguous, read only.
+ * (mamba-rs Phase B3 reads saved per-step states back; here only the chunk
+ * boundaries are kept.)  The backward then skips rebuilding the states of each
+ * segment: its first pass only sums delta and the adjoint summary of each
+ * segment, and each chunk starts from the given state.  Same outputs as
+ * ssm_scan_bwd up to float rounding when h_ckpt holds the forward's states;
+ * arguments otherwise as ssm_scan_bwd, with `stage_events` as in
+ * ssm_scan_bwd_timed (nullable).  h_ckpt must not be null.
+ * Workspace: ssm_scan_bwd_ckpt_workspace_size() (smaller: no local
+ * checkpoints).
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan_bwd_ckpt_workspace_size(const ssm_dims* dims, int dtype);
+int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A_log, const void* B,
+                      const void* C, const float* D, const void* z, const void* d_out,
+                      const float* h_ckpt, void* d_u, void* d_delta, float* d_A_log, void* d_B,
+                      void* d_C, float* d_D, void* d_z, int softplus_epilogue,
+                      void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype,
+                      void* stream, void* const* stage_events);
+
+/* ---------------------------------------------------------------------------
  * ssm_scan_fwd — the forward recurrence above (the page's forward is implied
  * by the states Phase B3 reads back).  Writes y (nullable), out = y * SiLU(z)
  * (nullable; requires z) and, if h_ckpt is not null, the state before every

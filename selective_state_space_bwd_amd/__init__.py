@@ -63,6 +63,9 @@ _SIGS = {
                           _vp, _sz, _dims_p, _i, _vp]),
     "ssm_scan_bwd_timed": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _i,
                                 _vp, _sz, _dims_p, _i, _vp, ctypes.POINTER(ctypes.c_void_p)]),
+    "ssm_scan_bwd_ckpt_workspace_size": (_sz, [_dims_p, _i]),
+    "ssm_scan_bwd_ckpt": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _i,
+                               _vp, _sz, _dims_p, _i, _vp, ctypes.POINTER(ctypes.c_void_p)]),
     "ssm_scan_fwd_workspace_size": (_sz, [_dims_p, _i]),
     "ssm_scan_fwd": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _i, _vp, _sz, _dims_p, _i, _vp]),
     "gating_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _vp]),
@@ -174,6 +177,11 @@ def ssm_scan_bwd_workspace_size(dims: ssm_dims, dtype: torch.dtype) -> int:
     return int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(dims), SSM_F32 if dtype == torch.float32 else SSM_BF16))
 
 
+def ssm_scan_bwd_ckpt_workspace_size(dims: ssm_dims, dtype: torch.dtype) -> int:
+    return int(lib().ssm_scan_bwd_ckpt_workspace_size(ctypes.byref(dims),
+                                                      SSM_F32 if dtype == torch.float32 else SSM_BF16))
+
+
 def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool = False, seg_len: int = 0,
                  out: dict | None = None, workspace: torch.Tensor | None = None, stage_events=None) -> dict:
     """Backward of out = y * SiLU(z) through the selective scan; returns the seven gradients.
@@ -181,6 +189,21 @@ def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool 
     ``out`` may supply any of the output tensors (d_B / d_C may be strided views into a
     wider row, as the layer's x_proj gradient).  See ``ssm_scan_bwd`` in include/ssmbwd.h.
     """
+    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, None, softplus_epilogue, seg_len, out, workspace,
+                     stage_events)
+
+
+def ssm_scan_bwd_ckpt(u, delta, A_log, B, C, D, z, d_out, h_ckpt, *, softplus_epilogue: bool = False,
+                      seg_len: int = 0, out: dict | None = None, workspace: torch.Tensor | None = None,
+                      stage_events=None) -> dict:
+    """ssm_scan_bwd taking the forward's state before every 8-step chunk, h_ckpt
+    [B, ceil(T / 8), N, Di] float32 (``ssm_scan_fwd(..., ckpt_every=8)["h_ckpt"]``)."""
+    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, softplus_epilogue, seg_len, out, workspace,
+                     stage_events)
+
+
+def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, softplus_epilogue, seg_len, out, workspace,
+              stage_events) -> dict:
     dt = _dtype_code(u)
     batch, seqlen, d_inner = u.shape
     n = A_log.shape[1]
@@ -208,17 +231,29 @@ def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool 
     ldd = _row_stride(o["d_B"], batch, seqlen, n, "d_B")
     _need(_row_stride(o["d_C"], batch, seqlen, n, "d_C") == ldd, "d_B and d_C must share a row stride")
     dims = ssm_dims(batch, seqlen, d_inner, n, ld, ldd, seg_len, ldz)
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
+    if h_ckpt is not None:
+        nk = (seqlen + 7) // 8
+        _need(h_ckpt.dtype == torch.float32 and tuple(h_ckpt.shape) == (batch, nk, n, d_inner)
+              and h_ckpt.is_contiguous(), f"h_ckpt must be float32 [{batch}, {nk}, {n}, {d_inner}], contiguous")
+        nbytes = int(lib().ssm_scan_bwd_ckpt_workspace_size(ctypes.byref(dims), dt))
+        ws, wsb = _workspace(nbytes, dev, workspace)
+        rc = lib().ssm_scan_bwd_ckpt(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                     _ptr(d_out), _ptr(h_ckpt), _ptr(o["d_u"]), _ptr(o["d_delta"]),
+                                     _ptr(o["d_A_log"]), _ptr(o["d_B"]), _ptr(o["d_C"]), _ptr(o["d_D"]),
+                                     _ptr(o["d_z"]), int(bool(softplus_epilogue)), _ptr(ws), wsb,
+                                     ctypes.byref(dims), dt, _stream(u), ev)
+        _check("ssm_scan_bwd_ckpt", rc)
+        return o
     nbytes = int(lib().ssm_scan_bwd_workspace_size(ctypes.byref(dims), dt))
     ws, wsb = _workspace(nbytes, dev, workspace)
     args = (_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(d_out),
             _ptr(o["d_u"]), _ptr(o["d_delta"]), _ptr(o["d_A_log"]), _ptr(o["d_B"]),
             _ptr(o["d_C"]), _ptr(o["d_D"]), _ptr(o["d_z"]), int(bool(softplus_epilogue)),
             _ptr(ws), wsb, ctypes.byref(dims), dt, _stream(u))
-    if stage_events is None:
-        rc = lib().ssm_scan_bwd(*args)
-    else:
-        ev = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
-        rc = lib().ssm_scan_bwd_timed(*args, ev)
+    rc = lib().ssm_scan_bwd(*args) if ev is None else lib().ssm_scan_bwd_timed(*args, ev)
     _check("ssm_scan_bwd", rc)
     return o
 

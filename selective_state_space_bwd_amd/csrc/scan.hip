@@ -211,11 +211,65 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
   seg_sd[sg * Di + d] = sd;
 }
 
+// 1'. segment summaries when the states before every chunk are given (the
+// forward's checkpoints): the main sweep starts each chunk from them, so a
+// segment only needs its delta sum and its adjoint summary
+// G = sum_t exp(A S_t) dy_t C_t, S_t the delta sum of the segment's steps up to
+// and including t (the running decay product of the summary above, taken as one
+// exponential of the running sum).  u and B are not read.  Segment 0's summary
+// is never used, so the grid starts at segment 1.
+template <typename T, int NS>
+__global__ __launch_bounds__(kBlock) void scan_gsum(const T* __restrict__ delta, const float* __restrict__ A_log,
+                                                    const T* __restrict__ Cm, const T* __restrict__ z,
+                                                    const T* __restrict__ dout, float* __restrict__ seg_g,
+                                                    float* __restrict__ seg_sd, ScanShape sh) {
+  const int d = blockIdx.x * kBlock + threadIdx.x;
+  const int s = blockIdx.y + 1, b = blockIdx.z;
+  if (d >= sh.Di) return;
+  const int Di = sh.Di;
+  float A2[NS], G[NS];
+  load_A2<NS>(A_log, d, A2);
+#pragma unroll
+  for (int n = 0; n < NS; ++n) G[n] = 0.f;
+  float S = 0.f;
+  const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
+  const size_t bo = (size_t)b * sh.T * Di;
+  const T* __restrict__ db = delta + bo;
+  const T* __restrict__ gb = dout + bo;
+  const T* __restrict__ zb = z + (size_t)b * sh.T * sh.ld_z;
+  const T* __restrict__ Cb = Cm + (size_t)b * sh.T * sh.ld_bc;
+  for (int tc = t0; tc < t1; tc += kChunk) {
+    const int nv = min(kChunk, t1 - tc);
+    float dl[kChunk], dy[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {  // a ragged last chunk reads its last step again, with zero weight
+      const unsigned tj = (unsigned)(tc + min(j, nv - 1));
+      dl[j] = ld(db, tj * Di + d);
+      dy[j] = ld(gb, tj * Di + d);
+      const float zz = ld(zb, tj * sh.ld_z + d);
+      dy[j] *= zz * sigmoid(zz);
+      if (j >= nv) dl[j] = dy[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      float Cv[NS];
+      load_row<NS>(Cb + (size_t)(tc + min(j, nv - 1)) * sh.ld_bc, Cv);
+      S += dl[j];
+#pragma unroll
+      for (int n = 0; n < NS; ++n) G[n] = fmaf(fast_exp2(A2[n] * S), dy[j] * Cv[n], G[n]);
+    }
+  }
+  const size_t sg = (size_t)b * sh.nseg + s;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) seg_g[(sg * NS + n) * Di + d] = G[n];
+  seg_sd[sg * Di + d] = S;
+}
+
 // ---------------------------------------------------------------------------
 // 2. carries across segments, one thread per (b, n, d), in place.  Segment s's
-// decay is exp(A * sum of its delta); the forward carry runs over s ascending,
-// the adjoint carry descending.
-template <int NS, bool BWD>
+// decay is exp(A * sum of its delta); the forward carry (FWD) runs over s
+// ascending, the adjoint carry (BWD) descending.
+template <int NS, bool FWD, bool BWD>
 __global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A_log, float* __restrict__ seg_h,
                                                      float* __restrict__ seg_g, const float* __restrict__ seg_sd,
                                                      ScanShape sh) {
@@ -229,21 +283,23 @@ __global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A
   const size_t hs = (size_t)NS * Di;
   float H = 0.f;
 #pragma unroll 4
-  for (int s = 0; s < sh.nseg; ++s) {
+  for (int s = 0; FWD && s < sh.nseg; ++s) {
     const float dec = fast_exp2(A2 * seg_sd[sd0 + (size_t)s * Di]);
     const float loc = seg_h[h0 + s * hs];
     seg_h[h0 + s * hs] = H;
     H = fmaf(dec, H, loc);
   }
   if (!BWD) return;
+  // the adjoint leaving segment s; segment 0's own summary is not needed
   float G = 0.f;
 #pragma unroll 4
-  for (int s = sh.nseg - 1; s >= 0; --s) {
+  for (int s = sh.nseg - 1; s >= 1; --s) {
     const float dec = fast_exp2(A2 * seg_sd[sd0 + (size_t)s * Di]);
     const float loc = seg_g[h0 + s * hs];
     seg_g[h0 + s * hs] = G;
     G = fmaf(dec, G, loc);
   }
+  seg_g[h0] = G;
 }
 
 // ---------------------------------------------------------------------------
@@ -261,7 +317,10 @@ struct ChunkTile {
 // float asks for two waves per SIMD (B | C staged in LDS take VGPRs the
 // compiler would otherwise spend at the cost of occupancy); bf16 leaves the
 // choice to the compiler.
-template <typename T, int NS, bool SOFTPLUS>
+// GCK: `ckpt` holds the exact state before every chunk (the forward's
+// checkpoints) instead of the local ones of the summary pass; seg_h, ckpt_sd
+// are then unused.
+template <typename T, int NS, bool SOFTPLUS, bool GCK>
 __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
@@ -319,7 +378,11 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     const float bc_next = kStage && c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
     // state before the chunk: local checkpoint + decayed carry-in
     float h[NS];
-    if (c == c_first) {
+    if (GCK) {
+      const size_t cc = (size_t)b * sh.nchunk + c;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h[n] = ckpt[(cc * NS + n) * Di + dc];
+    } else if (c == c_first) {
 #pragma unroll
       for (int n = 0; n < NS; ++n) h[n] = (s == 0) ? 0.f : seg_h[(sg * NS + n) * Di + dc];
     } else {
@@ -564,12 +627,12 @@ struct Plan {
 // Segment length: the segments of all batch elements and channel tiles run as
 // independent blocks of the summary and the main kernel, so a pass takes about
 // (rounds of resident blocks) x (segment length + a fixed set-up cost) in each,
-// the main kernel's steps weighing about three summary steps.  Picks the length,
+// the main kernel's steps weighing about three summary steps (six of the
+// adjoint-only summary used when the chunk states are given).  Picks the length,
 // a multiple of 8 and at least 64 steps (or the whole sequence), that minimises
 // the sum; ties go to the longer segment (fewer carries, less workspace).
-int auto_seg(const ssm_dims& dm, long cap_summary, long cap_main) {
+int auto_seg(const ssm_dims& dm, long cap_summary, long cap_main, long main_weight) {
   constexpr int kSegOverhead = 16;  // steps' worth of checkpoint restore and carry work
-  constexpr long kMainWeight = 3;
   const long rows = (long)((dm.d_inner + kBlock - 1) / kBlock) * dm.batch;
   const int tmax = (dm.seqlen + kChunk - 1) / kChunk * kChunk;
   const int smin = tmax < 64 ? tmax : 64;
@@ -577,7 +640,7 @@ int auto_seg(const ssm_dims& dm, long cap_summary, long cap_main) {
   int best = tmax;
   for (int seg = tmax; seg >= smin && seg > 0; seg -= kChunk) {
     const long blocks = rows * ((dm.seqlen + seg - 1) / seg);
-    const long rounds = (blocks + cap_summary - 1) / cap_summary + kMainWeight * ((blocks + cap_main - 1) / cap_main);
+    const long rounds = (blocks + cap_summary - 1) / cap_summary + main_weight * ((blocks + cap_main - 1) / cap_main);
     const long cost = rounds * (seg + kSegOverhead);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
@@ -603,6 +666,7 @@ long device_cus() {
 // (its float variant holds the next chunk's values in registers)
 long summary_blocks_per_cu(int dtype) { return dtype == SSM_F32 ? 2 : 3; }
 constexpr long kMainBlocksPerCU = 2;
+constexpr long kGsumBlocksPerCU = 7;  // the adjoint-only summary holds seven waves per SIMD
 
 int check_dims(const ssm_dims* dm, int dtype) {
   if (!dm) return fail(SSM_ERR_INVALID_ARG, "dims is null");
@@ -630,7 +694,9 @@ int check_dims(const ssm_dims* dm, int dtype) {
   return SSM_OK;
 }
 
-Plan make_plan(const ssm_dims& dm, int dtype, bool bwd) {
+// given_ckpt: the backward takes the chunk states from the caller, so the local
+// checkpoints and the forward carry need no workspace.
+Plan make_plan(const ssm_dims& dm, int dtype, bool bwd, bool given_ckpt = false) {
   Plan p{};
   ScanShape& sh = p.sh;
   sh.Bt = dm.batch;
@@ -640,18 +706,20 @@ Plan make_plan(const ssm_dims& dm, int dtype, bool bwd) {
   sh.ld_dbc = dm.ld_dbc;
   sh.ld_z = dm.ld_z ? dm.ld_z : dm.d_inner;
   const long cus = dm.seg_len ? 0 : device_cus();
-  sh.seg = dm.seg_len ? dm.seg_len : auto_seg(dm, cus * summary_blocks_per_cu(dtype), cus * kMainBlocksPerCU);
+  sh.seg = dm.seg_len ? dm.seg_len
+                      : given_ckpt ? auto_seg(dm, cus * kGsumBlocksPerCU, cus * kMainBlocksPerCU, 6)
+                                   : auto_seg(dm, cus * summary_blocks_per_cu(dtype), cus * kMainBlocksPerCU, 3);
   if (sh.seg <= 0) sh.seg = kChunk;
   sh.nseg = (sh.T + sh.seg - 1) / sh.seg;
   sh.nchunk = (sh.T + kChunk - 1) / kChunk;
   sh.ntile = (sh.Di + kBlock - 1) / kBlock;
   const size_t N = dm.d_state, Bt = sh.Bt, Di = sh.Di;
   size_t sz[7] = {0, 0, 0, 0, 0, 0, 0};
-  if (bwd) {
+  if (bwd && !given_ckpt) {
     sz[0] = Bt * sh.nchunk * N * Di;
     sz[1] = Bt * sh.nchunk * Di;
   }
-  sz[2] = Bt * sh.nseg * N * Di;
+  sz[2] = given_ckpt ? 0 : Bt * sh.nseg * N * Di;
   sz[3] = bwd ? Bt * sh.nseg * N * Di : 0;
   sz[4] = Bt * sh.nseg * Di;
   if (bwd) {
@@ -684,7 +752,7 @@ template <typename T, int NS>
 int launch_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                const float* D, const void* z, const void* d_out, void* d_u, void* d_delta,
                float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus,
-               const Plan& p, ScanWs w, hipStream_t st, void* const* ev) {
+               const float* h_ckpt, const Plan& p, ScanWs w, hipStream_t st, void* const* ev) {
   auto mark = [&](int k) {
     if (ev && ev[k]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), st);
   };
@@ -696,23 +764,37 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
   const T* tz = static_cast<const T*>(z);
   const T* tdo = static_cast<const T*>(d_out);
   dim3 grid(sh.ntile, sh.nseg, sh.Bt);
+  const int ncarry = (int)(((size_t)sh.Bt * NS * sh.Di + kBlock - 1) / kBlock);
   mark(0);
-  hipLaunchKernelGGL((scan_summary<T, NS, true>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, tz, tdo,
-                     w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
-  mark(1);
-  if (sh.nseg > 1) {
-    const int nb = (int)(((size_t)sh.Bt * NS * sh.Di + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((scan_carry<NS, true>), dim3(nb), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g, w.seg_sd, sh);
+  if (!h_ckpt) {
+    hipLaunchKernelGGL((scan_summary<T, NS, true>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, tz, tdo,
+                       w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
+    mark(1);
+    if (sh.nseg > 1)
+      hipLaunchKernelGGL((scan_carry<NS, true, true>), dim3(ncarry), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g,
+                         w.seg_sd, sh);
+  } else {
+    if (sh.nseg > 1)
+      hipLaunchKernelGGL((scan_gsum<T, NS>), dim3(sh.ntile, sh.nseg - 1, sh.Bt), dim3(kBlock), 0, st, tdl, A_log, tC,
+                         tz, tdo, w.seg_g, w.seg_sd, sh);
+    mark(1);
+    if (sh.nseg > 1)
+      hipLaunchKernelGGL((scan_carry<NS, false, true>), dim3(ncarry), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g,
+                         w.seg_sd, sh);
   }
   mark(2);
-  if (softplus)
-    hipLaunchKernelGGL((scan_bwd_main<T, NS, true>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz,
-                       tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z), w.ckpt,
-                       w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);
-  else
-    hipLaunchKernelGGL((scan_bwd_main<T, NS, false>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz,
-                       tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z), w.ckpt,
-                       w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);
+#define SSM_MAIN(SP, GCK)                                                                                     \
+  hipLaunchKernelGGL((scan_bwd_main<T, NS, SP, GCK>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz, \
+                     tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),                 \
+                     GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh)
+  if (h_ckpt) {
+    if (softplus) SSM_MAIN(true, true);
+    else SSM_MAIN(false, true);
+  } else {
+    if (softplus) SSM_MAIN(true, false);
+    else SSM_MAIN(false, false);
+  }
+#undef SSM_MAIN
   mark(3);
   const size_t nbc = (size_t)sh.Bt * sh.T * 2 * NS;
   const int nblk_bc = (int)((nbc + kBlock - 1) / kBlock);
@@ -737,7 +819,7 @@ int launch_fwd(const void* u, const void* delta, const float* A_log, const void*
     hipLaunchKernelGGL((scan_summary<T, NS, false>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC,
                        (const T*)nullptr, (const T*)nullptr, w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.seg_sd, sh);
     const int nb = (int)(((size_t)sh.Bt * NS * sh.Di + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((scan_carry<NS, false>), dim3(nb), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g, w.seg_sd, sh);
+    hipLaunchKernelGGL((scan_carry<NS, true, false>), dim3(nb), dim3(kBlock), 0, st, A_log, w.seg_h, w.seg_g, w.seg_sd, sh);
   }
   const int nckpt = ckpt_every > 0 ? (sh.T + ckpt_every - 1) / ckpt_every : 0;
   hipLaunchKernelGGL((scan_fwd_main<T, NS>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D,
@@ -757,10 +839,56 @@ int zero_params(float* d_A_log, float* d_D, int n_a, int n_d, hipStream_t st) {
 
 using namespace ssm;
 
+namespace ssm {
+namespace {
+int run_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C, const float* D,
+            const void* z, const void* d_out, const float* h_ckpt, bool ckpt_given, void* d_u, void* d_delta,
+            float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus_epilogue, void* workspace,
+            size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream, void* const* stage_events) {
+  int rc = check_dims(dims, dtype);
+  if (rc != SSM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ssm_dims dm = *dims;
+  const int n_a = dm.d_inner * dm.d_state;
+  if (dm.d_inner > 0 && (!A_log || !D || !d_A_log || !d_D))
+    return fail(SSM_ERR_INVALID_ARG, "A_log, D, d_A_log and d_D are required");
+  if ((size_t)dm.batch * dm.seqlen * dm.d_inner == 0) return zero_params(d_A_log, d_D, n_a, dm.d_inner, st);
+  if (!u || !delta || !B || !C || !z || !d_out || !d_u || !d_delta || !d_B || !d_C || !d_z)
+    return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
+  if (ckpt_given && !h_ckpt) return fail(SSM_ERR_INVALID_ARG, "h_ckpt is null");
+  if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C) && aligned4(d_B) && aligned4(d_C)))
+    return fail(SSM_ERR_UNSUPPORTED, "bf16 B, C, d_B and d_C must be 4-byte aligned");
+  const Plan p = make_plan(dm, dtype, true, ckpt_given);
+  if (!workspace || ws_bytes < p.bytes)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
+  const ScanWs w = bind(p, workspace);
+#define SSM_BWD_CASE(TY, NSV)                                                                                    \
+  return launch_bwd<TY, NSV>(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z, \
+                             softplus_epilogue, h_ckpt, p, w, st, stage_events)
+  if (dtype == SSM_F32) {
+    if (dm.d_state == 16) SSM_BWD_CASE(float, 16);
+    if (dm.d_state == 8) SSM_BWD_CASE(float, 8);
+    SSM_BWD_CASE(float, 4);
+  } else {
+    if (dm.d_state == 16) SSM_BWD_CASE(bf16, 16);
+    if (dm.d_state == 8) SSM_BWD_CASE(bf16, 8);
+    SSM_BWD_CASE(bf16, 4);
+  }
+#undef SSM_BWD_CASE
+}
+}  // namespace
+}  // namespace ssm
+
 extern "C" size_t ssm_scan_bwd_workspace_size(const ssm_dims* dims, int dtype) {
   if (check_dims(dims, dtype) != SSM_OK) return 0;
   if ((size_t)dims->batch * dims->seqlen * dims->d_inner == 0) return 0;
   return make_plan(*dims, dtype, true).bytes;
+}
+
+extern "C" size_t ssm_scan_bwd_ckpt_workspace_size(const ssm_dims* dims, int dtype) {
+  if (check_dims(dims, dtype) != SSM_OK) return 0;
+  if ((size_t)dims->batch * dims->seqlen * dims->d_inner == 0) return 0;
+  return make_plan(*dims, dtype, true, true).bytes;
 }
 
 extern "C" size_t ssm_scan_fwd_workspace_size(const ssm_dims* dims, int dtype) {
@@ -773,8 +901,8 @@ extern "C" int ssm_scan_bwd(const void* u, const void* delta, const float* A_log
                             const float* D, const void* z, const void* d_out, void* d_u, void* d_delta,
                             float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus_epilogue,
                             void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream) {
-  return ssm_scan_bwd_timed(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
-                            softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, nullptr);
+  return run_bwd(u, delta, A_log, B, C, D, z, d_out, nullptr, false, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
+                 softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, nullptr);
 }
 
 extern "C" int ssm_scan_bwd_timed(const void* u, const void* delta, const float* A_log, const void* B,
@@ -782,35 +910,17 @@ extern "C" int ssm_scan_bwd_timed(const void* u, const void* delta, const float*
                                   void* d_delta, float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z,
                                   int softplus_epilogue, void* workspace, size_t ws_bytes, const ssm_dims* dims,
                                   int dtype, void* stream, void* const* stage_events) {
-  int rc = check_dims(dims, dtype);
-  if (rc != SSM_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const ssm_dims dm = *dims;
-  const int n_a = dm.d_inner * dm.d_state;
-  if (dm.d_inner > 0 && (!A_log || !D || !d_A_log || !d_D))
-    return fail(SSM_ERR_INVALID_ARG, "A_log, D, d_A_log and d_D are required");
-  if ((size_t)dm.batch * dm.seqlen * dm.d_inner == 0) return zero_params(d_A_log, d_D, n_a, dm.d_inner, st);
-  if (!u || !delta || !B || !C || !z || !d_out || !d_u || !d_delta || !d_B || !d_C || !d_z)
-    return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
-  if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C) && aligned4(d_B) && aligned4(d_C)))
-    return fail(SSM_ERR_UNSUPPORTED, "bf16 B, C, d_B and d_C must be 4-byte aligned");
-  const Plan p = make_plan(dm, dtype, true);
-  if (!workspace || ws_bytes < p.bytes)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
-  const ScanWs w = bind(p, workspace);
-#define SSM_BWD_CASE(TY, NSV)                                                                                    \
-  return launch_bwd<TY, NSV>(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z, \
-                             softplus_epilogue, p, w, st, stage_events)
-  if (dtype == SSM_F32) {
-    if (dm.d_state == 16) SSM_BWD_CASE(float, 16);
-    if (dm.d_state == 8) SSM_BWD_CASE(float, 8);
-    SSM_BWD_CASE(float, 4);
-  } else {
-    if (dm.d_state == 16) SSM_BWD_CASE(bf16, 16);
-    if (dm.d_state == 8) SSM_BWD_CASE(bf16, 8);
-    SSM_BWD_CASE(bf16, 4);
-  }
-#undef SSM_BWD_CASE
+  return run_bwd(u, delta, A_log, B, C, D, z, d_out, nullptr, false, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
+                 softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, stage_events);
+}
+
+extern "C" int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                                 const float* D, const void* z, const void* d_out, const float* h_ckpt, void* d_u,
+                                 void* d_delta, float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z,
+                                 int softplus_epilogue, void* workspace, size_t ws_bytes, const ssm_dims* dims,
+                                 int dtype, void* stream, void* const* stage_events) {
+  return run_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, true, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
+                 softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, stage_events);
 }
 
 extern "C" int ssm_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,

@@ -69,6 +69,24 @@ def test_bwd_rejects_null_and_workspace():
     assert _bwd(_dims(ld_bc=17), dtype=1) == ssm.SSM_ERR_UNSUPPORTED
 
 
+def _bwd_ckpt(dims, h_ckpt=FAKE, ws_bytes=1 << 40, dtype=0, ws=FAKE):
+    p = [FAKE] * 8 + [h_ckpt] + [FAKE] * 7
+    return L.ssm_scan_bwd_ckpt(*p, 0, ws, ws_bytes, ctypes.byref(dims) if dims is not None else None, dtype, None,
+                               None)
+
+
+def test_bwd_ckpt_validates():
+    d = _dims(seqlen=4096, seg_len=256)
+    full = L.ssm_scan_bwd_workspace_size(ctypes.byref(d), 0)
+    given = L.ssm_scan_bwd_ckpt_workspace_size(ctypes.byref(d), 0)
+    assert 0 < given < full   # no local checkpoints or forward carries
+    assert L.ssm_scan_bwd_ckpt_workspace_size(ctypes.byref(_dims(d_state=5)), 0) == 0
+    assert _bwd_ckpt(_dims(), h_ckpt=None) == ssm.SSM_ERR_INVALID_ARG
+    assert _bwd_ckpt(None) == ssm.SSM_ERR_INVALID_ARG
+    assert _bwd_ckpt(_dims(seg_len=12)) == ssm.SSM_ERR_INVALID_ARG
+    assert _bwd_ckpt(_dims(), ws_bytes=16) == ssm.SSM_ERR_WORKSPACE
+
+
 def test_other_entry_points_validate():
     assert L.gating_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 0, None) == ssm.SSM_ERR_INVALID_ARG
     assert L.gating_bwd(None, FAKE, FAKE, FAKE, FAKE, 10, 0, None) == ssm.SSM_ERR_INVALID_ARG
