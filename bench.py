@@ -116,38 +116,52 @@ def recorded_traffic(workload: str, kernel: str):
     return None
 
 
-def cpu_baseline_scan(cfg, batches: int):
-    """The fp64 oracle, single-threaded, on the first `batches` sequences of the workload."""
+CPU_SAMPLE_SECONDS = 10.0
+
+
+def cpu_baseline_scan(cfg):
+    """The fp64 oracle, single-threaded, one whole sequence of the workload at a time until
+    CPU_SAMPLE_SECONDS have passed (or the batch is done)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import ssm as orc
     from synth import scan_inputs
-    p = scan_inputs(batches, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
+    p = scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
+    dt, done = 0.0, 0
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        orc.ssm_scan_bwd(p["u"], p["delta"], p["A_log"], p["B"], p["C"], p["D"], p["z"], p["d_out"])
-        dt = time.perf_counter() - t0
-    se = batches * cfg.seqlen * cfg.d_inner * cfg.d_state
+        while done < cfg.batch and dt < CPU_SAMPLE_SECONDS:
+            q = {k: (v[done:done + 1] if v.ndim == 3 else v) for k, v in p.items()}
+            t0 = time.perf_counter()
+            orc.ssm_scan_bwd(q["u"], q["delta"], q["A_log"], q["B"], q["C"], q["D"], q["z"], q["d_out"])
+            dt += time.perf_counter() - t0
+            done += 1
+    se = done * cfg.seqlen * cfg.d_inner * cfg.d_state
     return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{batches} of {cfg.batch} sequences of the same workload ({se} state elements, "
+            "sample": f"{done} of {cfg.batch} sequences of the same workload, one at a time ({se} state elements, "
                       f"{dt:.1f} s, fp64 NumPy, 1 thread)"}
 
 
-def cpu_baseline_layer(cfg, steps: int):
-    """The fp64 oracle's whole-layer forward + backward, single-threaded, on one sequence of `steps` steps."""
+def cpu_baseline_layer(cfg):
+    """The fp64 oracle's whole-layer forward + backward, single-threaded, one whole sequence of the
+    workload at a time until CPU_SAMPLE_SECONDS have passed (or the batch is done)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import layer as orc
     from synth import layer_inputs
-    p = layer_inputs(1, steps, cfg.d_model, cfg.d_inner, cfg.d_state, cfg.dt_rank, cfg.d_conv, cfg.dtype, cfg.seed)
+    p = layer_inputs(cfg.batch, cfg.seqlen, cfg.d_model, cfg.d_inner, cfg.d_state, cfg.dt_rank, cfg.d_conv,
+                     cfg.dtype, cfg.seed)
+    dt, done = 0.0, 0
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        orc.layer_bwd(p, p["d_out"], cfg.d_state, cfg.dt_rank)
-        dt = time.perf_counter() - t0
-    se = steps * cfg.d_inner * cfg.d_state
+        while done < cfg.batch and dt < CPU_SAMPLE_SECONDS:
+            q = {k: (v[done:done + 1] if k in ("x", "d_out") else v) for k, v in p.items()}
+            t0 = time.perf_counter()
+            orc.layer_bwd(q, q["d_out"], cfg.d_state, cfg.dt_rank)
+            dt += time.perf_counter() - t0
+            done += 1
+    se = done * cfg.seqlen * cfg.d_inner * cfg.d_state
     return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 sequence of {steps} steps at the workload's widths ({se} state elements, {dt:.1f} s, "
-                      "fp64 NumPy forward + backward, 1 thread)"}
+            "sample": f"{done} of {cfg.batch} sequences of the same workload, one at a time ({se} state elements, "
+                      f"{dt:.1f} s, fp64 NumPy forward + backward, 1 thread)"}
 
 
 def timed(step, n_events: int, steps: int, warmup: int):
@@ -239,7 +253,7 @@ def run_scan(args, cfg):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_scan(cfg, batches=2 if cfg.seqlen * cfg.d_inner <= 2048 * 2048 else 1)
+        line["cpu_baseline"] = cpu_baseline_scan(cfg)
     return line
 
 
@@ -293,7 +307,7 @@ def run_layer(args, cfg):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_layer(cfg, steps=512)
+        line["cpu_baseline"] = cpu_baseline_layer(cfg)
     return line
 
 
