@@ -49,6 +49,20 @@ typedef enum ssm_status {
 
 typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
+/* Flags of the backward entry points (bitwise or; other bits are rejected).
+ * SSM_BWD_ACCUMULATE: parameter gradients (d_A_log, d_D; dW and db of
+ * linear_bwd; d_w and d_bias of conv1d_bwd; dw of rmsnorm_bwd) are added into
+ * the caller's buffers instead of overwriting them, as mamba-rs's gradient
+ * accumulators take `+=` (Phase B3's d_layer.a_log and d_param), so that
+ * micro-batches sum into one set of buffers.  Per-element gradients (d_u,
+ * d_delta, d_z, d_B, d_C, dX, d_x) are written either way.  Calls on an empty
+ * batch then leave the buffers as they are. */
+typedef enum ssm_bwd_flags {
+  SSM_BWD_SOFTPLUS = 1,      /* ssm_scan_bwd*: the softplus epilogue (see ssm_scan_bwd) */
+  SSM_BWD_ACCUMULATE = 2,
+  SSM_BWD_ACCUMULATE_DX = 4  /* linear_bwd: dX is added into dX's contents */
+} ssm_bwd_flags;
+
 /* Shape of one selective-scan call.
  *   u, delta, z, d_out, d_u, d_delta, d_z : [batch, seqlen, d_inner]
  *   B, C                                   : [batch, seqlen, *] rows of stride ld_bc,
@@ -89,17 +103,18 @@ const char* ssm_last_error(void);
  * Given d_out = dL/d out it writes dL/du, dL/d delta, dL/d A_log, dL/dB, dL/dC,
  * dL/dD and dL/dz.  The forward states are recomputed in chunks; no per-step
  * state is read from or written to memory by the caller.
- * softplus_epilogue != 0: delta is taken to be softplus(raw) (the layer's
+ * flags & SSM_BWD_SOFTPLUS: delta is taken to be softplus(raw) (the layer's
  * dt_proj output) and d_delta receives dL/d raw instead, using
  * sigmoid(raw) = 1 - exp(-delta) and passing the gradient through where
  * delta > 20 (the page's "Softplus backward" step, threshold 20).
+ * flags & SSM_BWD_ACCUMULATE: d_A_log and d_D are added into.
  * All output pointers are required.  Workspace: ssm_scan_bwd_workspace_size().
  * ------------------------------------------------------------------------- */
 size_t ssm_scan_bwd_workspace_size(const ssm_dims* dims, int dtype);
 int ssm_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B,
                  const void* C, const float* D, const void* z, const void* d_out,
                  void* d_u, void* d_delta, float* d_A_log, void* d_B, void* d_C,
-                 float* d_D, void* d_z, int softplus_epilogue,
+                 float* d_D, void* d_z, int flags,
                  void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype,
                  void* stream);
 
@@ -112,7 +127,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A_log, const voi
 int ssm_scan_bwd_timed(const void* u, const void* delta, const float* A_log, const void* B,
                        const void* C, const float* D, const void* z, const void* d_out,
                        void* d_u, void* d_delta, float* d_A_log, void* d_B, void* d_C,
-                       float* d_D, void* d_z, int softplus_epilogue,
+                       float* d_D, void* d_z, int flags,
                        void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype,
                        void* stream, void* const* stage_events);
 
@@ -135,7 +150,7 @@ size_t ssm_scan_bwd_ckpt_workspace_size(const ssm_dims* dims, int dtype);
 int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A_log, const void* B,
                       const void* C, const float* D, const void* z, const void* d_out,
                       const float* h_ckpt, void* d_u, void* d_delta, float* d_A_log, void* d_B,
-                      void* d_C, float* d_D, void* d_z, int softplus_epilogue,
+                      void* d_C, float* d_D, void* d_z, int flags,
                       void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype,
                       void* stream, void* const* stage_events);
 
@@ -172,13 +187,14 @@ int gating_bwd(const void* d_out, const void* y, const void* z, void* d_y, void*
  * d_bias[d] = sum g.  x, d_u, d_x rows have strides ld_x, ld_du, ld_dx (>= d_inner)
  * so that x can be the first half of the in_proj output row and d_x the first
  * half of its gradient.  w [d_inner, d_conv] and bias are float; d_conv <= 8.
+ * flags: 0 or SSM_BWD_ACCUMULATE (d_w and d_bias added into).
  * Workspace: conv1d_bwd_workspace_size().
  * ------------------------------------------------------------------------- */
 size_t conv1d_bwd_workspace_size(int batch, int seqlen, int d_inner, int d_conv);
 int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u,
                void* d_x, float* d_w, float* d_bias, int batch, int seqlen, int d_inner,
-               int d_conv, int ld_x, int ld_du, int ld_dx, void* workspace, size_t ws_bytes,
-               int dtype, void* stream);
+               int d_conv, int ld_x, int ld_du, int ld_dx, int flags, void* workspace,
+               size_t ws_bytes, int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * rmsnorm_bwd — rlx-cpu training_bwd.rs rms_norm_backward_row over `rows`
@@ -188,20 +204,22 @@ int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u
  *     dx = inv_r w dy - inv_r^3 x mean(dy w x)  (+ d_residual if not null)
  *     dw = sum over rows of dy x inv_r
  * x, dy, d_residual, dx: [rows, dim] in dtype; w, dw: [dim] float.
+ * flags: 0 or SSM_BWD_ACCUMULATE (dw added into).
  * Workspace: rmsnorm_bwd_workspace_size().
  * ------------------------------------------------------------------------- */
 size_t rmsnorm_bwd_workspace_size(int64_t rows, int dim);
 int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_residual,
-                void* dx, float* dw, int64_t rows, int dim, float eps, void* workspace,
-                size_t ws_bytes, int dtype, void* stream);
+                void* dx, float* dw, int64_t rows, int dim, float eps, int flags,
+                void* workspace, size_t ws_bytes, int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * linear_bwd — the weight-layer backward that mamba-rs cpu/backward.rs runs
  * (sgemm_backward) in Phases B1 (out_proj), B4 (dt_proj, with bias), B5
  * (x_proj) and B7 (in_proj), for Y = X W^T (+ b) with W [N, K] (out, in):
- *     dX = dY W            [M, K]   (bf16; added to dX's contents if accumulate_dx)
- *     dW = dY^T X          [N, K]   (float, overwritten)
- *     db = sum over rows of dY [N] (float, overwritten)
+ *     dX = dY W            [M, K]   (bf16; added to dX's contents with SSM_BWD_ACCUMULATE_DX)
+ *     dW = dY^T X          [N, K]   (float; added into with SSM_BWD_ACCUMULATE)
+ *     db = sum over rows of dY [N] (float; added into with SSM_BWD_ACCUMULATE)
+ * flags: SSM_BWD_ACCUMULATE_DX | SSM_BWD_ACCUMULATE or 0.
  * X [M, K] rows of stride ldx, dY [M, N] rows of stride lddy, dX rows of
  * stride lddx, W contiguous; all bf16 (dtype must be SSM_BF16), products on the
  * matrix cores with float accumulation.  dX, dW, db are each nullable (skipped);
@@ -211,7 +229,7 @@ int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_res
  * ------------------------------------------------------------------------- */
 size_t linear_bwd_workspace_size(int64_t M, int K, int N);
 int linear_bwd(const void* X, int64_t ldx, const void* W, const void* dY, int64_t lddy,
-               void* dX, int64_t lddx, int accumulate_dx, float* dW, float* db,
+               void* dX, int64_t lddx, int flags, float* dW, float* db,
                int64_t M, int K, int N, void* workspace, size_t ws_bytes, int dtype,
                void* stream);
 
@@ -285,6 +303,8 @@ typedef struct ssm_layer_grads {
   float* d_A_log;
   float* d_D;
   float* d_W_out;
+  int32_t accumulate; /* nonzero: every parameter gradient above is added into
+                         (SSM_BWD_ACCUMULATE); d_x is written either way */
 } ssm_layer_grads;
 
 /* mamba_layer_fwd — out [batch, seqlen, d_model] and the saved activations
@@ -296,7 +316,8 @@ int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* out, const 
 
 /* mamba_layer_bwd — Phases B1-B8: from x, the saved activations and
  * d_out = dL/d out, writes d_x = dL/dx (bf16, including the residual path) and
- * every parameter gradient (float, overwritten).  Recomputes RMSNorm, the conv
+ * every parameter gradient (float; overwritten, or added into when
+ * grads->accumulate is set, to sum micro-batches).  Recomputes RMSNorm, the conv
  * + SiLU output, the gate and the scan states on the way.  Workspace:
  * mamba_layer_bwd_workspace_size().
  * mamba_layer_bwd_timed: same, recording caller-created hipEvent_t handles

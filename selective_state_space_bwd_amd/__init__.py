@@ -22,6 +22,7 @@ _lib = None
 
 SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH = range(5)
 SSM_F32, SSM_BF16 = 0, 1
+SSM_BWD_SOFTPLUS, SSM_BWD_ACCUMULATE, SSM_BWD_ACCUMULATE_DX = 1, 2, 4
 
 
 class ssm_dims(ctypes.Structure):
@@ -49,7 +50,7 @@ class ssm_layer_saved(ctypes.Structure):
 
 
 class ssm_layer_grads(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_GRADS]
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_GRADS] + [("accumulate", ctypes.c_int32)]
 
 
 _vp, _fp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -70,9 +71,9 @@ _SIGS = {
     "ssm_scan_fwd": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _i, _vp, _sz, _dims_p, _i, _vp]),
     "gating_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _vp]),
     "conv1d_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
-    "conv1d_bwd": (_i, [_vp, _fp, _fp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
+    "conv1d_bwd": (_i, [_vp, _fp, _fp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
     "rmsnorm_bwd_workspace_size": (_sz, [_i64, _i]),
-    "rmsnorm_bwd": (_i, [_vp, _fp, _vp, _vp, _vp, _fp, _i64, _i, ctypes.c_float, _vp, _sz, _i, _vp]),
+    "rmsnorm_bwd": (_i, [_vp, _fp, _vp, _vp, _vp, _fp, _i64, _i, ctypes.c_float, _i, _vp, _sz, _i, _vp]),
     "linear_bwd_workspace_size": (_sz, [_i64, _i, _i]),
     "linear_bwd": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i, _fp, _fp, _i64, _i, _i, _vp, _sz, _i, _vp]),
     "linear_fwd_workspace_size": (_sz, [_i64, _i, _i]),
@@ -182,27 +183,33 @@ def ssm_scan_bwd_ckpt_workspace_size(dims: ssm_dims, dtype: torch.dtype) -> int:
                                                       SSM_F32 if dtype == torch.float32 else SSM_BF16))
 
 
-def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool = False, seg_len: int = 0,
-                 out: dict | None = None, workspace: torch.Tensor | None = None, stage_events=None) -> dict:
+def ssm_scan_bwd(u, delta, A_log, B, C, D, z, d_out, *, softplus_epilogue: bool = False, accumulate: bool = False,
+                 seg_len: int = 0, out: dict | None = None, workspace: torch.Tensor | None = None,
+                 stage_events=None) -> dict:
     """Backward of out = y * SiLU(z) through the selective scan; returns the seven gradients.
 
     ``out`` may supply any of the output tensors (d_B / d_C may be strided views into a
-    wider row, as the layer's x_proj gradient).  See ``ssm_scan_bwd`` in include/ssmbwd.h.
+    wider row, as the layer's x_proj gradient).  ``accumulate`` adds d_A_log and d_D into
+    ``out["d_A_log"]`` / ``out["d_D"]`` (SSM_BWD_ACCUMULATE).  See ``ssm_scan_bwd`` in include/ssmbwd.h.
     """
-    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, None, softplus_epilogue, seg_len, out, workspace,
-                     stage_events)
+    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, None, _bwd_flags(softplus_epilogue, accumulate), seg_len,
+                     out, workspace, stage_events)
 
 
 def ssm_scan_bwd_ckpt(u, delta, A_log, B, C, D, z, d_out, h_ckpt, *, softplus_epilogue: bool = False,
-                      seg_len: int = 0, out: dict | None = None, workspace: torch.Tensor | None = None,
-                      stage_events=None) -> dict:
+                      accumulate: bool = False, seg_len: int = 0, out: dict | None = None,
+                      workspace: torch.Tensor | None = None, stage_events=None) -> dict:
     """ssm_scan_bwd taking the forward's state before every 8-step chunk, h_ckpt
     [B, ceil(T / 8), N, Di] float32 (``ssm_scan_fwd(..., ckpt_every=8)["h_ckpt"]``)."""
-    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, softplus_epilogue, seg_len, out, workspace,
-                     stage_events)
+    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, _bwd_flags(softplus_epilogue, accumulate),
+                     seg_len, out, workspace, stage_events)
 
 
-def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, softplus_epilogue, seg_len, out, workspace,
+def _bwd_flags(softplus_epilogue: bool = False, accumulate: bool = False) -> int:
+    return (SSM_BWD_SOFTPLUS if softplus_epilogue else 0) | (SSM_BWD_ACCUMULATE if accumulate else 0)
+
+
+def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, flags, seg_len, out, workspace,
               stage_events) -> dict:
     dt = _dtype_code(u)
     batch, seqlen, d_inner = u.shape
@@ -243,7 +250,7 @@ def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, softplus_epilogue, seg
         rc = lib().ssm_scan_bwd_ckpt(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                      _ptr(d_out), _ptr(h_ckpt), _ptr(o["d_u"]), _ptr(o["d_delta"]),
                                      _ptr(o["d_A_log"]), _ptr(o["d_B"]), _ptr(o["d_C"]), _ptr(o["d_D"]),
-                                     _ptr(o["d_z"]), int(bool(softplus_epilogue)), _ptr(ws), wsb,
+                                     _ptr(o["d_z"]), int(flags), _ptr(ws), wsb,
                                      ctypes.byref(dims), dt, _stream(u), ev)
         _check("ssm_scan_bwd_ckpt", rc)
         return o
@@ -251,7 +258,7 @@ def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, softplus_epilogue, seg
     ws, wsb = _workspace(nbytes, dev, workspace)
     args = (_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(d_out),
             _ptr(o["d_u"]), _ptr(o["d_delta"]), _ptr(o["d_A_log"]), _ptr(o["d_B"]),
-            _ptr(o["d_C"]), _ptr(o["d_D"]), _ptr(o["d_z"]), int(bool(softplus_epilogue)),
+            _ptr(o["d_C"]), _ptr(o["d_D"]), _ptr(o["d_z"]), int(flags),
             _ptr(ws), wsb, ctypes.byref(dims), dt, _stream(u))
     rc = lib().ssm_scan_bwd(*args) if ev is None else lib().ssm_scan_bwd_timed(*args, ev)
     _check("ssm_scan_bwd", rc)
@@ -302,8 +309,9 @@ def gating_bwd(d_out, y, z):
     return d_y, d_z
 
 
-def conv1d_bwd(x, w, bias, d_u, *, d_x=None, workspace=None):
-    """Causal depthwise conv + SiLU backward; x and d_u are [B, T, Di] (last-dim contiguous rows)."""
+def conv1d_bwd(x, w, bias, d_u, *, d_x=None, d_w=None, d_b=None, accumulate: bool = False, workspace=None):
+    """Causal depthwise conv + SiLU backward; x and d_u are [B, T, Di] (last-dim contiguous rows).
+    ``accumulate`` adds the weight and bias gradients into the given ``d_w`` / ``d_b``."""
     dt = _dtype_code(x)
     batch, seqlen, d_inner = x.shape
     d_conv = w.shape[1]
@@ -315,18 +323,23 @@ def conv1d_bwd(x, w, bias, d_u, *, d_x=None, workspace=None):
     if d_x is None:
         d_x = torch.empty((batch, seqlen, d_inner), dtype=x.dtype, device=x.device)
     ldo = _row_stride(d_x, batch, seqlen, d_inner, "d_x")
-    d_w = torch.empty_like(w)
-    d_b = torch.empty((d_inner,), dtype=torch.float32, device=x.device)
+    _need(not accumulate or (d_w is not None and d_b is not None), "accumulate needs d_w and d_b")
+    d_w = torch.empty_like(w) if d_w is None else d_w
+    d_b = torch.empty((d_inner,), dtype=torch.float32, device=x.device) if d_b is None else d_b
+    _need(d_w.shape == w.shape and d_w.dtype == torch.float32 and d_w.is_contiguous(), "d_w is [Di, K] float32")
+    _need(d_b.shape == (d_inner,) and d_b.dtype == torch.float32, "d_b is [Di] float32")
     nbytes = int(lib().conv1d_bwd_workspace_size(batch, seqlen, d_inner, d_conv))
     ws, wsb = _workspace(nbytes, x.device, workspace)
     _check("conv1d_bwd", lib().conv1d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(d_u), _ptr(d_x), _ptr(d_w), _ptr(d_b),
-                                         batch, seqlen, d_inner, d_conv, ldx, ldu, ldo, _ptr(ws), wsb, dt,
-                                         _stream(x)))
+                                         batch, seqlen, d_inner, d_conv, ldx, ldu, ldo,
+                                         SSM_BWD_ACCUMULATE if accumulate else 0, _ptr(ws), wsb, dt, _stream(x)))
     return d_x, d_w, d_b
 
 
-def rmsnorm_bwd(x, w, dy, d_residual=None, eps: float = 1e-5, *, workspace=None):
-    """RMSNorm (weight only) backward over the last dim, plus an optional residual gradient."""
+def rmsnorm_bwd(x, w, dy, d_residual=None, eps: float = 1e-5, *, dw=None, accumulate: bool = False,
+                workspace=None):
+    """RMSNorm (weight only) backward over the last dim, plus an optional residual gradient.
+    ``accumulate`` adds the weight gradient into the given ``dw``."""
     dt = _dtype_code(x)
     dim = x.shape[-1]
     rows = x.numel() // dim if dim else 0
@@ -335,11 +348,14 @@ def rmsnorm_bwd(x, w, dy, d_residual=None, eps: float = 1e-5, *, workspace=None)
     if d_residual is not None:
         _need(d_residual.shape == x.shape and d_residual.dtype == x.dtype and d_residual.is_contiguous(), "residual")
     dx = torch.empty_like(x)
-    dw = torch.empty_like(w)
+    _need(not accumulate or dw is not None, "accumulate needs dw")
+    dw = torch.empty_like(w) if dw is None else dw
+    _need(dw.shape == w.shape and dw.dtype == torch.float32, "dw is [dim] float32")
     nbytes = int(lib().rmsnorm_bwd_workspace_size(rows, dim))
     ws, wsb = _workspace(nbytes, x.device, workspace)
     _check("rmsnorm_bwd", lib().rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(d_residual), _ptr(dx), _ptr(dw), rows,
-                                           dim, ctypes.c_float(eps), _ptr(ws), wsb, dt, _stream(x)))
+                                           dim, ctypes.c_float(eps), SSM_BWD_ACCUMULATE if accumulate else 0,
+                                           _ptr(ws), wsb, dt, _stream(x)))
     return dx, dw
 
 
@@ -361,12 +377,12 @@ def _matrix(x: torch.Tensor, name: str):
 
 
 def linear_bwd(X, W, dY, *, need_dx: bool = True, need_dw: bool = True, need_db: bool = False, dX=None,
-               accumulate_dx: bool = False, workspace=None):
+               accumulate_dx: bool = False, dW=None, db=None, accumulate: bool = False, workspace=None):
     """Backward of Y = X W^T (+ b): returns (dX bf16, dW float32, db float32), None where not asked.
 
     X [..., K] and dY [..., N] may be views with strided rows (e.g. column slices of a wider
     activation); W is [N, K] contiguous bf16.  ``dX`` may be given (and is accumulated into
-    when ``accumulate_dx``).
+    when ``accumulate_dx``); so may ``dW`` and ``db`` (accumulated into when ``accumulate``).
     """
     N, K = W.shape
     _need(W.dtype == torch.bfloat16 and W.is_contiguous(), "W must be contiguous bf16 [N, K]")
@@ -386,12 +402,23 @@ def linear_bwd(X, W, dY, *, need_dx: bool = True, need_dw: bool = True, need_db:
         _need(mx == M and k2 == K, "dX must be [M, K]")
     else:
         dX = None
-    dW = torch.empty((N, K), dtype=torch.float32, device=dev) if need_dw else None
-    db = torch.empty((N,), dtype=torch.float32, device=dev) if need_db else None
+    _need(not accumulate or ((dW is not None or not need_dw) and (db is not None or not need_db)),
+          "accumulate needs the dW / db buffers")
+    if need_dw:
+        dW = torch.empty((N, K), dtype=torch.float32, device=dev) if dW is None else dW
+        _need(dW.shape == (N, K) and dW.dtype == torch.float32 and dW.is_contiguous(), "dW must be float32 [N, K]")
+    else:
+        dW = None
+    if need_db:
+        db = torch.empty((N,), dtype=torch.float32, device=dev) if db is None else db
+        _need(db.shape == (N,) and db.dtype == torch.float32 and db.is_contiguous(), "db must be float32 [N]")
+    else:
+        db = None
+    flags = (SSM_BWD_ACCUMULATE_DX if accumulate_dx else 0) | (SSM_BWD_ACCUMULATE if accumulate else 0)
     nbytes = int(lib().linear_bwd_workspace_size(M, K, N))
     ws, wsb = _workspace(nbytes, dev, workspace)
     _check("linear_bwd", lib().linear_bwd(_ptr(X) if need_dw else None, ldx, _ptr(W), _ptr(dY), lddy, _ptr(dX),
-                                         lddx, int(bool(accumulate_dx)), _ptr(dW), _ptr(db), M, K, N, _ptr(ws), wsb,
+                                         lddx, flags, _ptr(dW), _ptr(db), M, K, N, _ptr(ws), wsb,
                                          SSM_BF16, _stream(dY)))
     return dX, dW, db
 
@@ -464,8 +491,9 @@ def mamba_layer_bwd_workspace_size(x, weights: dict, **kw) -> int:
 
 
 def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, seg_len: int = 0, workspace=None,
-                    out: dict | None = None, stage_events=None) -> dict:
-    """Layer backward (Phases B1-B8): returns d_x (bf16) and every parameter gradient (float32)."""
+                    out: dict | None = None, accumulate: bool = False, stage_events=None) -> dict:
+    """Layer backward (Phases B1-B8): returns d_x (bf16) and every parameter gradient (float32).
+    ``accumulate`` adds the parameter gradients into the buffers given in ``out``."""
     _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.is_contiguous(), "x must be contiguous bf16 [B, T, d_model]")
     _need(d_out.shape == x.shape and d_out.dtype == x.dtype and d_out.is_contiguous(), "d_out must match x")
     dims = layer_dims(x, weights, eps=eps, seg_len=seg_len)
@@ -477,13 +505,14 @@ def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, 
         _need(tuple(t.shape) == shp and t.dtype == torch.bfloat16 and t.is_contiguous(), f"saved {k} must be {shp}")
     sv = ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED])
     o = dict(out or {})
+    _need(not accumulate or all(k in o for k in LAYER_GRADS), "accumulate needs every gradient buffer in out")
     o.setdefault("d_x", torch.empty_like(x))
     for k in LAYER_WEIGHTS:
         ref = weights.get(k)
         if ref is None:
             ref = weights["D"]
         o.setdefault("d_" + k, torch.empty(ref.shape, dtype=torch.float32, device=x.device))
-    g = ssm_layer_grads(*[ctypes.c_void_p(o[k].data_ptr()) for k in LAYER_GRADS])
+    g = ssm_layer_grads(*[ctypes.c_void_p(o[k].data_ptr()) for k in LAYER_GRADS], int(bool(accumulate)))
     nbytes = int(lib().mamba_layer_bwd_workspace_size(ctypes.byref(dims)))
     _need(nbytes > 0, "unsupported layer shape: " + (lib().ssm_last_error() or b"").decode())
     ws, wsb = _workspace(nbytes, x.device, workspace)

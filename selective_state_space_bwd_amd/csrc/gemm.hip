@@ -337,13 +337,13 @@ __global__ __launch_bounds__(256) void column_sum_part(const T* __restrict__ X, 
 }
 
 __global__ __launch_bounds__(256) void column_sum_final(const float* __restrict__ part, int chunks, int N,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, int accumulate) {
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= N) return;
   float acc = 0.f;
 #pragma unroll 8
   for (int c = 0; c < chunks; ++c) acc += part[(size_t)c * N + col];
-  out[col] = acc;
+  out[col] = accumulate ? out[col] + acc : acc;
 }
 
 namespace {
@@ -432,8 +432,8 @@ size_t column_sum_workspace_bytes(int M, int N) {
 }
 
 // workspace: column_sum_workspace_bytes(M, N)
-int column_sum_launch(const void* X, long long ldx, int M, int N, int dtype, float* out, void* workspace,
-                      hipStream_t st) {
+int column_sum_launch(const void* X, long long ldx, int M, int N, int dtype, float* out, int accumulate,
+                      void* workspace, hipStream_t st) {
   const int chunks = (M + kColRows - 1) / kColRows;
   float* part = static_cast<float*>(workspace);
   const dim3 grid((N + 63) / 64, chunks);
@@ -441,7 +441,7 @@ int column_sum_launch(const void* X, long long ldx, int M, int N, int dtype, flo
     hipLaunchKernelGGL(column_sum_part<float>, grid, dim3(256), 0, st, static_cast<const float*>(X), ldx, M, N, part);
   else
     hipLaunchKernelGGL(column_sum_part<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(X), ldx, M, N, part);
-  hipLaunchKernelGGL(column_sum_final, dim3((N + 255) / 256), dim3(256), 0, st, part, chunks, N, out);
+  hipLaunchKernelGGL(column_sum_final, dim3((N + 255) / 256), dim3(256), 0, st, part, chunks, N, out, accumulate);
   return SSM_OK;
 }
 
@@ -459,14 +459,17 @@ extern "C" size_t linear_bwd_workspace_size(int64_t M, int K, int N) {
 }
 
 extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void* dY, int64_t lddy, void* dX,
-                          int64_t lddx, int accumulate_dx, float* dW, float* db, int64_t M, int K, int N,
+                          int64_t lddx, int flags, float* dW, float* db, int64_t M, int K, int N,
                           void* workspace, size_t ws_bytes, int dtype, void* stream) {
   if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "linear_bwd runs on bf16 operands");
+  if (flags & ~(SSM_BWD_ACCUMULATE | SSM_BWD_ACCUMULATE_DX)) return fail(SSM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (M < 0 || K <= 0 || N <= 0 || M >= (1LL << 31))
     return fail(SSM_ERR_INVALID_ARG, "bad size (M %lld K %d N %d)", (long long)M, K, N);
   if ((dW && ldx < K) || lddy < N || (dX && lddx < K)) return fail(SSM_ERR_INVALID_ARG, "row strides below the row length");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int acc_w = (flags & SSM_BWD_ACCUMULATE) ? 1 : 0, acc_x = (flags & SSM_BWD_ACCUMULATE_DX) ? 1 : 0;
   if (M == 0) {  // dX is empty; dW and db are sums over no rows
+    if (acc_w || (!dW && !db)) return SSM_OK;
     if (dW) launch_fill_zero(dW, (int64_t)N * K, st);
     if (db) launch_fill_zero(db, N, st);
     return check_launch("linear_bwd (no rows)");
@@ -480,9 +483,9 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
   if (db && (!workspace || ws_bytes < column_sum_workspace_bytes(m, N)))
     return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace too small for the bias sums");
-  if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, accumulate_dx, workspace, st);
-  if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, 0, workspace, st);
-  if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, workspace, st);
+  if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, acc_x, workspace, st);
+  if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, acc_w, workspace, st);
+  if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, acc_w, workspace, st);
   return check_launch("linear_bwd");
 }
 

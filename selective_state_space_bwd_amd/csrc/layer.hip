@@ -242,36 +242,38 @@ extern "C" int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, 
   launch_gate_fwd(static_cast<const bf16*>(saved->y), xz + di, 2 * di, b.gated, M, di, st);
   mark(ev, 1, st);
   // B1: out = gated W_out^T (+ x)
-  TRY(linear_bwd(b.gated, di, w->W_out, d_out, dm, b.d_gated, di, 0, g->d_W_out, nullptr, M, di, dm, sc, scb,
+  const int acc = g->accumulate ? SSM_BWD_ACCUMULATE : 0;
+  TRY(linear_bwd(b.gated, di, w->W_out, d_out, dm, b.d_gated, di, acc, g->d_W_out, nullptr, M, di, dm, sc, scb,
                  SSM_BF16, stream));
   mark(ev, 2, st);
   launch_conv_silu_fwd(xz, 2 * di, w->conv_w, w->conv_b, b.u, di, d.batch, d.seqlen, di, d.d_conv, st);
   mark(ev, 3, st);
   // B2 + B3 (+ softplus backward): d_z lands in the second half of d_xz, d_B | d_C in d_xdbl
   TRY(ssm_scan_bwd(b.u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated, b.d_u, b.d_raw,
-                   g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D, b.d_xz + di, 1, sc, scb, &sd, SSM_BF16,
-                   stream));
+                   g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D, b.d_xz + di, SSM_BWD_SOFTPLUS | acc, sc, scb,
+                   &sd, SSM_BF16, stream));
   mark(ev, 4, st);
   // B4: raw = dt_in W_dt^T + b_dt, dt_in = xdbl[:, :R]; d_dt_in fills d_xdbl[:, :R]
-  TRY(linear_bwd(xdbl, R2, w->W_dt, b.d_raw, di, b.d_xdbl, R2, 0, g->d_W_dt, g->d_b_dt, M, R, di, sc, scb,
+  TRY(linear_bwd(xdbl, R2, w->W_dt, b.d_raw, di, b.d_xdbl, R2, acc, g->d_W_dt, g->d_b_dt, M, R, di, sc, scb,
                  SSM_BF16, stream));
   mark(ev, 5, st);
   // B5: xdbl = u W_x^T; d_u collects the scan's and this product's parts
-  TRY(linear_bwd(b.u, di, w->W_x, b.d_xdbl, R2, b.d_u, di, 1, g->d_W_x, nullptr, M, di, R2, sc, scb, SSM_BF16,
+  TRY(linear_bwd(b.u, di, w->W_x, b.d_xdbl, R2, b.d_u, di, SSM_BWD_ACCUMULATE_DX | acc, g->d_W_x, nullptr, M, di,
+                 R2, sc, scb, SSM_BF16,
                  stream));
   mark(ev, 6, st);
   // B6: SiLU + conv backward; d_x_b fills the first half of d_xz
   TRY(conv1d_bwd(xz, w->conv_w, w->conv_b, b.d_u, b.d_xz, g->d_conv_w, g->d_conv_b, d.batch, d.seqlen, di,
-                 d.d_conv, 2 * di, di, 2 * di, sc, scb, SSM_BF16, stream));
+                 d.d_conv, 2 * di, di, 2 * di, acc, sc, scb, SSM_BF16, stream));
   mark(ev, 7, st);
   launch_rmsnorm_fwd(static_cast<const bf16*>(x), w->norm_w, b.xn, M, dm, d.eps, st);
   mark(ev, 8, st);
   // B7: xz = xn W_in^T
-  TRY(linear_bwd(b.xn, dm, w->W_in, b.d_xz, 2 * di, b.d_xn, dm, 0, g->d_W_in, nullptr, M, dm, 2 * di, sc, scb,
+  TRY(linear_bwd(b.xn, dm, w->W_in, b.d_xz, 2 * di, b.d_xn, dm, acc, g->d_W_in, nullptr, M, dm, 2 * di, sc, scb,
                  SSM_BF16, stream));
   mark(ev, 9, st);
   // B8: RMSNorm backward plus the residual path
-  TRY(rmsnorm_bwd(x, w->norm_w, b.d_xn, d_out, d_x, g->d_norm_w, M, dm, d.eps, sc, scb, SSM_BF16, stream));
+  TRY(rmsnorm_bwd(x, w->norm_w, b.d_xn, d_out, d_x, g->d_norm_w, M, dm, d.eps, acc, sc, scb, SSM_BF16, stream));
   mark(ev, 10, st);
   return check_launch("mamba_layer_bwd");
 }

@@ -318,7 +318,8 @@ __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_vec(
 template <int K>
 __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_finalize(const float* __restrict__ part,
                                                                 float* __restrict__ d_w,
-                                                                float* __restrict__ d_bias, int parts, int Di) {
+                                                                float* __restrict__ d_bias, int parts, int Di,
+                                                                int accumulate) {
   __shared__ float s[4][kWave];
   const int lane = threadIdx.x & (kWave - 1), grp = threadIdx.x / kWave;
   const int ncol = (K + 1) * Di;
@@ -333,8 +334,8 @@ __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_finalize(const float* __r
   if (grp == 0 && col < ncol) {
     const float v = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
     const int k = col / Di, d = col - k * Di;
-    if (k < K) d_w[(size_t)d * K + k] = v;
-    else if (d_bias) d_bias[d] = v;
+    float* dst = k < K ? &d_w[(size_t)d * K + k] : d_bias ? &d_bias[d] : nullptr;
+    if (dst) *dst = accumulate ? *dst + v : v;
   }
 }
 
@@ -543,7 +544,8 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_wave(const T* __restrict
 // dw[col] = sum over parts, in a fixed order: a block owns 64 columns, its four
 // waves take every fourth part and combine in LDS
 __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_finalize(const float* __restrict__ part,
-                                                                 float* __restrict__ dw, int parts, int dim) {
+                                                                 float* __restrict__ dw, int parts, int dim,
+                                                                 int accumulate) {
   __shared__ float s[4][kWave];
   const int lane = threadIdx.x & (kWave - 1), grp = threadIdx.x / kWave;
   const int col = blockIdx.x * kWave + lane;
@@ -554,7 +556,10 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_bwd_finalize(const float* __
   }
   s[grp][lane] = acc;
   __syncthreads();
-  if (grp == 0 && col < dim) dw[col] = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
+  if (grp == 0 && col < dim) {
+    const float v = s[0][lane] + s[1][lane] + s[2][lane] + s[3][lane];
+    dw[col] = accumulate ? dw[col] + v : v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -762,8 +767,10 @@ extern "C" size_t conv1d_bwd_workspace_size(int batch, int seqlen, int d_inner, 
 
 extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u, void* d_x, float* d_w,
                           float* d_bias, int batch, int seqlen, int d_inner, int d_conv, int ld_x, int ld_du,
-                          int ld_dx, void* workspace, size_t ws_bytes, int dtype, void* stream) {
+                          int ld_dx, int flags, void* workspace, size_t ws_bytes, int dtype, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~SSM_BWD_ACCUMULATE) return fail(SSM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const int acc = (flags & SSM_BWD_ACCUMULATE) ? 1 : 0;
   if (batch < 0 || seqlen < 0 || d_inner <= 0 || d_conv <= 0)
     return fail(SSM_ERR_INVALID_ARG, "bad size (batch %d seqlen %d d_inner %d d_conv %d)", batch, seqlen, d_inner,
                 d_conv);
@@ -773,6 +780,7 @@ extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, cons
   if (!w || !d_w) return fail(SSM_ERR_INVALID_ARG, "w and d_w are required");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((size_t)batch * seqlen == 0) {  // sums over nothing
+    if (acc) return SSM_OK;
     hipLaunchKernelGGL(fill_zero_f32, dim3((d_inner * d_conv + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0, st,
                        d_w, (int64_t)d_inner * d_conv);
     if (d_bias)
@@ -801,7 +809,7 @@ extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, cons
       hipLaunchKernelGGL((conv1d_bwd_kernel<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,     \
                          (const TY*)d_u, (TY*)d_x, part, batch, seqlen, d_inner, ld_x, ld_du, ld_dx, nchunk); \
     hipLaunchKernelGGL((conv1d_bwd_finalize<KV>), fgrid, dim3(kPwBlock), 0, st, part, d_w, d_bias,            \
-                       batch * nchunk, d_inner);                                                              \
+                       batch * nchunk, d_inner, acc);                                                         \
     break;
   if (dtype == SSM_F32) {
     switch (d_conv) { CONV_CASE(float, 1) CONV_CASE(float, 2) CONV_CASE(float, 3) CONV_CASE(float, 4)
@@ -823,14 +831,17 @@ extern "C" size_t rmsnorm_bwd_workspace_size(int64_t rows, int dim) {
 }
 
 extern "C" int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_residual, void* dx,
-                           float* dw, int64_t rows, int dim, float eps, void* workspace, size_t ws_bytes, int dtype,
-                           void* stream) {
+                           float* dw, int64_t rows, int dim, float eps, int flags, void* workspace, size_t ws_bytes,
+                           int dtype, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (flags & ~SSM_BWD_ACCUMULATE) return fail(SSM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const int acc = (flags & SSM_BWD_ACCUMULATE) ? 1 : 0;
   if (rows < 0 || dim <= 0) return fail(SSM_ERR_INVALID_ARG, "bad size (rows %lld dim %d)", (long long)rows, dim);
   if (dim > kPwBlock * kRmsMaxCols) return fail(SSM_ERR_UNSUPPORTED, "dim %d > %d", dim, kPwBlock * kRmsMaxCols);
   if (!(eps >= 0.f)) return fail(SSM_ERR_INVALID_ARG, "eps must be >= 0");
   if (!dw) return fail(SSM_ERR_INVALID_ARG, "dw is required");
   if (rows == 0) {  // sum over no rows
+    if (acc) return SSM_OK;
     hipLaunchKernelGGL(fill_zero_f32, dim3((dim + kPwBlock - 1) / kPwBlock), dim3(kPwBlock), 0,
                        static_cast<hipStream_t>(stream), dw, (int64_t)dim);
     return check_launch("rmsnorm_bwd (empty)");
@@ -869,6 +880,6 @@ extern "C" int rmsnorm_bwd(const void* x, const float* w, const void* dy, const 
                          (const bf16*)dy, (const bf16*)d_residual, (bf16*)dx, part, rows, dim, eps);
   }
   hipLaunchKernelGGL(rmsnorm_bwd_finalize, dim3((dim + kWave - 1) / kWave), dim3(kPwBlock), 0, st, part, dw,
-                     blocks, dim);
+                     blocks, dim, acc);
   return check_launch("rmsnorm_bwd");
 }

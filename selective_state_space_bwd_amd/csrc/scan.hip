@@ -525,7 +525,7 @@ template <typename T, int NS>
 __global__ __launch_bounds__(kBlock) void scan_bwd_finalize(
     const float* __restrict__ A_log, T* __restrict__ d_B, T* __restrict__ d_C,
     float* __restrict__ d_A_log, float* __restrict__ d_D, const float* __restrict__ part_bc,
-    const float* __restrict__ part_a, ScanShape sh, int nblk_bc) {
+    const float* __restrict__ part_a, ScanShape sh, int nblk_bc, int accumulate) {
   __shared__ float grp_sum[kBlock / kWave][kWave];
   if ((int)blockIdx.x < nblk_bc) {
     const size_t rows = (size_t)sh.Bt * sh.T;
@@ -556,8 +556,9 @@ __global__ __launch_bounds__(kBlock) void scan_bwd_finalize(
       float tot = 0.f;
 #pragma unroll
       for (int g = 0; g < kBlock / kWave; ++g) tot += grp_sum[g][lane];
-      if (n < NS) d_A_log[(size_t)d * NS + n] = -expf(A_log[(size_t)d * NS + n]) * tot;
-      else d_D[d] = tot;
+      float* dst = n < NS ? &d_A_log[(size_t)d * NS + n] : &d_D[d];
+      const float v = n < NS ? -expf(A_log[(size_t)d * NS + n]) * tot : tot;
+      *dst = accumulate ? *dst + v : v;
     }
   }
 }
@@ -751,7 +752,7 @@ ScanWs bind(const Plan& p, void* ws) {
 template <typename T, int NS>
 int launch_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                const float* D, const void* z, const void* d_out, void* d_u, void* d_delta,
-               float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus,
+               float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int flags,
                const float* h_ckpt, const Plan& p, ScanWs w, hipStream_t st, void* const* ev) {
   auto mark = [&](int k) {
     if (ev && ev[k]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), st);
@@ -788,10 +789,10 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
                      tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),                 \
                      GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh)
   if (h_ckpt) {
-    if (softplus) SSM_MAIN(true, true);
+    if (flags & SSM_BWD_SOFTPLUS) SSM_MAIN(true, true);
     else SSM_MAIN(false, true);
   } else {
-    if (softplus) SSM_MAIN(true, false);
+    if (flags & SSM_BWD_SOFTPLUS) SSM_MAIN(true, false);
     else SSM_MAIN(false, false);
   }
 #undef SSM_MAIN
@@ -800,7 +801,8 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
   const int nblk_bc = (int)((nbc + kBlock - 1) / kBlock);
   const int nblk_a = (NS + 1) * ((sh.Di + kWave - 1) / kWave);
   hipLaunchKernelGGL((scan_bwd_finalize<T, NS>), dim3(nblk_bc + nblk_a), dim3(kBlock), 0, st, A_log,
-                     static_cast<T*>(d_B), static_cast<T*>(d_C), d_A_log, d_D, w.part_bc, w.part_a, sh, nblk_bc);
+                     static_cast<T*>(d_B), static_cast<T*>(d_C), d_A_log, d_D, w.part_bc, w.part_a, sh, nblk_bc,
+                     (flags & SSM_BWD_ACCUMULATE) ? 1 : 0);
   mark(4);
   return check_launch("ssm_scan_bwd");
 }
@@ -843,7 +845,7 @@ namespace ssm {
 namespace {
 int run_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C, const float* D,
             const void* z, const void* d_out, const float* h_ckpt, bool ckpt_given, void* d_u, void* d_delta,
-            float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus_epilogue, void* workspace,
+            float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int flags, void* workspace,
             size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream, void* const* stage_events) {
   int rc = check_dims(dims, dtype);
   if (rc != SSM_OK) return rc;
@@ -852,7 +854,9 @@ int run_bwd(const void* u, const void* delta, const float* A_log, const void* B,
   const int n_a = dm.d_inner * dm.d_state;
   if (dm.d_inner > 0 && (!A_log || !D || !d_A_log || !d_D))
     return fail(SSM_ERR_INVALID_ARG, "A_log, D, d_A_log and d_D are required");
-  if ((size_t)dm.batch * dm.seqlen * dm.d_inner == 0) return zero_params(d_A_log, d_D, n_a, dm.d_inner, st);
+  if (flags & ~(SSM_BWD_SOFTPLUS | SSM_BWD_ACCUMULATE)) return fail(SSM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((size_t)dm.batch * dm.seqlen * dm.d_inner == 0)  // sums over nothing
+    return (flags & SSM_BWD_ACCUMULATE) ? SSM_OK : zero_params(d_A_log, d_D, n_a, dm.d_inner, st);
   if (!u || !delta || !B || !C || !z || !d_out || !d_u || !d_delta || !d_B || !d_C || !d_z)
     return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
   if (ckpt_given && !h_ckpt) return fail(SSM_ERR_INVALID_ARG, "h_ckpt is null");
@@ -864,7 +868,7 @@ int run_bwd(const void* u, const void* delta, const float* A_log, const void* B,
   const ScanWs w = bind(p, workspace);
 #define SSM_BWD_CASE(TY, NSV)                                                                                    \
   return launch_bwd<TY, NSV>(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z, \
-                             softplus_epilogue, h_ckpt, p, w, st, stage_events)
+                             flags, h_ckpt, p, w, st, stage_events)
   if (dtype == SSM_F32) {
     if (dm.d_state == 16) SSM_BWD_CASE(float, 16);
     if (dm.d_state == 8) SSM_BWD_CASE(float, 8);
@@ -899,28 +903,28 @@ extern "C" size_t ssm_scan_fwd_workspace_size(const ssm_dims* dims, int dtype) {
 
 extern "C" int ssm_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                             const float* D, const void* z, const void* d_out, void* d_u, void* d_delta,
-                            float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int softplus_epilogue,
+                            float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int flags,
                             void* workspace, size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream) {
   return run_bwd(u, delta, A_log, B, C, D, z, d_out, nullptr, false, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
-                 softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, nullptr);
+                 flags, workspace, ws_bytes, dims, dtype, stream, nullptr);
 }
 
 extern "C" int ssm_scan_bwd_timed(const void* u, const void* delta, const float* A_log, const void* B,
                                   const void* C, const float* D, const void* z, const void* d_out, void* d_u,
                                   void* d_delta, float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z,
-                                  int softplus_epilogue, void* workspace, size_t ws_bytes, const ssm_dims* dims,
+                                  int flags, void* workspace, size_t ws_bytes, const ssm_dims* dims,
                                   int dtype, void* stream, void* const* stage_events) {
   return run_bwd(u, delta, A_log, B, C, D, z, d_out, nullptr, false, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
-                 softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, stage_events);
+                 flags, workspace, ws_bytes, dims, dtype, stream, stage_events);
 }
 
 extern "C" int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                                  const float* D, const void* z, const void* d_out, const float* h_ckpt, void* d_u,
                                  void* d_delta, float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z,
-                                 int softplus_epilogue, void* workspace, size_t ws_bytes, const ssm_dims* dims,
+                                 int flags, void* workspace, size_t ws_bytes, const ssm_dims* dims,
                                  int dtype, void* stream, void* const* stage_events) {
   return run_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, true, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
-                 softplus_epilogue, workspace, ws_bytes, dims, dtype, stream, stage_events);
+                 flags, workspace, ws_bytes, dims, dtype, stream, stage_events);
 }
 
 extern "C" int ssm_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,

@@ -91,18 +91,40 @@ def test_other_entry_points_validate():
     assert L.gating_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 0, None) == ssm.SSM_ERR_INVALID_ARG
     assert L.gating_bwd(None, FAKE, FAKE, FAKE, FAKE, 10, 0, None) == ssm.SSM_ERR_INVALID_ARG
     assert L.gating_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, None) == ssm.SSM_OK   # nothing to do
-    assert L.conv1d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 9, 4, 4, 4, FAKE, 1 << 30, 0,
+    assert L.conv1d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 9, 4, 4, 4, 0, FAKE, 1 << 30, 0,
                         None) == ssm.SSM_ERR_UNSUPPORTED
     assert L.conv1d_bwd_workspace_size(1, 8, 4, 9) == 0
-    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 8192, ctypes.c_float(1e-5), FAKE, 1 << 30, 0,
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 8192, ctypes.c_float(1e-5), 0, FAKE, 1 << 30, 0,
                          None) == ssm.SSM_ERR_UNSUPPORTED
-    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 64, ctypes.c_float(-1.0), FAKE, 1 << 30, 0,
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 64, ctypes.c_float(-1.0), 0, FAKE, 1 << 30, 0,
                          None) == ssm.SSM_ERR_INVALID_ARG
     dims = _dims()
     assert L.ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0, FAKE, 1 << 40,
                           ctypes.byref(dims), 0, None) == ssm.SSM_ERR_INVALID_ARG   # out needs z
     assert L.ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 12, FAKE, 1 << 40,
                           ctypes.byref(dims), 0, None) == ssm.SSM_ERR_INVALID_ARG   # ckpt_every % 8
+
+
+def test_unknown_flags_are_rejected():
+    p = [FAKE] * 15
+    d = _dims()
+    assert L.ssm_scan_bwd(*p, 8, FAKE, 1 << 40, ctypes.byref(d), 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.ssm_scan_bwd(*p, 0x100, FAKE, 1 << 40, ctypes.byref(d), 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.conv1d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 4, 4, 4, 4, 1, FAKE, 1 << 30, 0,
+                        None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 64, ctypes.c_float(1e-5), 4, FAKE, 1 << 30, 0,
+                         None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.linear_bwd(FAKE, 64, FAKE, FAKE, 64, FAKE, 64, 1, FAKE, FAKE, 16, 64, 64, FAKE, 1 << 40, 1,
+                        None) == ssm.SSM_ERR_INVALID_ARG
+    # accumulating over an empty batch leaves the parameter gradients alone: nothing is launched
+    e = _dims(batch=0)
+    assert L.ssm_scan_bwd(*p, ssm.SSM_BWD_ACCUMULATE, None, 0, ctypes.byref(e), 0, None) == ssm.SSM_OK
+    assert L.conv1d_bwd(None, FAKE, None, None, None, FAKE, FAKE, 0, 8, 4, 4, 4, 4, 4, ssm.SSM_BWD_ACCUMULATE, None, 0,
+                        0, None) == ssm.SSM_OK
+    assert L.rmsnorm_bwd(None, FAKE, None, None, None, FAKE, 0, 64, ctypes.c_float(1e-5), ssm.SSM_BWD_ACCUMULATE,
+                         None, 0, 0, None) == ssm.SSM_OK
+    assert L.linear_bwd(None, 64, FAKE, None, 64, None, 64, ssm.SSM_BWD_ACCUMULATE, FAKE, FAKE, 0, 64, 64, None, 0,
+                        1, None) == ssm.SSM_OK
 
 
 def test_linear_entry_points_validate():
