@@ -311,6 +311,76 @@ def run_layer(args, cfg):
     return line
 
 
+def cpu_baseline_recurrence(cfg):
+    """The fp64 oracle, single-threaded, one whole sequence at a time until CPU_SAMPLE_SECONDS have passed."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import recurrence as orc
+    from synth import recurrence_inputs
+    p = recurrence_inputs(cfg.batch, cfg.seqlen, cfg.channels, cfg.dtype, seed=cfg.seed, decay="ssm")
+    dt, done = 0.0, 0
+    with threadpool_limits(1):
+        while done < cfg.batch and dt < CPU_SAMPLE_SECONDS:
+            t0 = time.perf_counter()
+            orc.reverse_linear_scan(p["a"][done:done + 1], p["b"][done:done + 1])
+            dt += time.perf_counter() - t0
+            done += 1
+    n = done * cfg.seqlen * cfg.channels
+    return {"value": n / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences of the same workload, one at a time ({n} elements, "
+                      f"{dt:.1f} s, fp64 NumPy, 1 thread)"}
+
+
+def run_recurrence(args, cfg):
+    """reverse_linear_scan on [B, T, C]: the decayed sweep (the value) and the a = 1 cumsum backward."""
+    import torch
+
+    import selective_state_space_bwd_amd as ssm
+    from synth import recurrence_inputs
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    p = recurrence_inputs(cfg.batch, cfg.seqlen, cfg.channels, cfg.dtype, seed=cfg.seed, decay="ssm")
+    a = torch.from_numpy(p["a"]).to(tdt).to(dev)
+    b = torch.from_numpy(p["b"]).to(tdt).to(dev)
+    x = torch.empty_like(b)
+    ws = torch.empty(max(1, ssm.lib().reverse_linear_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.channels, 1)),
+                     dtype=torch.uint8, device=dev)
+
+    def run(decayed):
+        for _ in range(args.warmup):
+            ssm.reverse_linear_scan(a if decayed else None, b, x=x, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            ssm.reverse_linear_scan(a if decayed else None, b, x=x, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = run(True)
+    ms_unit = run(False)
+    el = 4 if cfg.dtype == "f32" else 2
+    alg = 3 * cfg.elements * el          # a, b read, x written
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "reverse linear scan elements/s (B·T·C)", "value": cfg.elements / (ms * 1e-3),
+        "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "channels": cfg.channels,
+                   "decay": "exp(-softplus(N(-2, 0.5)))"},
+        "unit_decay_ms": round(ms_unit, 4),
+        "unit_decay_GBps": round(2 * cfg.elements * el / (ms_unit * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "reverse_linear_scan (summary + carry + final sweep, one call)",
+                     "kernel_ms": round(ms, 4), "algorithmic_bytes": alg},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_recurrence(cfg)
+    return line
+
+
 def copy_probe(args):
     """A plain device-to-device copy of 1 GiB, `steps` times: 1 GiB read + 1 GiB written per launch."""
     import torch
@@ -338,9 +408,14 @@ def main():
     if args.copy_probe:
         print(json.dumps(copy_probe(args)), flush=True)
         return
-    from synth import CONFIGS, LayerConfig
+    from synth import CONFIGS, LayerConfig, RecurrenceConfig
     cfg = CONFIGS[args.workload]
-    line = run_layer(args, cfg) if isinstance(cfg, LayerConfig) else run_scan(args, cfg)
+    if isinstance(cfg, LayerConfig):
+        line = run_layer(args, cfg)
+    elif isinstance(cfg, RecurrenceConfig):
+        line = run_recurrence(args, cfg)
+    else:
+        line = run_scan(args, cfg)
     print(json.dumps(line), flush=True)
 
 

@@ -197,6 +197,23 @@ int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u
                size_t ws_bytes, int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * reverse_linear_scan — the one-state adjoint sweep of mamba-rs cpu/backward.rs
+ * Phase B3 (d_h <- da * d_h after each step) as a primitive, along t of
+ * time-major [batch, seqlen, channels] tensors (contiguous, channel fastest):
+ *     x_t = b_t + a_{t+1} x_{t+1},   x_seqlen = 0         (exclusive == 0)
+ *     x_t = a_{t+1} (b_{t+1} + ...) = (inclusive x)_t - b_t  (exclusive != 0)
+ * a == NULL means a = 1: the cumsum backward of rlx-cpu training_bwd.rs
+ * cumsum_backward_row (suffix sums, inclusive or exclusive) along t for every
+ * (batch, channel).  a, b, x share dtype (SSM_F32 / SSM_BF16 storage, float
+ * arithmetic); x must not overlap a or b.  Workspace:
+ * reverse_linear_scan_workspace_size(batch, seqlen, channels, a != NULL)
+ * (0 bytes for short sequences; the workspace pointer may then be null).
+ * ------------------------------------------------------------------------- */
+size_t reverse_linear_scan_workspace_size(int batch, int seqlen, int channels, int has_a);
+int reverse_linear_scan(const void* a, const void* b, void* x, int batch, int seqlen, int channels,
+                        int exclusive, void* workspace, size_t ws_bytes, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * rmsnorm_bwd — rlx-cpu training_bwd.rs rms_norm_backward_row over `rows`
  * rows of `dim`, without the shift term (Phase B8 of the layer passes only the
  * norm weight), plus the residual of Phase B8:

@@ -70,6 +70,8 @@ _SIGS = {
     "ssm_scan_fwd_workspace_size": (_sz, [_dims_p, _i]),
     "ssm_scan_fwd": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _i, _vp, _sz, _dims_p, _i, _vp]),
     "gating_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _vp]),
+    "reverse_linear_scan_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "reverse_linear_scan": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
     "conv1d_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "conv1d_bwd": (_i, [_vp, _fp, _fp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]),
     "rmsnorm_bwd_workspace_size": (_sz, [_i64, _i]),
@@ -295,6 +297,24 @@ def ssm_scan_fwd(u, delta, A_log, B, C, D, z=None, *, want_y: bool = True, want_
     if ck is not None:
         res["h_ckpt"] = ck
     return res
+
+
+def reverse_linear_scan(a, b, *, exclusive: bool = False, x=None, workspace=None):
+    """x_t = b_t + a_{t+1} x_{t+1} along t of [B, T, C] tensors (a None: a = 1, the cumsum
+    backward); ``exclusive`` returns x_t - b_t.  See ``reverse_linear_scan`` in include/ssmbwd.h."""
+    dt = _dtype_code(b)
+    _need(b.dim() == 3 and b.is_contiguous(), "b must be a contiguous [B, T, C] tensor")
+    if a is not None:
+        _need(a.shape == b.shape and a.dtype == b.dtype and a.is_contiguous(), "a must match b")
+    batch, seqlen, channels = b.shape
+    if x is None:
+        x = torch.empty_like(b)
+    _need(x.shape == b.shape and x.dtype == b.dtype and x.is_contiguous(), "x must match b")
+    nbytes = int(lib().reverse_linear_scan_workspace_size(batch, seqlen, channels, int(a is not None)))
+    ws, wsb = _workspace(nbytes, b.device, workspace)
+    _check("reverse_linear_scan", lib().reverse_linear_scan(_ptr(a), _ptr(b), _ptr(x), batch, seqlen, channels,
+                                                           int(bool(exclusive)), _ptr(ws), wsb, dt, _stream(b)))
+    return x
 
 
 def gating_bwd(d_out, y, z):

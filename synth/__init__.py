@@ -8,8 +8,10 @@ callers share.
 from .inputs import (  # noqa: F401
     CONFIGS,
     LayerConfig,
+    RecurrenceConfig,
     ScanConfig,
     layer_inputs,
+    recurrence_inputs,
     round_bf16,
     round_storage,
     scan_inputs,

@@ -90,6 +90,20 @@ class LayerConfig:
         return self.batch * self.seqlen * self.d_inner * self.d_state
 
 
+@dataclass(frozen=True)
+class RecurrenceConfig:
+    name: str
+    batch: int
+    seqlen: int
+    channels: int
+    dtype: str
+    seed: int
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.channels
+
+
 CONFIGS = {
     "tiny": ScanConfig("tiny B1 T64 Di32 N8 f32", 1, 64, 32, 8, "f32", 0),
     "mamba130m": ScanConfig("mamba-130m-shaped B8 T1024 Di1536 N16 f32", 8, 1024, 1536, 16, "f32", 1),
@@ -97,7 +111,26 @@ CONFIGS = {
     "mamba2p8b": ScanConfig("mamba-2.8b-shaped B2 T8192 Di5120 N16 bf16", 2, 8192, 5120, 16, "bf16", 3),
     "layer": LayerConfig("full layer B8 T2048 dm1536 di3072 N16 r96 k4 bf16",
                          8, 2048, 1536, 3072, 16, 96, 4, "bf16", 4),
+    "revscan": RecurrenceConfig("reverse linear scan B8 T2048 C2048 f32", 8, 2048, 2048, "f32", 5),
 }
+
+
+def recurrence_inputs(batch: int, seqlen: int, channels: int, dtype: str = "f32", seed: int = 5,
+                      decay: str | None = "ssm") -> dict:
+    """b ~ N(0, 1) [B, T, C] and the decay a: None (a = 1, the cumsum backward),
+    "uniform" (U(0.2, 1.0)) or "ssm" (exp(-delta) with delta = softplus(N(-2, 0.5)),
+    the decay of one state of the mamba-370m-shaped scan inputs); rounded to ``dtype``."""
+    rng = np.random.default_rng(seed)
+    b = rng.standard_normal((batch, seqlen, channels))
+    if decay is None:
+        a = None
+    elif decay == "uniform":
+        a = rng.uniform(0.2, 1.0, (batch, seqlen, channels))
+    elif decay == "ssm":
+        a = np.exp(-_softplus(-2.0 + 0.5 * rng.standard_normal((batch, seqlen, channels))))
+    else:
+        raise ValueError(f"unknown decay {decay!r}")
+    return {"a": None if a is None else round_storage(a, dtype), "b": round_storage(b, dtype)}
 
 
 def scan_inputs(batch: int, seqlen: int, d_inner: int, d_state: int, dtype: str = "f32",

@@ -127,6 +127,17 @@ def test_unknown_flags_are_rejected():
                         1, None) == ssm.SSM_OK
 
 
+def test_reverse_linear_scan_validates():
+    assert L.reverse_linear_scan(FAKE, FAKE, FAKE, 2, 64, 32, 0, FAKE, 1 << 30, 5, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.reverse_linear_scan(FAKE, None, FAKE, 2, 64, 32, 0, FAKE, 1 << 30, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.reverse_linear_scan(FAKE, FAKE, FAKE, -1, 64, 32, 0, FAKE, 1 << 30, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.reverse_linear_scan(None, None, None, 0, 64, 32, 0, None, 0, 0, None) == ssm.SSM_OK   # nothing to do
+    need = L.reverse_linear_scan_workspace_size(2, 4096, 64, 1)
+    assert need > L.reverse_linear_scan_workspace_size(2, 4096, 64, 0) > 0   # decay products need their own half
+    assert L.reverse_linear_scan(FAKE, FAKE, FAKE, 2, 4096, 64, 0, FAKE, need - 1, 0, None) == ssm.SSM_ERR_WORKSPACE
+    assert L.reverse_linear_scan_workspace_size(1, 16, 8, 1) == 0   # one segment
+
+
 def test_linear_entry_points_validate():
     ok_ws = 1 << 40
     # bf16 only
