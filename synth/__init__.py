@@ -10,6 +10,7 @@ from .inputs import (  # noqa: F401
     LayerConfig,
     RecurrenceConfig,
     ScanConfig,
+    backbone_inputs,
     layer_inputs,
     recurrence_inputs,
     round_bf16,

@@ -115,6 +115,33 @@ CONFIGS = {
 }
 
 
+def backbone_inputs(n_layers: int, input_dim: int, batch: int, seqlen: int, d_model: int, d_inner: int,
+                    d_state: int, dt_rank: int, d_conv: int, dtype: str = "bf16", seed: int = 6,
+                    weight_std: float = 0.02) -> tuple:
+    """Inputs of one backbone backward call: (bp, layers).
+
+    bp: the input embedding inp [B, T, input_dim] ~ N(0, 1) and d_out [B, T, d_model]
+    ~ N(0, 1) (rounded to ``dtype``), the input projection W_ip [d_model, input_dim]
+    ~ N(0, 1 / input_dim) (rounded to ``dtype``) with bias b_ip ~ N(0, 0.01) and the
+    final norm weight norm_f_w = 1 (float32).  layers: one parameter dict per layer
+    as ``layer_inputs`` draws them (seed 1000 seed + l), without its x and d_out.
+    """
+    rng = np.random.default_rng(seed)
+    bp = {
+        "inp": round_storage(rng.standard_normal((batch, seqlen, input_dim)), dtype),
+        "W_ip": round_storage(rng.standard_normal((d_model, input_dim)) / np.sqrt(input_dim), dtype),
+        "b_ip": (0.1 * rng.standard_normal(d_model)).astype(np.float32),
+        "norm_f_w": np.ones(d_model, dtype=np.float32),
+        "d_out": round_storage(rng.standard_normal((batch, seqlen, d_model)), dtype),
+    }
+    layers = []
+    for l in range(n_layers):
+        p = layer_inputs(1, 1, d_model, d_inner, d_state, dt_rank, d_conv, dtype, seed=1000 * seed + l,
+                         weight_std=weight_std)
+        layers.append({k: v for k, v in p.items() if k not in ("x", "d_out")})
+    return bp, layers
+
+
 def recurrence_inputs(batch: int, seqlen: int, channels: int, dtype: str = "f32", seed: int = 5,
                       decay: str | None = "ssm") -> dict:
     """b ~ N(0, 1) [B, T, C] and the decay a: None (a = 1, the cumsum backward),
