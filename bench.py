@@ -381,6 +381,84 @@ def run_recurrence(args, cfg):
     return line
 
 
+def cpu_baseline_backbone(cfg, steps: int = 0):
+    """The fp64 oracle's backbone forward + backward, single-threaded, on the first `steps` steps (default: all)
+    of one sequence."""
+    steps = steps or cfg.seqlen
+    from threadpoolctl import threadpool_limits
+
+    from oracle import backbone as orc
+    from synth import backbone_inputs
+    bp, layers = backbone_inputs(cfg.n_layers, cfg.input_dim, 1, steps, cfg.d_model, cfg.d_inner, cfg.d_state,
+                                 cfg.dt_rank, cfg.d_conv, cfg.dtype, seed=cfg.seed)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        orc.backbone_bwd(bp, layers, bp["d_out"], cfg.d_state, cfg.dt_rank, cfg.eps)
+        dt = time.perf_counter() - t0
+    se = cfg.n_layers * steps * cfg.d_inner * cfg.d_state
+    return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {steps} steps of 1 sequence at the workload's widths ({se} state elements, "
+                      f"{dt:.1f} s, fp64 NumPy forward + backward, 1 thread)"}
+
+
+def run_backbone(args, cfg):
+    """mamba_backbone_bwd on the backbone workload; its activations come from mamba_backbone_fwd before the timing."""
+    import torch
+
+    import selective_state_space_bwd_amd as ssm
+    from synth import backbone_inputs
+    dev = torch.device("cuda:0")
+    bp, layers = backbone_inputs(cfg.n_layers, cfg.input_dim, cfg.batch, cfg.seqlen, cfg.d_model, cfg.d_inner,
+                                 cfg.d_state, cfg.dt_rank, cfg.d_conv, cfg.dtype, seed=cfg.seed)
+    bf = ("inp", "W_ip", "d_out", "W_in", "W_x", "W_dt", "W_out")
+    cv = lambda k, v: (torch.from_numpy(v).to(torch.bfloat16) if k in bf else torch.from_numpy(v)).to(dev)
+    tb = {k: cv(k, v) for k, v in bp.items()}
+    tl = [{k: cv(k, v) for k, v in p.items()} for p in layers]
+    del bp, layers
+    _, kept = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, seg_len=args.seg_len)
+    ws = torch.empty(ssm.mamba_backbone_bwd_workspace_size(tb["inp"], tb["W_ip"], tl, seg_len=args.seg_len),
+                     dtype=torch.uint8, device=dev)
+    out = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws,
+                                 seg_len=args.seg_len)
+
+    def step():
+        ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws, out=out,
+                               seg_len=args.seg_len)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    M = cfg.batch * cfg.seqlen
+    dm, di, R2 = cfg.d_model, cfg.d_inner, cfg.dt_rank + 2 * cfg.d_state
+    layer_flops = 4 * M * (dm * di + di * cfg.dt_rank + di * R2 + 2 * di * dm)
+    flops = cfg.n_layers * layer_flops + 2 * M * cfg.input_dim * dm      # input projection: dW only
+    tf = flops / (ms * 1e-3) / 1e12
+    kept_bytes = sum(x.numel() * 2 for x in kept["xs"]) + sum(v.numel() * 2 for s_ in kept["saved"] for v in s_.values())
+    line = {
+        "metric": METRIC, "value": cfg.state_elements / (ms * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "input_dim": cfg.input_dim, "batch": cfg.batch,
+                   "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di, "d_state": cfg.d_state,
+                   "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv, "seg_len": args.seg_len or "auto"},
+        "memory": {"kept_activations_bytes": kept_bytes, "workspace_bytes": ws.numel()},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "every product of the step (GEMM flops over the whole step time: a lower bound)",
+                     "kernel_ms": round(ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_backbone(cfg)
+    return line
+
+
 def copy_probe(args):
     """A plain device-to-device copy of 1 GiB, `steps` times: 1 GiB read + 1 GiB written per launch."""
     import torch
@@ -408,9 +486,11 @@ def main():
     if args.copy_probe:
         print(json.dumps(copy_probe(args)), flush=True)
         return
-    from synth import CONFIGS, LayerConfig, RecurrenceConfig
+    from synth import CONFIGS, BackboneConfig, LayerConfig, RecurrenceConfig
     cfg = CONFIGS[args.workload]
-    if isinstance(cfg, LayerConfig):
+    if isinstance(cfg, BackboneConfig):
+        line = run_backbone(args, cfg)
+    elif isinstance(cfg, LayerConfig):
         line = run_layer(args, cfg)
     elif isinstance(cfg, RecurrenceConfig):
         line = run_recurrence(args, cfg)

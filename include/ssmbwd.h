@@ -350,6 +350,47 @@ int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, const ssm_l
                           size_t ws_bytes, const ssm_layer_dims* dims, void* stream,
                           void* const* stage_events);
 
+/* ---------------------------------------------------------------------------
+ * The backbone around the layers: mamba-rs cpu/backward.rs,
+ * backward_mamba_backbone_batched, and the forward it implies:
+ *     x_0 = inp W_ip^T + b_ip           (input projection, bias)
+ *     x_{l+1} = layer_l(x_l)            (mamba_layer_fwd, l = 0 .. n_layers-1)
+ *     out = RMSNorm(x_L; norm_f_w)      (eps = dims->layer.eps, no shift)
+ * The backward runs the norm_f backward first, then every layer's backward in
+ * reverse order (each hands its d_x to the layer before it), then the input
+ * projection's backward (weight and bias; the input gradient d_inp is written
+ * only if d_inp is not null: the page discards it).
+ * inp [batch, seqlen, input_dim] and W_ip [d_model, input_dim] are bf16 (input_dim
+ * a multiple of 8); b_ip (nullable in the forward), norm_f_w and their gradients
+ * are float.  `layers`, `saved`, `grads`: arrays of n_layers structs as for
+ * mamba_layer_*; `xs`: n_layers + 1 pointers to [batch, seqlen, d_model] bf16
+ * buffers, xs[0] the input projection's output, xs[l + 1] layer l's output
+ * (xs[n_layers] is norm_f's input).  The forward writes xs, saved and out; the
+ * backward reads them (the activations a training step keeps: per layer its
+ * input and the four saved tensors, 1.3 GB per layer of the full layer shape).
+ * flags: 0 or SSM_BWD_ACCUMULATE (every parameter gradient of the backbone and
+ * of every layer is added into).  Workspaces: the *_workspace_size() calls
+ * (one layer's workspace, shared by all layers in turn, plus two d_x buffers).
+ * ------------------------------------------------------------------------- */
+typedef struct ssm_backbone_dims {
+  ssm_layer_dims layer; /* every layer's shape */
+  int32_t n_layers;     /* >= 1 */
+  int32_t input_dim;    /* width of the input embedding */
+} ssm_backbone_dims;
+
+size_t mamba_backbone_fwd_workspace_size(const ssm_backbone_dims* dims);
+int mamba_backbone_fwd(const void* inp, const void* W_ip, const float* b_ip, const float* norm_f_w,
+                       const ssm_layer_weights* layers, void* const* xs, const ssm_layer_saved* saved,
+                       void* out, void* workspace, size_t ws_bytes, const ssm_backbone_dims* dims,
+                       void* stream);
+size_t mamba_backbone_bwd_workspace_size(const ssm_backbone_dims* dims);
+int mamba_backbone_bwd(const void* inp, const void* W_ip, const float* norm_f_w,
+                       const ssm_layer_weights* layers, const void* const* xs,
+                       const ssm_layer_saved* saved, const void* d_out, void* d_inp,
+                       const ssm_layer_grads* grads, float* d_W_ip, float* d_b_ip, float* d_norm_f_w,
+                       int flags, void* workspace, size_t ws_bytes, const ssm_backbone_dims* dims,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,10 @@ class ssm_layer_grads(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in LAYER_GRADS] + [("accumulate", ctypes.c_int32)]
 
 
+class ssm_backbone_dims(ctypes.Structure):
+    _fields_ = [("layer", ssm_layer_dims), ("n_layers", ctypes.c_int32), ("input_dim", ctypes.c_int32)]
+
+
 _vp, _fp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 _dims_p = ctypes.POINTER(ssm_dims)
 
@@ -89,6 +93,14 @@ _SIGS = {
                                    ctypes.POINTER(ssm_layer_grads), _vp, _sz, ctypes.POINTER(ssm_layer_dims), _vp,
                                    ctypes.POINTER(ctypes.c_void_p)]),
     "linear_fwd": (_i, [_vp, _i64, _vp, _fp, _vp, _i64, _i64, _i, _i, _vp, _sz, _i, _vp]),
+    "mamba_backbone_fwd_workspace_size": (_sz, [ctypes.POINTER(ssm_backbone_dims)]),
+    "mamba_backbone_fwd": (_i, [_vp, _vp, _fp, _fp, ctypes.POINTER(ssm_layer_weights), ctypes.POINTER(_vp),
+                                ctypes.POINTER(ssm_layer_saved), _vp, _vp, _sz, ctypes.POINTER(ssm_backbone_dims),
+                                _vp]),
+    "mamba_backbone_bwd_workspace_size": (_sz, [ctypes.POINTER(ssm_backbone_dims)]),
+    "mamba_backbone_bwd": (_i, [_vp, _vp, _fp, ctypes.POINTER(ssm_layer_weights), ctypes.POINTER(_vp),
+                                ctypes.POINTER(ssm_layer_saved), _vp, _vp, ctypes.POINTER(ssm_layer_grads), _fp, _fp,
+                                _fp, _i, _vp, _sz, ctypes.POINTER(ssm_backbone_dims), _vp]),
 }
 
 
@@ -544,4 +556,87 @@ def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, 
         ev = (ctypes.c_void_p * 11)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
         rc = lib().mamba_layer_bwd_timed(*args, ev)
     _check("mamba_layer_bwd", rc)
+    return o
+
+
+# ---------------------------------------------------------------------------
+# backbone: input projection, the layers, final RMSNorm (mamba_backbone_* in include/ssmbwd.h)
+
+def backbone_dims(inp, W_ip, layers: list, *, eps: float = 1e-5, seg_len: int = 0) -> ssm_backbone_dims:
+    batch, seqlen, input_dim = inp.shape
+    _need(len(layers) >= 1, "at least one layer")
+    d_model = W_ip.shape[0]
+    x_like = torch.empty((batch, seqlen, d_model), device="meta")
+    return ssm_backbone_dims(layer_dims(x_like, layers[0], eps=eps, seg_len=seg_len), len(layers), input_dim)
+
+
+def _backbone_arrays(bd, layers, xs, saved):
+    L = bd.n_layers
+    W = (ssm_layer_weights * L)(*[_layer_weights(p, bd.layer) for p in layers])
+    X = (ctypes.c_void_p * (L + 1))(*[ctypes.c_void_p(x.data_ptr()) for x in xs])
+    S = (ssm_layer_saved * L)(*[ssm_layer_saved(*[ctypes.c_void_p(sv[k].data_ptr()) for k in LAYER_SAVED])
+                                for sv in saved])
+    return W, X, S
+
+
+def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 1e-5, seg_len: int = 0,
+                       workspace=None):
+    """Backbone forward on bf16 activations: returns (out, kept) with kept = {"xs": [n_layers + 1 tensors],
+    "saved": [per-layer {xz, xdbl, delta, y}]}, what the backward reads."""
+    _need(inp.dtype == torch.bfloat16 and inp.dim() == 3 and inp.is_contiguous(), "inp must be contiguous bf16")
+    _need(W_ip.dtype == torch.bfloat16 and W_ip.is_contiguous() and W_ip.shape[1] == inp.shape[2], "W_ip [d_model, in]")
+    bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len)
+    d = bd.layer
+    dev = inp.device
+    B_, T_, dm, di, R2 = d.batch, d.seqlen, d.d_model, d.d_inner, d.dt_rank + 2 * d.d_state
+    xs = [torch.empty((B_, T_, dm), dtype=torch.bfloat16, device=dev) for _ in range(bd.n_layers + 1)]
+    saved = [{"xz": torch.empty((B_, T_, 2 * di), dtype=torch.bfloat16, device=dev),
+              "xdbl": torch.empty((B_, T_, R2), dtype=torch.bfloat16, device=dev),
+              "delta": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=dev),
+              "y": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=dev)} for _ in range(bd.n_layers)]
+    out = torch.empty((B_, T_, dm), dtype=torch.bfloat16, device=dev)
+    W, X, S = _backbone_arrays(bd, layers, xs, saved)
+    nbytes = int(lib().mamba_backbone_fwd_workspace_size(ctypes.byref(bd)))
+    _need(nbytes > 0, "unsupported backbone shape: " + (lib().ssm_last_error() or b"").decode())
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    _check("mamba_backbone_fwd", lib().mamba_backbone_fwd(_ptr(inp), _ptr(W_ip), _ptr(b_ip), _ptr(norm_f_w), W, X, S,
+                                                         _ptr(out), _ptr(ws), wsb, ctypes.byref(bd), _stream(inp)))
+    return out, {"xs": xs, "saved": saved}
+
+
+def mamba_backbone_bwd_workspace_size(inp, W_ip, layers: list, **kw) -> int:
+    return int(lib().mamba_backbone_bwd_workspace_size(ctypes.byref(backbone_dims(inp, W_ip, layers, **kw))))
+
+
+def mamba_backbone_bwd(inp, W_ip, norm_f_w, layers: list, kept: dict, d_out, *, need_d_inp: bool = False,
+                       accumulate: bool = False, out: dict | None = None, eps: float = 1e-5, seg_len: int = 0,
+                       workspace=None) -> dict:
+    """Backbone backward: returns {"d_W_ip", "d_b_ip", "d_norm_f_w", "layers": [per-layer gradient dicts]}
+    (and "d_inp" if asked).  ``accumulate`` adds every parameter gradient into the buffers given in ``out``."""
+    bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len)
+    d = bd.layer
+    dev = inp.device
+    _need(d_out.dtype == torch.bfloat16 and d_out.is_contiguous() and tuple(d_out.shape) == (d.batch, d.seqlen,
+                                                                                             d.d_model), "d_out")
+    o = dict(out or {})
+    if accumulate:
+        _need(all(k in o for k in ("d_W_ip", "d_b_ip", "d_norm_f_w", "layers")), "accumulate needs the buffers in out")
+    o.setdefault("d_W_ip", torch.empty(W_ip.shape, dtype=torch.float32, device=dev))
+    o.setdefault("d_b_ip", torch.empty((d.d_model,), dtype=torch.float32, device=dev))
+    o.setdefault("d_norm_f_w", torch.empty((d.d_model,), dtype=torch.float32, device=dev))
+    if "layers" not in o:
+        o["layers"] = [{"d_" + k: torch.empty((p[k] if p.get(k) is not None else p["D"]).shape, dtype=torch.float32,
+                                              device=dev) for k in LAYER_WEIGHTS} for p in layers]
+    if need_d_inp:
+        o.setdefault("d_inp", torch.empty_like(inp))
+    W, X, S = _backbone_arrays(bd, layers, kept["xs"], kept["saved"])
+    G = (ssm_layer_grads * bd.n_layers)(*[ssm_layer_grads(*[ctypes.c_void_p(g[k].data_ptr()) for k in LAYER_GRADS], 0)
+                                          for g in o["layers"]])
+    nbytes = int(lib().mamba_backbone_bwd_workspace_size(ctypes.byref(bd)))
+    _need(nbytes > 0, "unsupported backbone shape: " + (lib().ssm_last_error() or b"").decode())
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    _check("mamba_backbone_bwd", lib().mamba_backbone_bwd(
+        _ptr(inp), _ptr(W_ip), _ptr(norm_f_w), W, X, S, _ptr(d_out), _ptr(o.get("d_inp")), G, _ptr(o["d_W_ip"]),
+        _ptr(o["d_b_ip"]), _ptr(o["d_norm_f_w"]), SSM_BWD_ACCUMULATE if accumulate else 0, _ptr(ws), wsb,
+        ctypes.byref(bd), _stream(inp)))
     return o

@@ -151,5 +151,6 @@ void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* 
                           int Tn, int Di, int K, hipStream_t st);
 void launch_gate_fwd(const bf16* y, const bf16* z, int ld_z, bf16* g, int64_t rows, int Di, hipStream_t st);
 void launch_bias_softplus(bf16* v, const float* b, int64_t rows, int Di, hipStream_t st);
+void launch_bias_add(bf16* y, const float* b, int64_t rows, int n, hipStream_t st);
 
 }  // namespace ssm

@@ -283,3 +283,129 @@ extern "C" int mamba_layer_bwd(const void* x, const ssm_layer_weights* w, const 
                                size_t ws_bytes, const ssm_layer_dims* dims, void* stream) {
   return mamba_layer_bwd_timed(x, w, saved, d_out, d_x, g, workspace, ws_bytes, dims, stream, nullptr);
 }
+
+// ---------------------------------------------------------------------------
+// The backbone around the layers (mamba-rs cpu/backward.rs,
+// backward_mamba_backbone_batched): forward x_0 = inp W_ip^T + b_ip, each layer
+// x_{l+1} = layer_l(x_l), out = RMSNorm(x_L; norm_f_w); backward norm_f first,
+// the layers in reverse, then the input projection.  Every argument is checked
+// before the first launch.
+namespace {
+
+int check_backbone(const ssm_backbone_dims* bd) {
+  if (!bd) return fail(SSM_ERR_INVALID_ARG, "dims is null");
+  TRY(check_layer(&bd->layer));
+  if (bd->n_layers < 1) return fail(SSM_ERR_INVALID_ARG, "n_layers %d < 1", bd->n_layers);
+  if (bd->input_dim <= 0 || (bd->input_dim & 7))
+    return fail(SSM_ERR_UNSUPPORTED, "input_dim %d must be a positive multiple of 8", bd->input_dim);
+  return SSM_OK;
+}
+
+int check_layer_arrays(const ssm_backbone_dims* bd, const ssm_layer_weights* layers, const void* const* xs,
+                       const ssm_layer_saved* saved) {
+  if (!layers || !xs || !saved) return fail(SSM_ERR_INVALID_ARG, "layers, xs and saved are required");
+  for (int l = 0; l < bd->n_layers; ++l) {
+    TRY(check_weights(&layers[l]));
+    TRY(check_saved(&saved[l]));
+  }
+  for (int l = 0; l <= bd->n_layers; ++l)
+    if (!xs[l] || !aligned16(xs[l])) return fail(SSM_ERR_INVALID_ARG, "xs[%d] null or misaligned", l);
+  return SSM_OK;
+}
+
+size_t backbone_fwd_scratch(const ssm_backbone_dims& bd) {
+  const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
+  return max_of({mamba_layer_fwd_workspace_size(&bd.layer), linear_fwd_workspace_size(M, bd.input_dim, bd.layer.d_model)});
+}
+
+// the two [B, T, d_model] bf16 gradient buffers the layers hand along, then the scratch
+size_t backbone_bwd_scratch(const ssm_backbone_dims& bd) {
+  const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
+  return max_of({mamba_layer_bwd_workspace_size(&bd.layer), rmsnorm_bwd_workspace_size(M, bd.layer.d_model),
+                 linear_bwd_workspace_size(M, bd.input_dim, bd.layer.d_model)});
+}
+
+}  // namespace
+
+extern "C" size_t mamba_backbone_fwd_workspace_size(const ssm_backbone_dims* dims) {
+  if (!dims || check_backbone(dims) != SSM_OK) return 0;
+  return backbone_fwd_scratch(*dims);
+}
+
+extern "C" int mamba_backbone_fwd(const void* inp, const void* W_ip, const float* b_ip, const float* norm_f_w,
+                                  const ssm_layer_weights* layers, void* const* xs, const ssm_layer_saved* saved,
+                                  void* out, void* workspace, size_t ws_bytes, const ssm_backbone_dims* dims,
+                                  void* stream) {
+  TRY(check_backbone(dims));
+  const ssm_backbone_dims& bd = *dims;
+  TRY(check_layer_arrays(dims, layers, xs, saved));
+  if (!inp || !W_ip || !norm_f_w || !out || !aligned16(out)) return fail(SSM_ERR_INVALID_ARG, "a pointer is null");
+  const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
+  const int dm = bd.layer.d_model, L = bd.n_layers;
+  const size_t need = backbone_fwd_scratch(bd);
+  if (!workspace || ws_bytes < need)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  TRY(gemm_check(inp, bd.input_dim, W_ip, bd.input_dim, xs[0], (int)M, dm, bd.input_dim, ws_bytes, workspace));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY(linear_fwd(inp, bd.input_dim, W_ip, nullptr, xs[0], dm, M, bd.input_dim, dm, workspace, ws_bytes, SSM_BF16,
+                 stream));
+  if (b_ip) launch_bias_add(static_cast<bf16*>(xs[0]), b_ip, M, dm, st);
+  for (int l = 0; l < L; ++l)
+    TRY(mamba_layer_fwd(xs[l], &layers[l], xs[l + 1], &saved[l], workspace, ws_bytes, &bd.layer, stream));
+  launch_rmsnorm_fwd(static_cast<const bf16*>(xs[L]), norm_f_w, static_cast<bf16*>(out), M, dm, bd.layer.eps, st);
+  return check_launch("mamba_backbone_fwd");
+}
+
+extern "C" size_t mamba_backbone_bwd_workspace_size(const ssm_backbone_dims* dims) {
+  if (!dims || check_backbone(dims) != SSM_OK) return 0;
+  const size_t grad = align_up((size_t)dims->layer.batch * dims->layer.seqlen * dims->layer.d_model * 2);
+  return 2 * grad + backbone_bwd_scratch(*dims);
+}
+
+extern "C" int mamba_backbone_bwd(const void* inp, const void* W_ip, const float* norm_f_w,
+                                  const ssm_layer_weights* layers, const void* const* xs,
+                                  const ssm_layer_saved* saved, const void* d_out, void* d_inp,
+                                  const ssm_layer_grads* grads, float* d_W_ip, float* d_b_ip, float* d_norm_f_w,
+                                  int flags, void* workspace, size_t ws_bytes, const ssm_backbone_dims* dims,
+                                  void* stream) {
+  TRY(check_backbone(dims));
+  const ssm_backbone_dims& bd = *dims;
+  TRY(check_layer_arrays(dims, layers, xs, saved));
+  if (flags & ~SSM_BWD_ACCUMULATE) return fail(SSM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!inp || !W_ip || !norm_f_w || !d_out || !aligned16(d_out) || !grads || !d_W_ip || !d_b_ip || !d_norm_f_w)
+    return fail(SSM_ERR_INVALID_ARG, "a pointer is null");
+  for (int l = 0; l < bd.n_layers; ++l) {
+    const ssm_layer_grads* g = &grads[l];
+    if (!g->d_norm_w || !g->d_W_in || !g->d_conv_w || !g->d_conv_b || !g->d_W_x || !g->d_W_dt || !g->d_b_dt ||
+        !g->d_A_log || !g->d_D || !g->d_W_out)
+      return fail(SSM_ERR_INVALID_ARG, "a gradient pointer of layer %d is null", l);
+  }
+  const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
+  const int dm = bd.layer.d_model, L = bd.n_layers;
+  const size_t grad = align_up((size_t)M * dm * 2);
+  const size_t need = 2 * grad + backbone_bwd_scratch(bd);
+  if (!workspace || ws_bytes < need)
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  char* base = static_cast<char*>(workspace);
+  void* dbuf[2] = {base, base + grad};
+  void* sc = base + 2 * grad;
+  const size_t scb = ws_bytes - 2 * grad;
+  // the input projection's products (run last) are checked here, before anything is launched
+  TRY(gemm_check(d_out, dm, W_ip, bd.input_dim, d_inp ? d_inp : d_out, (int)M, bd.input_dim, dm, scb, sc));
+  TRY(gemm_check(d_out, dm, inp, bd.input_dim, d_W_ip, dm, bd.input_dim, (int)M, scb, sc));
+  const int acc = flags & SSM_BWD_ACCUMULATE;
+  // norm_f: d x_L (no residual here; each layer's backward adds its own)
+  TRY(rmsnorm_bwd(xs[L], norm_f_w, d_out, nullptr, dbuf[0], d_norm_f_w, M, dm, bd.layer.eps, acc, sc, scb, SSM_BF16,
+                  stream));
+  int cur = 0;
+  for (int l = L - 1; l >= 0; --l) {
+    ssm_layer_grads g = grads[l];
+    if (acc) g.accumulate = 1;
+    TRY(mamba_layer_bwd(xs[l], &layers[l], &saved[l], dbuf[cur], dbuf[cur ^ 1], &g, sc, scb, &bd.layer, stream));
+    cur ^= 1;
+  }
+  // input projection: dW_ip, db_ip (and d_inp if asked)
+  TRY(linear_bwd(inp, bd.input_dim, W_ip, dbuf[cur], dm, d_inp, bd.input_dim, acc, d_W_ip, d_b_ip, M, bd.input_dim,
+                 dm, sc, scb, SSM_BF16, stream));
+  return check_launch("mamba_backbone_bwd");
+}

@@ -679,6 +679,15 @@ __global__ __launch_bounds__(kPwBlock) void bias_softplus_kernel(bf16* __restric
   }
 }
 
+// y[r, c] += b[c] on bf16 rows of n (a linear layer's bias)
+__global__ __launch_bounds__(kPwBlock) void bias_add_kernel(bf16* __restrict__ y, const float* __restrict__ b,
+                                                            int64_t rows, int n) {
+  const int64_t total = rows * n;
+  const int64_t stride = (int64_t)gridDim.x * kPwBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kPwBlock + threadIdx.x; i < total; i += stride)
+    st(y, i, ld(y, i) + b[(int)(i % n)]);
+}
+
 namespace {
 int grid_for(int64_t n) {
   const int64_t want = (n + kPwBlock - 1) / kPwBlock;
@@ -730,6 +739,11 @@ void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* 
 void launch_gate_fwd(const bf16* y, const bf16* z, int ld_z, bf16* g, int64_t rows, int Di, hipStream_t st) {
   if (rows * Di == 0) return;
   hipLaunchKernelGGL(gate_fwd_vec, dim3(grid_for(rows * Di / 8)), dim3(kPwBlock), 0, st, y, z, ld_z, g, rows, Di / 8);
+}
+
+void launch_bias_add(bf16* y, const float* b, int64_t rows, int n, hipStream_t st) {
+  if (rows * n == 0) return;
+  hipLaunchKernelGGL(bias_add_kernel, dim3(grid_for(rows * n)), dim3(kPwBlock), 0, st, y, b, rows, n);
 }
 
 void launch_bias_softplus(bf16* v, const float* b, int64_t rows, int Di, hipStream_t st) {

@@ -7,6 +7,7 @@ callers share.
 """
 from .inputs import (  # noqa: F401
     CONFIGS,
+    BackboneConfig,
     LayerConfig,
     RecurrenceConfig,
     ScanConfig,

@@ -91,6 +91,27 @@ class LayerConfig:
 
 
 @dataclass(frozen=True)
+class BackboneConfig:
+    name: str
+    n_layers: int
+    input_dim: int
+    batch: int
+    seqlen: int
+    d_model: int
+    d_inner: int
+    d_state: int
+    dt_rank: int
+    d_conv: int
+    dtype: str
+    seed: int
+    eps: float = 1e-5
+
+    @property
+    def state_elements(self) -> int:
+        return self.n_layers * self.batch * self.seqlen * self.d_inner * self.d_state
+
+
+@dataclass(frozen=True)
 class RecurrenceConfig:
     name: str
     batch: int
@@ -111,6 +132,8 @@ CONFIGS = {
     "mamba2p8b": ScanConfig("mamba-2.8b-shaped B2 T8192 Di5120 N16 bf16", 2, 8192, 5120, 16, "bf16", 3),
     "layer": LayerConfig("full layer B8 T2048 dm1536 di3072 N16 r96 k4 bf16",
                          8, 2048, 1536, 3072, 16, 96, 4, "bf16", 4),
+    "backbone": BackboneConfig("backbone L4 B8 T2048 in512 dm1536 di3072 N16 r96 k4 bf16",
+                               4, 512, 8, 2048, 1536, 3072, 16, 96, 4, "bf16", 6),
     "revscan": RecurrenceConfig("reverse linear scan B8 T2048 C2048 f32", 8, 2048, 2048, "f32", 5),
 }
 

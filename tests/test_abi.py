@@ -138,6 +138,19 @@ def test_reverse_linear_scan_validates():
     assert L.reverse_linear_scan_workspace_size(1, 16, 8, 1) == 0   # one segment
 
 
+def test_backbone_entry_points_validate():
+    lay = ssm.ssm_layer_dims(2, 64, 64, 128, 16, 8, 4, 0, 1e-5)
+    ok = ssm.ssm_backbone_dims(lay, 2, 32)
+    assert L.mamba_backbone_bwd_workspace_size(ctypes.byref(ok)) > L.mamba_layer_bwd_workspace_size(ctypes.byref(lay))
+    assert L.mamba_backbone_fwd_workspace_size(ctypes.byref(ssm.ssm_backbone_dims(lay, 0, 32))) == 0    # no layers
+    assert L.mamba_backbone_fwd_workspace_size(ctypes.byref(ssm.ssm_backbone_dims(lay, 2, 30))) == 0    # input_dim % 8
+    # null layer arrays are rejected before anything is launched
+    assert L.mamba_backbone_bwd(FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+                                1 << 40, ctypes.byref(ok), None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.mamba_backbone_fwd(FAKE, FAKE, None, FAKE, None, None, None, FAKE, FAKE, 1 << 40, ctypes.byref(ok),
+                                None) == ssm.SSM_ERR_INVALID_ARG
+
+
 def test_linear_entry_points_validate():
     ok_ws = 1 << 40
     # bf16 only
