@@ -52,8 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--ckpt", action="store_true",
-                    help="scan workloads: time ssm_scan_bwd_ckpt, the backward that takes the forward's state "
-                         "before every 8-step chunk (made once by ssm_scan_fwd before the timed steps)")
+                    help="time the backward that takes the scan's state before every 8-step chunk from the "
+                         "forward (scan workloads: ssm_scan_bwd_ckpt after one ssm_scan_fwd; layer and backbone: "
+                         "the forward keeps them) instead of rebuilding the states")
     return ap.parse_args()
 
 
@@ -273,7 +274,7 @@ def run_layer(args, cfg):
     t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in bf else torch.from_numpy(v)).to(dev) for k, v in p.items()}
     del p
     W = {k: t[k] for k in ssm.LAYER_WEIGHTS}
-    _, saved = ssm.mamba_layer_fwd(t["x"], W, seg_len=args.seg_len)
+    _, saved = ssm.mamba_layer_fwd(t["x"], W, seg_len=args.seg_len, keep_scan_states=args.ckpt)
     ws = torch.empty(ssm.mamba_layer_bwd_workspace_size(t["x"], W, seg_len=args.seg_len), dtype=torch.uint8,
                      device=dev)
     out = ssm.mamba_layer_bwd(t["x"], W, saved, t["d_out"], workspace=ws, seg_len=args.seg_len)
@@ -299,7 +300,8 @@ def run_layer(args, cfg):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di,
                    "d_state": cfg.d_state, "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv,
-                   "seg_len": args.seg_len or "auto", "storage": "bf16"},
+                   "seg_len": args.seg_len or "auto", "storage": "bf16",
+                   "scan_states": "kept by the forward" if args.ckpt else "rebuilt"},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "gemm": {"TFLOP": round(sum(gemm_flops.values()) / 1e12, 4), "ms": round(gemm_ms, 4),
                  "TFLOPs": round(sum(gemm_flops.values()) / (gemm_ms * 1e-3) / 1e12, 1),
@@ -415,7 +417,8 @@ def run_backbone(args, cfg):
     tb = {k: cv(k, v) for k, v in bp.items()}
     tl = [{k: cv(k, v) for k, v in p.items()} for p in layers]
     del bp, layers
-    _, kept = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, seg_len=args.seg_len)
+    _, kept = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, seg_len=args.seg_len,
+                                     keep_scan_states=args.ckpt)
     ws = torch.empty(ssm.mamba_backbone_bwd_workspace_size(tb["inp"], tb["W_ip"], tl, seg_len=args.seg_len),
                      dtype=torch.uint8, device=dev)
     out = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws,
@@ -440,14 +443,16 @@ def run_backbone(args, cfg):
     layer_flops = 4 * M * (dm * di + di * cfg.dt_rank + di * R2 + 2 * di * dm)
     flops = cfg.n_layers * layer_flops + 2 * M * cfg.input_dim * dm      # input projection: dW only
     tf = flops / (ms * 1e-3) / 1e12
-    kept_bytes = sum(x.numel() * 2 for x in kept["xs"]) + sum(v.numel() * 2 for s_ in kept["saved"] for v in s_.values())
+    kept_bytes = (sum(x.numel() * x.element_size() for x in kept["xs"])
+                  + sum(v.numel() * v.element_size() for s_ in kept["saved"] for v in s_.values()))
     line = {
         "metric": METRIC, "value": cfg.state_elements / (ms * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "input_dim": cfg.input_dim, "batch": cfg.batch,
                    "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di, "d_state": cfg.d_state,
-                   "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv, "seg_len": args.seg_len or "auto"},
+                   "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv, "seg_len": args.seg_len or "auto",
+                   "scan_states": "kept by the forward" if args.ckpt else "rebuilt"},
         "memory": {"kept_activations_bytes": kept_bytes, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,

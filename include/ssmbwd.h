@@ -307,6 +307,10 @@ typedef struct ssm_layer_saved {
   void* xdbl;  /* [batch, seqlen, dt_rank + 2 d_state] x_proj output */
   void* delta; /* [batch, seqlen, d_inner] softplus output */
   void* y;     /* [batch, seqlen, d_inner] scan output before the gate */
+  float* h_ckpt; /* nullable: [batch, ceil(seqlen / 8), d_state, d_inner] float, the
+                    scan's state before every 8-step chunk; when given, the forward
+                    writes it and the backward starts its scan chunks from it
+                    (ssm_scan_bwd_ckpt) instead of rebuilding the states */
 } ssm_layer_saved;
 
 typedef struct ssm_layer_grads {

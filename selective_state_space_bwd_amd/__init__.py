@@ -46,7 +46,16 @@ class ssm_layer_weights(ctypes.Structure):
 
 
 class ssm_layer_saved(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_SAVED]
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_SAVED] + [("h_ckpt", ctypes.c_void_p)]
+
+
+def _saved_struct(saved: dict) -> ssm_layer_saved:
+    return ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED], _ptr(saved.get("h_ckpt")))
+
+
+def _scan_states(batch, seqlen, d_state, d_inner, device):
+    """The scan's state before every 8-step chunk, [B, ceil(T / 8), N, Di] float32."""
+    return torch.empty((batch, (seqlen + 7) // 8, d_state, d_inner), dtype=torch.float32, device=device)
 
 
 class ssm_layer_grads(ctypes.Structure):
@@ -498,8 +507,10 @@ def _layer_weights(weights: dict, dims: ssm_layer_dims):
                                for k in LAYER_WEIGHTS])
 
 
-def mamba_layer_fwd(x, weights: dict, *, eps: float = 1e-5, seg_len: int = 0, workspace=None):
-    """Layer forward on bf16 activations: returns (out, saved) with saved = {xz, xdbl, delta, y}."""
+def mamba_layer_fwd(x, weights: dict, *, eps: float = 1e-5, seg_len: int = 0, keep_scan_states: bool = False,
+                    workspace=None):
+    """Layer forward on bf16 activations: returns (out, saved) with saved = {xz, xdbl, delta, y}
+    (and h_ckpt, the scan's chunk states, with ``keep_scan_states``: the backward then skips rebuilding them)."""
     _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.is_contiguous(), "x must be contiguous bf16 [B, T, d_model]")
     dims = layer_dims(x, weights, eps=eps, seg_len=seg_len)
     w = _layer_weights(weights, dims)
@@ -508,8 +519,10 @@ def mamba_layer_fwd(x, weights: dict, *, eps: float = 1e-5, seg_len: int = 0, wo
              "xdbl": torch.empty((B_, T_, R2), dtype=torch.bfloat16, device=x.device),
              "delta": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=x.device),
              "y": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=x.device)}
+    if keep_scan_states:
+        saved["h_ckpt"] = _scan_states(B_, T_, dims.d_state, di, x.device)
     out = torch.empty_like(x)
-    sv = ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED])
+    sv = _saved_struct(saved)
     nbytes = int(lib().mamba_layer_fwd_workspace_size(ctypes.byref(dims)))
     _need(nbytes > 0, "unsupported layer shape: " + (lib().ssm_last_error() or b"").decode())
     ws, wsb = _workspace(nbytes, x.device, workspace)
@@ -535,7 +548,8 @@ def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, 
     for k, shp in want.items():
         t = saved[k]
         _need(tuple(t.shape) == shp and t.dtype == torch.bfloat16 and t.is_contiguous(), f"saved {k} must be {shp}")
-    sv = ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED])
+    _check_scan_states(saved, dims)
+    sv = _saved_struct(saved)
     o = dict(out or {})
     _need(not accumulate or all(k in o for k in LAYER_GRADS), "accumulate needs every gradient buffer in out")
     o.setdefault("d_x", torch.empty_like(x))
@@ -570,17 +584,26 @@ def backbone_dims(inp, W_ip, layers: list, *, eps: float = 1e-5, seg_len: int = 
     return ssm_backbone_dims(layer_dims(x_like, layers[0], eps=eps, seg_len=seg_len), len(layers), input_dim)
 
 
+def _check_scan_states(saved: dict, dims: ssm_layer_dims):
+    h = saved.get("h_ckpt")
+    if h is not None:
+        shp = (dims.batch, (dims.seqlen + 7) // 8, dims.d_state, dims.d_inner)
+        _need(tuple(h.shape) == shp and h.dtype == torch.float32 and h.is_contiguous(),
+              f"saved h_ckpt must be float32 {shp}")
+
+
 def _backbone_arrays(bd, layers, xs, saved):
+    for sv in saved:
+        _check_scan_states(sv, bd.layer)
     L = bd.n_layers
     W = (ssm_layer_weights * L)(*[_layer_weights(p, bd.layer) for p in layers])
     X = (ctypes.c_void_p * (L + 1))(*[ctypes.c_void_p(x.data_ptr()) for x in xs])
-    S = (ssm_layer_saved * L)(*[ssm_layer_saved(*[ctypes.c_void_p(sv[k].data_ptr()) for k in LAYER_SAVED])
-                                for sv in saved])
+    S = (ssm_layer_saved * L)(*[_saved_struct(sv) for sv in saved])
     return W, X, S
 
 
 def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 1e-5, seg_len: int = 0,
-                       workspace=None):
+                       keep_scan_states: bool = False, workspace=None):
     """Backbone forward on bf16 activations: returns (out, kept) with kept = {"xs": [n_layers + 1 tensors],
     "saved": [per-layer {xz, xdbl, delta, y}]}, what the backward reads."""
     _need(inp.dtype == torch.bfloat16 and inp.dim() == 3 and inp.is_contiguous(), "inp must be contiguous bf16")
@@ -594,6 +617,9 @@ def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 
               "xdbl": torch.empty((B_, T_, R2), dtype=torch.bfloat16, device=dev),
               "delta": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=dev),
               "y": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=dev)} for _ in range(bd.n_layers)]
+    if keep_scan_states:
+        for sv in saved:
+            sv["h_ckpt"] = _scan_states(B_, T_, d.d_state, di, dev)
     out = torch.empty((B_, T_, dm), dtype=torch.bfloat16, device=dev)
     W, X, S = _backbone_arrays(bd, layers, xs, saved)
     nbytes = int(lib().mamba_backbone_fwd_workspace_size(ctypes.byref(bd)))

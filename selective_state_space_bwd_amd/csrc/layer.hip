@@ -57,7 +57,8 @@ int check_weights(const ssm_layer_weights* w) {
 
 int check_saved(const ssm_layer_saved* s) {
   if (!s || !s->xz || !s->xdbl || !s->delta || !s->y) return fail(SSM_ERR_INVALID_ARG, "a saved activation is null");
-  if (!aligned16(s->xz) || !aligned16(s->xdbl) || !aligned16(s->delta) || !aligned16(s->y))
+  if (!aligned16(s->xz) || !aligned16(s->xdbl) || !aligned16(s->delta) || !aligned16(s->y) ||
+      (s->h_ckpt && !aligned16(s->h_ckpt)))
     return fail(SSM_ERR_UNSUPPORTED, "activations must be 16-byte aligned");
   return SSM_OK;
 }
@@ -196,8 +197,8 @@ extern "C" int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* 
   gemm_bf16(xdbl, true, R2, w->W_dt, true, R, delta, di, SSM_BF16, (int)M, di, R, 0, b.scratch, st);
   launch_bias_softplus(delta, w->b_dt, M, di, st);
   const ssm_dims sd = scan_dims_of(d);
-  TRY(ssm_scan_fwd(b.u, delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, saved->y, b.gated, nullptr, 0,
-                   b.scratch, b.scratch_bytes, &sd, SSM_BF16, stream));
+  TRY(ssm_scan_fwd(b.u, delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, saved->y, b.gated, saved->h_ckpt,
+                   saved->h_ckpt ? 8 : 0, b.scratch, b.scratch_bytes, &sd, SSM_BF16, stream));
   // residual: out = x, then out += gated W_out^T
   if (hipMemcpyAsync(out, x, (size_t)M * dm * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
     return fail(SSM_ERR_LAUNCH, "residual copy failed");
@@ -249,9 +250,14 @@ extern "C" int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, 
   launch_conv_silu_fwd(xz, 2 * di, w->conv_w, w->conv_b, b.u, di, d.batch, d.seqlen, di, d.d_conv, st);
   mark(ev, 3, st);
   // B2 + B3 (+ softplus backward): d_z lands in the second half of d_xz, d_B | d_C in d_xdbl
-  TRY(ssm_scan_bwd(b.u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated, b.d_u, b.d_raw,
-                   g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D, b.d_xz + di, SSM_BWD_SOFTPLUS | acc, sc, scb,
-                   &sd, SSM_BF16, stream));
+  if (saved->h_ckpt)
+    TRY(ssm_scan_bwd_ckpt(b.u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated,
+                          saved->h_ckpt, b.d_u, b.d_raw, g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D,
+                          b.d_xz + di, SSM_BWD_SOFTPLUS | acc, sc, scb, &sd, SSM_BF16, stream, nullptr));
+  else
+    TRY(ssm_scan_bwd(b.u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated, b.d_u, b.d_raw,
+                     g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D, b.d_xz + di, SSM_BWD_SOFTPLUS | acc, sc, scb,
+                     &sd, SSM_BF16, stream));
   mark(ev, 4, st);
   // B4: raw = dt_in W_dt^T + b_dt, dt_in = xdbl[:, :R]; d_dt_in fills d_xdbl[:, :R]
   TRY(linear_bwd(xdbl, R2, w->W_dt, b.d_raw, di, b.d_xdbl, R2, acc, g->d_W_dt, g->d_b_dt, M, R, di, sc, scb,

@@ -99,6 +99,25 @@ def test_layer_end_to_end(shape):
     _check({k: _np(v) for k, v in g.items()}, ref, GRADS, "backward", tol=TOL_END_TO_END)
 
 
+@pytest.mark.parametrize("shape", SHAPES[:2])
+def test_layer_end_to_end_with_scan_states(shape):
+    """The forward keeps the scan's chunk states (saved h_ckpt) and the backward starts
+    its scan chunks from them: the oracle's bar end to end, and close to the backward
+    that rebuilds the states (only float rounding in the scan differs)."""
+    Bt, T, dm, di, N, R, K = shape
+    p = _inputs(shape, seed=5 + sum(shape))
+    t = _dev(p)
+    print(f"case: layer fwd (keeping scan states) + bwd {shape}", flush=True)
+    out, saved = _ssm().mamba_layer_fwd(t["x"], _weights(t), seg_len=16, keep_scan_states=True)
+    g = _ssm().mamba_layer_bwd(t["x"], _weights(t), saved, t["d_out"], seg_len=16)
+    plain = {k: v for k, v in saved.items() if k != "h_ckpt"}
+    h = _ssm().mamba_layer_bwd(t["x"], _weights(t), plain, t["d_out"], seg_len=16)
+    torch.cuda.synchronize()
+    ref = orc.layer_bwd(p, p["d_out"], N, R)
+    _check({k: _np(v) for k, v in g.items()}, ref, GRADS, "backward from states", tol=TOL_END_TO_END)
+    _check({k: _np(v) for k, v in g.items()}, {k: _np(v) for k, v in h.items()}, GRADS, "vs rebuilt states", tol=1e-2)
+
+
 @pytest.mark.parametrize("variant", ["default", "perturbed"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_layer_bwd_from_oracle_activations(shape, variant):
