@@ -16,6 +16,8 @@
 // global loads are in flight while the matrix cores work on the current one,
 // one barrier per k step.  Split-k writes fp32 partial tiles that a second
 // kernel sums in a fixed order.
+#include <math.h>
+
 #include "common.hpp"
 
 namespace ssm {
@@ -348,21 +350,62 @@ __global__ __launch_bounds__(256) void column_sum_final(const float* __restrict_
 
 namespace {
 
-// the block tile: 256 rows when the product has enough rows that the grid still
-// covers the chip, else 128
-int pick_bm(int M, int N) {
-  const long long big = (long long)((M + 255) / 256) * ((N + 127) / 128);
-  return (M >= 1024 && big >= 256) ? 256 : 128;
+// CUs of the current device (256 if it cannot be queried), looked up once per device
+long gemm_device_cus() {
+  static int cached[64];  // 0 = not looked up yet; every writer stores the same value
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  return cus;
 }
 
-// how many k splits: enough blocks to cover the chip, each split at least 4 k steps
-int pick_splits(int M, int N, int K) {
-  const int bm = pick_bm(M, N);
-  const long long tiles = (long long)((M + bm - 1) / bm) * ((N + 127) / 128);
-  int s = 1;
-  while (tiles * s * 2 <= 1024 && (K / (s * 2)) >= 4 * kBK) s *= 2;
-  return s;
+// Block tile height (256 or 128 rows; two or three blocks per CU) and k splits,
+// picked together from a cost model fitted to measured times of the layer's
+// products on the chip: the product's flops at a per-tile-size rate, stretched
+// when the last round of blocks leaves CUs idle, plus the split-k partial
+// traffic.  256-row tiles need at least 1024 rows and 512 k to pay for their
+// set-up; a split keeps at least 128 k.
+struct TilePick {
+  int bm, splits;
+};
+
+TilePick pick_tiles(int M, int N, int K) {
+  static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+  const long cus = gemm_device_cus();
+  TilePick best{128, 1};
+  double best_t = -1.0;
+  for (int bm : {128, 256}) {
+    if (bm == 256 && (M < 1024 || K < 512)) continue;
+    const double rate = bm == 256 ? 650e12 : 500e12;  // flop/s of the whole chip at this tile size
+    const double slots = (double)cus * (bm == 256 ? 2 : 3);
+    const double tiles = (double)((M + bm - 1) / bm) * ((N + 127) / 128);
+    for (int s : kSplits) {
+      if (s > 1 && K / s < 4 * kBK) break;
+      const int ks = ((K + s - 1) / s + kBK - 1) / kBK * kBK;
+      const int used = (K + ks - 1) / ks;  // splits that get k
+      const double r = tiles * used / slots, rounds = ceil(r);
+      const double work = 2.0 * M * N * K / rate;
+      double t = r < 1.0 ? work * rounds / r : work * (1.0 + 0.2 * (rounds - r) / r);
+      if (used > 1) t += 2.0 * used * (double)M * N * 4.0 / 3e12;
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        best = TilePick{bm, s};
+      }
+    }
+  }
+  return best;
 }
+
+int pick_bm(int M, int N, int K) { return pick_tiles(M, N, K).bm; }
+int pick_splits(int M, int N, int K) { return K > 0 ? pick_tiles(M, N, K).splits : 1; }
 
 template <bool A_K, bool B_K, typename OutT>
 int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) {
@@ -370,7 +413,7 @@ int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) 
   const int ksplit = max(kBK, ((g.K + splits - 1) / splits + kBK - 1) / kBK * kBK);
   g.k_per_split = ksplit;
   const int nsplit = (g.K + ksplit - 1) / ksplit;
-  const int bm = pick_bm(g.M, g.N);
+  const int bm = pick_bm(g.M, g.N, g.K);
   dim3 grid((g.N + 127) / 128, (g.M + bm - 1) / bm, nsplit);
   g.partial = nsplit > 1 ? partial : nullptr;
   if (bm == 256)
@@ -412,7 +455,7 @@ int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool 
   const long long vec = out_dtype == SSM_F32 ? 4 : 8;  // elements per 16-byte vector of C
   GemmArgs g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, nullptr, lda, ldb, ldc, M, N, K,
              0, accumulate, aligned16(C) && ldc % vec == 0};
-  const int splits = K > 0 ? pick_splits(M, N, K) : 1;
+  const int splits = pick_splits(M, N, K);
   float* part = static_cast<float*>(workspace);
 #define GEMM_CASE(AK, BK)                                                                      \
   if (a_kcontig == AK && b_kcontig == BK) {                                                    \
