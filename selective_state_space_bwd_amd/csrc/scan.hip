@@ -361,10 +361,11 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
   const int c_first = t0 / kChunk, c_last = (t1 - 1) / kChunk;
   const T* __restrict__ Bb = Bm + row0 * sh.ld_bc;
   const T* __restrict__ Cb = Cm + row0 * sh.ld_bc;
-  // float: the last chunk's B | C rows go to LDS before the sweep, and each chunk
-  // fetches the next one's while it computes.  bf16 reads them per step with
-  // scalar loads (its VGPR budget has no room for the staged rows).
-  constexpr bool kStage = sizeof(T) == 4;
+  // float, and bf16 when the chunk states are given: the last chunk's B | C rows
+  // go to LDS before the sweep, and each chunk fetches the next one's while it
+  // computes.  bf16 rebuilding its own states reads them per step with scalar
+  // loads instead (its VGPR budget has no room for the staged rows).
+  constexpr bool kStage = sizeof(T) == 4 || GCK;
   if (kStage) {
     if (tid < kChunk * 2 * NS)
       (&bcs[c_last & 1][0][0])[tid] =
