@@ -150,6 +150,7 @@ void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, i
 void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* bias, bf16* u, int ld_u, int Bt,
                           int Tn, int Di, int K, hipStream_t st);
 void launch_gate_fwd(const bf16* y, const bf16* z, int ld_z, bf16* g, int64_t rows, int Di, hipStream_t st);
+// (Di a multiple of 8, v 16-byte aligned: the layer's shapes)
 void launch_bias_softplus(bf16* v, const float* b, int64_t rows, int Di, hipStream_t st);
 void launch_bias_add(bf16* y, const float* b, int64_t rows, int n, hipStream_t st);
 

@@ -200,3 +200,21 @@ def test_full_size_sampled_mamba370m():
     q = {k: (v[:1] if v.ndim == 3 else v) for k, v in p.items()}
     r = oracle_bwd(q)
     _check({"d_B": g["d_B"][:1], "d_C": g["d_C"][:1]}, r, TOL[c.dtype], keys=("d_B", "d_C"), label="batch 0")
+
+
+@pytest.mark.parametrize("nb,T", [(0, 16), (2, 0)])
+def test_empty_inputs(nb, T):
+    """Sums over nothing: d_A_log and d_D are zeroed, or left as they are when accumulating."""
+    p = scan_inputs(1, 8, 12, 8, "f32", seed=1)
+    t = _to_dev(p, "f32")
+    e = torch.empty((nb, T, 12), device=DEV)
+    eb = torch.empty((nb, T, 8), device=DEV)
+    h = torch.empty((nb, (T + 7) // 8, 8, 12), device=DEV)
+    print(f"case: ssm_scan_bwd_ckpt empty batch {nb} seqlen {T}", flush=True)
+    g = _ssm().ssm_scan_bwd_ckpt(e, e, t["A_log"], eb, eb, t["D"], e, e, h,
+                                 out={"d_A_log": torch.full_like(t["A_log"], 3.0), "d_D": torch.full_like(t["D"], 3.0)})
+    a = _ssm().ssm_scan_bwd_ckpt(e, e, t["A_log"], eb, eb, t["D"], e, e, h, accumulate=True,
+                                 out={"d_A_log": torch.full_like(t["A_log"], 3.0), "d_D": torch.full_like(t["D"], 3.0)})
+    torch.cuda.synchronize()
+    assert torch.all(g["d_A_log"] == 0) and torch.all(g["d_D"] == 0)
+    assert torch.all(a["d_A_log"] == 3.0) and torch.all(a["d_D"] == 3.0)
