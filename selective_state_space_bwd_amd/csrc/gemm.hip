@@ -63,21 +63,23 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ p, long
 // One operand's R x 32 tile: its global -> register -> LDS moves and its MFMA
 // operand reads.
 // KC (k contiguous): LDS [row][k], rows of 32 bf16 = four 16-byte chunks, chunk
-// c of row r stored at c ^ ((r >> 1) & 3).  Eight lanes of a 16-byte access then
-// fall in eight different 16-byte bank groups both when a store writes two rows'
-// four chunks and when a fragment read takes one chunk of eight rows.
-// Otherwise: LDS [k][row], rows of R + 16 bf16 (the padding spreads the four k
-// rows a transposing read touches over different banks).
+// c of row r stored at c ^ ((r >> 2) & 3).  The 16 lanes that the 64-bank LDS
+// serves together in a 16-byte access then fall in 16 different 16-byte bank
+// groups both when a store writes four rows' four chunks and when a fragment
+// read takes one chunk of 16 rows (rows 4 apart would otherwise share a group).
+// Otherwise: LDS [k][row], rows of R + 32 bf16: the 32 lanes of a transposing
+// 8-byte read touch four k rows at two column offsets, and the 64-byte row
+// padding puts those eight 32-byte pieces on eight different bank ranges.
 template <bool KC, int R>
 struct OperandTile {
-  static constexpr int kLd = KC ? kBK : R + 16;
+  static constexpr int kLd = KC ? kBK : R + 32;
   static constexpr int kElems = KC ? R * kLd : kBK * kLd;
   static constexpr int kPer = R * kBK / 8 / kGemmThreads;  // 16-byte chunks per thread
   static_assert(kPer >= 1 && R % 32 == 0, "tile shape");
   uint4 v[kPer];
 
   static __device__ __forceinline__ int kc_offset(int r, int chunk) {
-    return r * kLd + ((chunk ^ ((r >> 1) & 3)) << 3);
+    return r * kLd + ((chunk ^ ((r >> 2) & 3)) << 3);
   }
   // Interior tiles: each thread's chunks sit at fixed byte offsets from the
   // tile's first element, so a k step only moves a wave-uniform base.
