@@ -18,6 +18,8 @@
 // kernel sums in a fixed order.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.hpp"
 
 namespace ssm {
@@ -354,18 +356,21 @@ namespace {
 
 // CUs of the current device (256 if it cannot be queried), looked up once per device
 long gemm_device_cus() {
-  static int cached[64];  // 0 = not looked up yet; every writer stores the same value
+  static std::atomic<int> cached[64];  // 0 = not looked up yet; every writer stores the same value
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return 256;
   }
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
     (void)hipGetLastError();
     cus = 256;
   }
-  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  if (dev >= 0 && dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
