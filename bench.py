@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="backbone: keep only the layer inputs (SSM_KEEP_INPUTS); the backward reruns each layer's "
+                         "forward")
     ap.add_argument("--ckpt", action="store_true",
                     help="time the backward that takes the scan's state before every 8-step chunk from the "
                          "forward (scan workloads: ssm_scan_bwd_ckpt after one ssm_scan_fwd; layer and backbone: "
@@ -417,9 +420,10 @@ def run_backbone(args, cfg):
     tb = {k: cv(k, v) for k, v in bp.items()}
     tl = [{k: cv(k, v) for k, v in p.items()} for p in layers]
     del bp, layers
+    keep = "inputs" if args.recompute else "all"
     _, kept = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, seg_len=args.seg_len,
-                                     keep_scan_states=args.ckpt)
-    ws = torch.empty(ssm.mamba_backbone_bwd_workspace_size(tb["inp"], tb["W_ip"], tl, seg_len=args.seg_len),
+                                     keep=keep, keep_scan_states=args.ckpt)
+    ws = torch.empty(ssm.mamba_backbone_bwd_workspace_size(tb["inp"], tb["W_ip"], tl, seg_len=args.seg_len, keep=keep),
                      dtype=torch.uint8, device=dev)
     out = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws,
                                  seg_len=args.seg_len)
@@ -444,7 +448,7 @@ def run_backbone(args, cfg):
     flops = cfg.n_layers * layer_flops + 2 * M * cfg.input_dim * dm      # input projection: dW only
     tf = flops / (ms * 1e-3) / 1e12
     kept_bytes = (sum(x.numel() * x.element_size() for x in kept["xs"])
-                  + sum(v.numel() * v.element_size() for s_ in kept["saved"] for v in s_.values()))
+                  + sum(v.numel() * v.element_size() for s_ in (kept["saved"] or []) for v in s_.values()))
     line = {
         "metric": METRIC, "value": cfg.state_elements / (ms * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
@@ -452,7 +456,8 @@ def run_backbone(args, cfg):
         "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "input_dim": cfg.input_dim, "batch": cfg.batch,
                    "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di, "d_state": cfg.d_state,
                    "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv, "seg_len": args.seg_len or "auto",
-                   "scan_states": "kept by the forward" if args.ckpt else "rebuilt"},
+                   "scan_states": "kept by the forward" if args.ckpt else "rebuilt",
+                   "kept": "layer inputs only (activations recomputed)" if args.recompute else "all activations"},
         "memory": {"kept_activations_bytes": kept_bytes, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,

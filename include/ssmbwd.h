@@ -380,7 +380,19 @@ typedef struct ssm_backbone_dims {
   ssm_layer_dims layer; /* every layer's shape */
   int32_t n_layers;     /* >= 1 */
   int32_t input_dim;    /* width of the input embedding */
+  int32_t keep;         /* SSM_KEEP_ALL or SSM_KEEP_INPUTS (activation memory plan) */
 } ssm_backbone_dims;
+
+/* What a training step keeps between the backbone's forward and backward:
+ * SSM_KEEP_ALL: xs and every layer's saved activations (`saved`, with its
+ *   optional h_ckpt), 455 MB per layer of the full layer shape;
+ * SSM_KEEP_INPUTS: only xs (50 MB per layer); `saved` may be null, the forward
+ *   writes each layer's activations into its workspace and drops them, and the
+ *   backward runs each layer's forward again (into its workspace) just before
+ *   that layer's backward: one more layer forward per layer for about 86 % less
+ *   kept memory.  Results are the same bitwise (the same kernels rebuild the
+ *   same activations). */
+enum { SSM_KEEP_ALL = 0, SSM_KEEP_INPUTS = 1 };
 
 size_t mamba_backbone_fwd_workspace_size(const ssm_backbone_dims* dims);
 int mamba_backbone_fwd(const void* inp, const void* W_ip, const float* b_ip, const float* norm_f_w,

@@ -63,7 +63,11 @@ class ssm_layer_grads(ctypes.Structure):
 
 
 class ssm_backbone_dims(ctypes.Structure):
-    _fields_ = [("layer", ssm_layer_dims), ("n_layers", ctypes.c_int32), ("input_dim", ctypes.c_int32)]
+    _fields_ = [("layer", ssm_layer_dims), ("n_layers", ctypes.c_int32), ("input_dim", ctypes.c_int32),
+                ("keep", ctypes.c_int32)]
+
+
+SSM_KEEP_ALL, SSM_KEEP_INPUTS = 0, 1
 
 
 _vp, _fp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -576,12 +580,17 @@ def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, 
 # ---------------------------------------------------------------------------
 # backbone: input projection, the layers, final RMSNorm (mamba_backbone_* in include/ssmbwd.h)
 
-def backbone_dims(inp, W_ip, layers: list, *, eps: float = 1e-5, seg_len: int = 0) -> ssm_backbone_dims:
+def backbone_dims(inp, W_ip, layers: list, *, eps: float = 1e-5, seg_len: int = 0,
+                  keep: str = "all") -> ssm_backbone_dims:
+    """keep: "all" (every layer's saved activations, SSM_KEEP_ALL) or "inputs" (only the layer
+    inputs, SSM_KEEP_INPUTS: the backward recomputes each layer's activations)."""
     batch, seqlen, input_dim = inp.shape
     _need(len(layers) >= 1, "at least one layer")
+    _need(keep in ("all", "inputs"), 'keep is "all" or "inputs"')
     d_model = W_ip.shape[0]
     x_like = torch.empty((batch, seqlen, d_model), device="meta")
-    return ssm_backbone_dims(layer_dims(x_like, layers[0], eps=eps, seg_len=seg_len), len(layers), input_dim)
+    return ssm_backbone_dims(layer_dims(x_like, layers[0], eps=eps, seg_len=seg_len), len(layers), input_dim,
+                             SSM_KEEP_ALL if keep == "all" else SSM_KEEP_INPUTS)
 
 
 def _check_scan_states(saved: dict, dims: ssm_layer_dims):
@@ -593,22 +602,25 @@ def _check_scan_states(saved: dict, dims: ssm_layer_dims):
 
 
 def _backbone_arrays(bd, layers, xs, saved):
-    for sv in saved:
-        _check_scan_states(sv, bd.layer)
     L = bd.n_layers
     W = (ssm_layer_weights * L)(*[_layer_weights(p, bd.layer) for p in layers])
     X = (ctypes.c_void_p * (L + 1))(*[ctypes.c_void_p(x.data_ptr()) for x in xs])
+    if saved is None:
+        return W, X, None
+    for sv in saved:
+        _check_scan_states(sv, bd.layer)
     S = (ssm_layer_saved * L)(*[_saved_struct(sv) for sv in saved])
     return W, X, S
 
 
 def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 1e-5, seg_len: int = 0,
-                       keep_scan_states: bool = False, workspace=None):
+                       keep: str = "all", keep_scan_states: bool = False, workspace=None):
     """Backbone forward on bf16 activations: returns (out, kept) with kept = {"xs": [n_layers + 1 tensors],
-    "saved": [per-layer {xz, xdbl, delta, y}]}, what the backward reads."""
+    "saved": [per-layer {xz, xdbl, delta, y}] (None with keep="inputs"), "keep": keep}, what the backward reads."""
     _need(inp.dtype == torch.bfloat16 and inp.dim() == 3 and inp.is_contiguous(), "inp must be contiguous bf16")
     _need(W_ip.dtype == torch.bfloat16 and W_ip.is_contiguous() and W_ip.shape[1] == inp.shape[2], "W_ip [d_model, in]")
-    bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len)
+    _need(not (keep == "inputs" and keep_scan_states), "scan states are kept only with keep=\"all\"")
+    bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len, keep=keep)
     d = bd.layer
     dev = inp.device
     B_, T_, dm, di, R2 = d.batch, d.seqlen, d.d_model, d.d_inner, d.dt_rank + 2 * d.d_state
@@ -620,6 +632,8 @@ def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 
     if keep_scan_states:
         for sv in saved:
             sv["h_ckpt"] = _scan_states(B_, T_, d.d_state, di, dev)
+    if keep == "inputs":
+        saved = None
     out = torch.empty((B_, T_, dm), dtype=torch.bfloat16, device=dev)
     W, X, S = _backbone_arrays(bd, layers, xs, saved)
     nbytes = int(lib().mamba_backbone_fwd_workspace_size(ctypes.byref(bd)))
@@ -627,7 +641,11 @@ def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 
     ws, wsb = _workspace(nbytes, dev, workspace)
     _check("mamba_backbone_fwd", lib().mamba_backbone_fwd(_ptr(inp), _ptr(W_ip), _ptr(b_ip), _ptr(norm_f_w), W, X, S,
                                                          _ptr(out), _ptr(ws), wsb, ctypes.byref(bd), _stream(inp)))
-    return out, {"xs": xs, "saved": saved}
+    return out, {"xs": xs, "saved": saved, "keep": keep}
+
+
+def mamba_backbone_fwd_workspace_size(inp, W_ip, layers: list, **kw) -> int:
+    return int(lib().mamba_backbone_fwd_workspace_size(ctypes.byref(backbone_dims(inp, W_ip, layers, **kw))))
 
 
 def mamba_backbone_bwd_workspace_size(inp, W_ip, layers: list, **kw) -> int:
@@ -638,8 +656,10 @@ def mamba_backbone_bwd(inp, W_ip, norm_f_w, layers: list, kept: dict, d_out, *, 
                        accumulate: bool = False, out: dict | None = None, eps: float = 1e-5, seg_len: int = 0,
                        workspace=None) -> dict:
     """Backbone backward: returns {"d_W_ip", "d_b_ip", "d_norm_f_w", "layers": [per-layer gradient dicts]}
-    (and "d_inp" if asked).  ``accumulate`` adds every parameter gradient into the buffers given in ``out``."""
-    bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len)
+    (and "d_inp" if asked).  ``accumulate`` adds every parameter gradient into the buffers given in ``out``.
+    ``kept`` as mamba_backbone_fwd returns it (its "keep" plan decides whether the layers' activations are
+    read or recomputed)."""
+    bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len, keep=kept.get("keep", "all"))
     d = bd.layer
     dev = inp.device
     _need(d_out.dtype == torch.bfloat16 and d_out.is_contiguous() and tuple(d_out.shape) == (d.batch, d.seqlen,

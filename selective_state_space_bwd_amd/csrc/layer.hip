@@ -302,6 +302,8 @@ int check_backbone(const ssm_backbone_dims* bd) {
   if (!bd) return fail(SSM_ERR_INVALID_ARG, "dims is null");
   TRY(check_layer(&bd->layer));
   if (bd->n_layers < 1) return fail(SSM_ERR_INVALID_ARG, "n_layers %d < 1", bd->n_layers);
+  if (bd->keep != SSM_KEEP_ALL && bd->keep != SSM_KEEP_INPUTS)
+    return fail(SSM_ERR_INVALID_ARG, "keep %d is neither SSM_KEEP_ALL nor SSM_KEEP_INPUTS", bd->keep);
   if (bd->input_dim <= 0 || (bd->input_dim & 7))
     return fail(SSM_ERR_UNSUPPORTED, "input_dim %d must be a positive multiple of 8", bd->input_dim);
   return SSM_OK;
@@ -309,10 +311,11 @@ int check_backbone(const ssm_backbone_dims* bd) {
 
 int check_layer_arrays(const ssm_backbone_dims* bd, const ssm_layer_weights* layers, const void* const* xs,
                        const ssm_layer_saved* saved) {
-  if (!layers || !xs || !saved) return fail(SSM_ERR_INVALID_ARG, "layers, xs and saved are required");
+  const bool kept = bd->keep == SSM_KEEP_ALL;
+  if (!layers || !xs || (kept && !saved)) return fail(SSM_ERR_INVALID_ARG, "layers, xs and saved are required");
   for (int l = 0; l < bd->n_layers; ++l) {
     TRY(check_weights(&layers[l]));
-    TRY(check_saved(&saved[l]));
+    if (kept) TRY(check_saved(&saved[l]));
   }
   for (int l = 0; l <= bd->n_layers; ++l)
     if (!xs[l] || !aligned16(xs[l])) return fail(SSM_ERR_INVALID_ARG, "xs[%d] null or misaligned", l);
@@ -324,18 +327,47 @@ size_t backbone_fwd_scratch(const ssm_backbone_dims& bd) {
   return max_of({mamba_layer_fwd_workspace_size(&bd.layer), linear_fwd_workspace_size(M, bd.input_dim, bd.layer.d_model)});
 }
 
-// the two [B, T, d_model] bf16 gradient buffers the layers hand along, then the scratch
 size_t backbone_bwd_scratch(const ssm_backbone_dims& bd) {
   const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
-  return max_of({mamba_layer_bwd_workspace_size(&bd.layer), rmsnorm_bwd_workspace_size(M, bd.layer.d_model),
-                 linear_bwd_workspace_size(M, bd.input_dim, bd.layer.d_model)});
+  size_t s = max_of({mamba_layer_bwd_workspace_size(&bd.layer), rmsnorm_bwd_workspace_size(M, bd.layer.d_model),
+                     linear_bwd_workspace_size(M, bd.input_dim, bd.layer.d_model)});
+  if (bd.keep == SSM_KEEP_INPUTS) s = max_of({s, mamba_layer_fwd_workspace_size(&bd.layer)});
+  return s;
+}
+
+// With SSM_KEEP_INPUTS, one layer's saved activations and its (recomputed)
+// output live in the workspace, reused by every layer in turn.
+struct LayerKeep {
+  ssm_layer_saved saved;
+  void* out;
+};
+
+LayerKeep carve_keep(const ssm_layer_dims& d, void* ws, size_t* total) {
+  const size_t M = (size_t)d.batch * d.seqlen;
+  Carver c{static_cast<char*>(ws)};
+  LayerKeep k{};
+  k.saved.xz = c.take(M * 2 * d.d_inner * 2);
+  k.saved.xdbl = c.take(M * (d.dt_rank + 2 * d.d_state) * 2);
+  k.saved.delta = c.take(M * d.d_inner * 2);
+  k.saved.y = c.take(M * d.d_inner * 2);
+  k.saved.h_ckpt = nullptr;
+  k.out = c.take(M * d.d_model * 2);
+  *total = c.off;
+  return k;
+}
+
+size_t keep_bytes(const ssm_backbone_dims& bd) {
+  if (bd.keep != SSM_KEEP_INPUTS) return 0;
+  size_t total = 0;
+  carve_keep(bd.layer, nullptr, &total);
+  return total;
 }
 
 }  // namespace
 
 extern "C" size_t mamba_backbone_fwd_workspace_size(const ssm_backbone_dims* dims) {
   if (!dims || check_backbone(dims) != SSM_OK) return 0;
-  return backbone_fwd_scratch(*dims);
+  return keep_bytes(*dims) + backbone_fwd_scratch(*dims);
 }
 
 extern "C" int mamba_backbone_fwd(const void* inp, const void* W_ip, const float* b_ip, const float* norm_f_w,
@@ -348,16 +380,20 @@ extern "C" int mamba_backbone_fwd(const void* inp, const void* W_ip, const float
   if (!inp || !W_ip || !norm_f_w || !out || !aligned16(out)) return fail(SSM_ERR_INVALID_ARG, "a pointer is null");
   const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
   const int dm = bd.layer.d_model, L = bd.n_layers;
-  const size_t need = backbone_fwd_scratch(bd);
+  const size_t kb = keep_bytes(bd);
+  const size_t need = kb + backbone_fwd_scratch(bd);
   if (!workspace || ws_bytes < need)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
-  TRY(gemm_check(inp, bd.input_dim, W_ip, bd.input_dim, xs[0], (int)M, dm, bd.input_dim, ws_bytes, workspace));
+  size_t unused = 0;
+  const LayerKeep keep = carve_keep(bd.layer, workspace, &unused);   // used with SSM_KEEP_INPUTS only
+  void* sc = static_cast<char*>(workspace) + kb;
+  const size_t scb = ws_bytes - kb;
+  TRY(gemm_check(inp, bd.input_dim, W_ip, bd.input_dim, xs[0], (int)M, dm, bd.input_dim, scb, sc));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  TRY(linear_fwd(inp, bd.input_dim, W_ip, nullptr, xs[0], dm, M, bd.input_dim, dm, workspace, ws_bytes, SSM_BF16,
-                 stream));
+  TRY(linear_fwd(inp, bd.input_dim, W_ip, nullptr, xs[0], dm, M, bd.input_dim, dm, sc, scb, SSM_BF16, stream));
   if (b_ip) launch_bias_add(static_cast<bf16*>(xs[0]), b_ip, M, dm, st);
   for (int l = 0; l < L; ++l)
-    TRY(mamba_layer_fwd(xs[l], &layers[l], xs[l + 1], &saved[l], workspace, ws_bytes, &bd.layer, stream));
+    TRY(mamba_layer_fwd(xs[l], &layers[l], xs[l + 1], kb ? &keep.saved : &saved[l], sc, scb, &bd.layer, stream));
   launch_rmsnorm_fwd(static_cast<const bf16*>(xs[L]), norm_f_w, static_cast<bf16*>(out), M, dm, bd.layer.eps, st);
   return check_launch("mamba_backbone_fwd");
 }
@@ -365,7 +401,7 @@ extern "C" int mamba_backbone_fwd(const void* inp, const void* W_ip, const float
 extern "C" size_t mamba_backbone_bwd_workspace_size(const ssm_backbone_dims* dims) {
   if (!dims || check_backbone(dims) != SSM_OK) return 0;
   const size_t grad = align_up((size_t)dims->layer.batch * dims->layer.seqlen * dims->layer.d_model * 2);
-  return 2 * grad + backbone_bwd_scratch(*dims);
+  return 2 * grad + keep_bytes(*dims) + backbone_bwd_scratch(*dims);
 }
 
 extern "C" int mamba_backbone_bwd(const void* inp, const void* W_ip, const float* norm_f_w,
@@ -389,13 +425,16 @@ extern "C" int mamba_backbone_bwd(const void* inp, const void* W_ip, const float
   const int64_t M = (int64_t)bd.layer.batch * bd.layer.seqlen;
   const int dm = bd.layer.d_model, L = bd.n_layers;
   const size_t grad = align_up((size_t)M * dm * 2);
-  const size_t need = 2 * grad + backbone_bwd_scratch(bd);
+  const size_t kb = keep_bytes(bd);
+  const size_t need = 2 * grad + kb + backbone_bwd_scratch(bd);
   if (!workspace || ws_bytes < need)
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
   char* base = static_cast<char*>(workspace);
   void* dbuf[2] = {base, base + grad};
-  void* sc = base + 2 * grad;
-  const size_t scb = ws_bytes - 2 * grad;
+  size_t unused = 0;
+  const LayerKeep keep = carve_keep(bd.layer, base + 2 * grad, &unused);   // used with SSM_KEEP_INPUTS only
+  void* sc = base + 2 * grad + kb;
+  const size_t scb = ws_bytes - 2 * grad - kb;
   // the input projection's products (run last) are checked here, before anything is launched
   TRY(gemm_check(d_out, dm, W_ip, bd.input_dim, d_inp ? d_inp : d_out, (int)M, bd.input_dim, dm, scb, sc));
   TRY(gemm_check(d_out, dm, inp, bd.input_dim, d_W_ip, dm, bd.input_dim, (int)M, scb, sc));
@@ -407,7 +446,10 @@ extern "C" int mamba_backbone_bwd(const void* inp, const void* W_ip, const float
   for (int l = L - 1; l >= 0; --l) {
     ssm_layer_grads g = grads[l];
     if (acc) g.accumulate = 1;
-    TRY(mamba_layer_bwd(xs[l], &layers[l], &saved[l], dbuf[cur], dbuf[cur ^ 1], &g, sc, scb, &bd.layer, stream));
+    // SSM_KEEP_INPUTS: this layer's activations again, from its kept input
+    if (kb) TRY(mamba_layer_fwd(xs[l], &layers[l], keep.out, &keep.saved, sc, scb, &bd.layer, stream));
+    const ssm_layer_saved* sv = kb ? &keep.saved : &saved[l];
+    TRY(mamba_layer_bwd(xs[l], &layers[l], sv, dbuf[cur], dbuf[cur ^ 1], &g, sc, scb, &bd.layer, stream));
     cur ^= 1;
   }
   // input projection: dW_ip, db_ip (and d_inp if asked)

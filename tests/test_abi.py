@@ -144,6 +144,11 @@ def test_backbone_entry_points_validate():
     assert L.mamba_backbone_bwd_workspace_size(ctypes.byref(ok)) > L.mamba_layer_bwd_workspace_size(ctypes.byref(lay))
     assert L.mamba_backbone_fwd_workspace_size(ctypes.byref(ssm.ssm_backbone_dims(lay, 0, 32))) == 0    # no layers
     assert L.mamba_backbone_fwd_workspace_size(ctypes.byref(ssm.ssm_backbone_dims(lay, 2, 30))) == 0    # input_dim % 8
+    assert L.mamba_backbone_fwd_workspace_size(ctypes.byref(ssm.ssm_backbone_dims(lay, 2, 32, 5))) == 0  # keep plan
+    # keeping only the layer inputs: one layer's activations move into the workspaces
+    inputs = ssm.ssm_backbone_dims(lay, 2, 32, ssm.SSM_KEEP_INPUTS)
+    assert L.mamba_backbone_bwd_workspace_size(ctypes.byref(inputs)) > L.mamba_backbone_bwd_workspace_size(ctypes.byref(ok))
+    assert L.mamba_backbone_fwd_workspace_size(ctypes.byref(inputs)) > L.mamba_backbone_fwd_workspace_size(ctypes.byref(ok))
     # null layer arrays are rejected before anything is launched
     assert L.mamba_backbone_bwd(FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
                                 1 << 40, ctypes.byref(ok), None) == ssm.SSM_ERR_INVALID_ARG

@@ -131,3 +131,28 @@ def test_backbone_bwd_accumulate_two_micro_batches_and_determinism():
     for k in gf:
         assert np.array_equal(gf[k], g2[k]), k          # bitwise repeatable
         assert norm_err(ga[k], gf[k]) < 1e-4, k         # only the float summation order differs
+
+
+def test_backbone_keep_inputs_recomputes_the_same_gradients():
+    """SSM_KEEP_INPUTS keeps only the layer inputs and reruns each layer's forward in
+    the backward: the same kernels rebuild the same activations, so the forward's
+    outputs and every gradient equal those of SSM_KEEP_ALL bitwise."""
+    shape = SHAPES[1]
+    L, Bt, T, mid, dm, di, N, R, K = shape
+    bp, layers = _inputs(shape, seed=91)
+    tb, tl = _dev(bp, layers)
+    ssm = _ssm()
+    print(f"case: backbone keep inputs vs keep all {shape}", flush=True)
+    out_a, kept_a = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, keep="all")
+    out_i, kept_i = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, keep="inputs")
+    assert kept_i["saved"] is None
+    ga = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept_a, tb["d_out"], need_d_inp=True)
+    gi = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept_i, tb["d_out"], need_d_inp=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_i)
+    for xa, xi in zip(kept_a["xs"], kept_i["xs"]):
+        assert torch.equal(xa, xi)
+    a, i = _grads(ga), _grads(gi)
+    for k in a:
+        assert np.array_equal(a[k], i[k]), k
+    assert torch.equal(ga["d_inp"], gi["d_inp"])
