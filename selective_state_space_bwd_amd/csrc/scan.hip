@@ -372,17 +372,44 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
           bc_element<T, NS>(Bb, Cb, sh.ld_bc, c_last * kChunk, min(kChunk, t1 - c_last * kChunk), tid);
     __syncthreads();
   }
+  // a chunk's loads: its per-step channel values (delta, u, z, d_out) and, when
+  // the states are given, its starting state.  With given states the next
+  // chunk's loads go out at the end of the current one, before its barrier, into
+  // registers it no longer needs (measured: 2-3 % off the sweep); a sweep that
+  // rebuilds its states issues them at the chunk's start (earlier costs bf16 a
+  // tenth and float nothing).
+  float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
+  float hg[NS];
+  const auto load_chunk = [&](int c) {
+    const int tc = c * kChunk;
+    const int nv = min(kChunk, t1 - tc);
+    if (GCK) {
+      const size_t cc = (size_t)b * sh.nchunk + c;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) hg[n] = ckpt[(cc * NS + n) * Di + dc];
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        const size_t i = (row0 + tc + j) * Di + dc;
+        dl[j] = ld(delta, i);
+        uu[j] = ld(u, i);
+        zr[j] = ld(z, (row0 + tc + j) * sh.ld_z + dc);
+        gr[j] = ld(dout, i);
+      }
+    }
+  };
+  if (GCK) load_chunk(c_last);
   for (int c = c_last; c >= c_first; --c) {
     const int tc = c * kChunk;
     const int nv = min(kChunk, t1 - tc);
     const int buf = c & 1;
     const float bc_next = kStage && c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
-    // state before the chunk: local checkpoint + decayed carry-in
+    // state before the chunk: given, or local checkpoint + decayed carry-in
     float h[NS];
     if (GCK) {
-      const size_t cc = (size_t)b * sh.nchunk + c;
 #pragma unroll
-      for (int n = 0; n < NS; ++n) h[n] = ckpt[(cc * NS + n) * Di + dc];
+      for (int n = 0; n < NS; ++n) h[n] = hg[n];
     } else if (c == c_first) {
 #pragma unroll
       for (int n = 0; n < NS; ++n) h[n] = (s == 0) ? 0.f : seg_h[(sg * NS + n) * Di + dc];
@@ -395,19 +422,9 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
         h[n] = fmaf(fast_exp2(A2[n] * sdv), hin, ckpt[(cc * NS + n) * Di + dc]);
       }
     }
-    // per-step channel values: delta, u, dy = d_out SiLU(z), and the d_z factor
-    // issue the chunk's loads together; the gate math waits for them step by step
-    float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      if (j < nv) {
-        const size_t i = (row0 + tc + j) * Di + dc;
-        dl[j] = ld(delta, i);
-        uu[j] = ld(u, i);
-        zr[j] = ld(z, (row0 + tc + j) * sh.ld_z + dc);
-        gr[j] = ld(dout, i);
-      }
-    }
+    // the gate math (dy = d_out SiLU(z) and the d_z factor) waits for the loads
+    // step by step
+    if (!GCK) load_chunk(c);
     // forward: rebuild the chunk's states, keep a_t h_{t-1}
     float ah[kReg][NS];
 #pragma unroll
@@ -498,6 +515,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
         if ((lane & (kRep - 1)) == 0) red[buf][wave][j][lane >> (6 - kLogNS)] = dB[0];
       }
     }
+    if (GCK && c > c_first) load_chunk(c - 1);
     // the buffer written here was last read before the previous chunk's barrier
     if (kStage && c > c_first && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
     __syncthreads();
