@@ -208,6 +208,7 @@ int conv1d_bwd(const void* x, const float* w, const float* bias, const void* d_u
  * arithmetic); x must not overlap a or b.  Workspace:
  * reverse_linear_scan_workspace_size(batch, seqlen, channels, a != NULL)
  * (0 bytes for short sequences; the workspace pointer may then be null).
+ * Limits: batch <= 65535 and batch * channels < 2^31, else SSM_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
 size_t reverse_linear_scan_workspace_size(int batch, int seqlen, int channels, int has_a);
 int reverse_linear_scan(const void* a, const void* b, void* x, int batch, int seqlen, int channels,

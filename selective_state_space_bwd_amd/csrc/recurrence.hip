@@ -62,20 +62,35 @@ __global__ __launch_bounds__(kRsBlock) void rs_summary(const T* __restrict__ a, 
   if (HAS_A) Dp[o] = D;
 }
 
-// in place: V[b, s] becomes the carry entering segment s from the right
+// in place: V[b, s] becomes the carry entering segment s from the right.  One
+// thread per channel walks the segments; each group's loads are issued together
+// (the carry chain itself is one fma per segment), and one-wave blocks spread the
+// few channels over many CUs.
+constexpr int kRsCarryBlock = 64;
+
 template <bool HAS_A>
-__global__ __launch_bounds__(kRsBlock) void rs_carry(float* __restrict__ V, const float* __restrict__ Dp, int Bt,
-                                                     RsShape sh) {
-  const int idx = blockIdx.x * kRsBlock + threadIdx.x;
+__global__ __launch_bounds__(kRsCarryBlock) void rs_carry(float* __restrict__ V, const float* __restrict__ Dp, int Bt,
+                                                          RsShape sh) {
+  const int idx = blockIdx.x * kRsCarryBlock + threadIdx.x;
   if (idx >= Bt * sh.C) return;
   const int bi = idx / sh.C, c = idx - bi * sh.C;
   const size_t o0 = (size_t)bi * sh.nseg * sh.C + c;
   float cin = 0.f;
-  for (int s = sh.nseg - 1; s >= 1; --s) {
-    const size_t o = o0 + (size_t)s * sh.C;
-    const float v = V[o];
-    V[o] = cin;
-    cin = HAS_A ? fmaf(Dp[o], cin, v) : v + cin;
+  for (int top = sh.nseg - 1; top >= 1; top -= kRsGroup) {
+    float v[kRsGroup], dp[kRsGroup];
+#pragma unroll
+    for (int j = 0; j < kRsGroup; ++j) {  // segments below 1 repeat segment 1 (never used)
+      const size_t o = o0 + (size_t)max(top - j, 1) * sh.C;
+      v[j] = V[o];
+      dp[j] = HAS_A ? Dp[o] : 1.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kRsGroup; ++j) {
+      if (top - j >= 1) {
+        V[o0 + (size_t)(top - j) * sh.C] = cin;
+        cin = HAS_A ? fmaf(dp[j], cin, v[j]) : v[j] + cin;
+      }
+    }
   }
   V[o0] = cin;
 }
@@ -136,13 +151,13 @@ void rs_launch(const void* a, const void* b, void* x, int batch, const RsShape& 
   const int ntile = (sh.C + kRsBlock - 1) / kRsBlock;
   if (sh.nseg > 1) {
     const dim3 g1(ntile, sh.nseg - 1, batch);
-    const int nc = (int)(((long long)batch * sh.C + kRsBlock - 1) / kRsBlock);
+    const int nc = (int)(((long long)batch * sh.C + kRsCarryBlock - 1) / kRsCarryBlock);
     if (a) {
       hipLaunchKernelGGL((rs_summary<T, true>), g1, dim3(kRsBlock), 0, st, ta, tb, V, Dp, sh);
-      hipLaunchKernelGGL((rs_carry<true>), dim3(nc), dim3(kRsBlock), 0, st, V, Dp, batch, sh);
+      hipLaunchKernelGGL((rs_carry<true>), dim3(nc), dim3(kRsCarryBlock), 0, st, V, Dp, batch, sh);
     } else {
       hipLaunchKernelGGL((rs_summary<T, false>), g1, dim3(kRsBlock), 0, st, ta, tb, V, Dp, sh);
-      hipLaunchKernelGGL((rs_carry<false>), dim3(nc), dim3(kRsBlock), 0, st, V, Dp, batch, sh);
+      hipLaunchKernelGGL((rs_carry<false>), dim3(nc), dim3(kRsCarryBlock), 0, st, V, Dp, batch, sh);
     }
   }
   const dim3 g3(ntile, sh.nseg, batch);
@@ -175,6 +190,9 @@ extern "C" int reverse_linear_scan(const void* a, const void* b, void* x, int ba
   if ((size_t)batch * seqlen * channels == 0) return SSM_OK;
   if (!b || !x) return fail(SSM_ERR_INVALID_ARG, "b and x are required");
   if ((double)seqlen * channels * batch > 9.0e15) return fail(SSM_ERR_INVALID_ARG, "tensor too large");
+  // batch is a grid dimension (<= 65535) and one carry thread runs per (batch, channel)
+  if (batch > 65535 || (long long)batch * channels >= (1LL << 31))
+    return fail(SSM_ERR_INVALID_ARG, "batch %d x channels %d beyond the supported range", batch, channels);
   const RsShape sh = rs_plan(batch, seqlen, channels);
   const size_t need = rs_workspace(batch, sh, a != nullptr);
   if (need && (!workspace || ws_bytes < need))

@@ -136,6 +136,9 @@ def test_reverse_linear_scan_validates():
     assert need > L.reverse_linear_scan_workspace_size(2, 4096, 64, 0) > 0   # decay products need their own half
     assert L.reverse_linear_scan(FAKE, FAKE, FAKE, 2, 4096, 64, 0, FAKE, need - 1, 0, None) == ssm.SSM_ERR_WORKSPACE
     assert L.reverse_linear_scan_workspace_size(1, 16, 8, 1) == 0   # one segment
+    # batch is a grid dimension; one carry thread per (batch, channel)
+    assert L.reverse_linear_scan(FAKE, FAKE, FAKE, 70000, 2, 8, 0, FAKE, 1 << 30, 0, None) == ssm.SSM_ERR_INVALID_ARG
+    assert L.reverse_linear_scan(FAKE, FAKE, FAKE, 4, 2, 1 << 29, 0, FAKE, 1 << 62, 0, None) == ssm.SSM_ERR_INVALID_ARG
 
 
 def test_backbone_entry_points_validate():
