@@ -268,7 +268,11 @@ __global__ __launch_bounds__(kBlock) void scan_gsum(const T* __restrict__ delta,
 // ---------------------------------------------------------------------------
 // 2. carries across segments, one thread per (b, n, d), in place.  Segment s's
 // decay is exp(A * sum of its delta); the forward carry (FWD) runs over s
-// ascending, the adjoint carry (BWD) descending.
+// ascending, the adjoint carry (BWD) descending.  Each group of segments' loads
+// goes out before the group's stores (a load behind a store to the same array
+// would otherwise wait for it), so a thread pays one memory round trip per group.
+constexpr int kCarryGroup = 8;
+
 template <int NS, bool FWD, bool BWD>
 __global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A_log, float* __restrict__ seg_h,
                                                      float* __restrict__ seg_g, const float* __restrict__ seg_sd,
@@ -282,22 +286,40 @@ __global__ __launch_bounds__(kBlock) void scan_carry(const float* __restrict__ A
   const size_t h0 = ((size_t)b * sh.nseg * NS + n) * Di + d;
   const size_t hs = (size_t)NS * Di;
   float H = 0.f;
-#pragma unroll 4
-  for (int s = 0; FWD && s < sh.nseg; ++s) {
-    const float dec = fast_exp2(A2 * seg_sd[sd0 + (size_t)s * Di]);
-    const float loc = seg_h[h0 + s * hs];
-    seg_h[h0 + s * hs] = H;
-    H = fmaf(dec, H, loc);
+  for (int s0 = 0; FWD && s0 < sh.nseg; s0 += kCarryGroup) {
+    float sd[kCarryGroup], loc[kCarryGroup];
+#pragma unroll
+    for (int j = 0; j < kCarryGroup; ++j) {  // past the last segment: repeat it (never used)
+      const size_t s = (size_t)min(s0 + j, sh.nseg - 1);
+      sd[j] = seg_sd[sd0 + s * Di];
+      loc[j] = seg_h[h0 + s * hs];
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryGroup; ++j) {
+      if (s0 + j < sh.nseg) {
+        seg_h[h0 + (size_t)(s0 + j) * hs] = H;
+        H = fmaf(fast_exp2(A2 * sd[j]), H, loc[j]);
+      }
+    }
   }
   if (!BWD) return;
   // the adjoint leaving segment s; segment 0's own summary is not needed
   float G = 0.f;
-#pragma unroll 4
-  for (int s = sh.nseg - 1; s >= 1; --s) {
-    const float dec = fast_exp2(A2 * seg_sd[sd0 + (size_t)s * Di]);
-    const float loc = seg_g[h0 + s * hs];
-    seg_g[h0 + s * hs] = G;
-    G = fmaf(dec, G, loc);
+  for (int s0 = sh.nseg - 1; s0 >= 1; s0 -= kCarryGroup) {
+    float sd[kCarryGroup], loc[kCarryGroup];
+#pragma unroll
+    for (int j = 0; j < kCarryGroup; ++j) {  // below segment 1: repeat it (never used)
+      const size_t s = (size_t)max(s0 - j, 1);
+      sd[j] = seg_sd[sd0 + s * Di];
+      loc[j] = seg_g[h0 + s * hs];
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryGroup; ++j) {
+      if (s0 - j >= 1) {
+        seg_g[h0 + (size_t)(s0 - j) * hs] = G;
+        G = fmaf(fast_exp2(A2 * sd[j]), G, loc[j]);
+      }
+    }
   }
   seg_g[h0] = G;
 }
