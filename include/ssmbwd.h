@@ -2,17 +2,19 @@
  * ssmbwd.h — C ABI of the MI355X (gfx950) selective-scan backward library.
  *
  * Operations are those of the Mamba layer backward walked by mamba-rs 0.5.1
- * (src/mamba_ssm/cpu/backward.rs, backward_mamba_layer_batched), with the
- * closed-form RMSNorm backward of rlx-cpu 0.2.17 (src/training_bwd.rs,
- * rms_norm_backward_row).  The CPU page runs them as sequential loops over one
- * sequence; here every call is a batch of sequences on one GPU.
+ * (src/mamba_ssm/cpu/backward.rs, backward_mamba_layer_batched, and the
+ * backbone around it, backward_mamba_backbone_batched), with the closed-form
+ * RMSNorm and cumsum backward of rlx-cpu 0.2.17 (src/training_bwd.rs,
+ * rms_norm_backward_row, cumsum_backward_row).  The CPU pages run them as
+ * sequential loops over one sequence; here every call is a batch of sequences
+ * on one GPU.
  *
  * Conventions for every entry point
  *  - Memory: all tensor pointers are DEVICE pointers to contiguous row-major
  *    storage owned by the caller.  The library never allocates or frees device
  *    memory; scratch space is a caller-provided workspace whose size the
- *    matching *_workspace_size() call returns.  Gradients are OVERWRITTEN, not
- *    accumulated.
+ *    matching *_workspace_size() call returns.  Gradients are overwritten
+ *    unless the call's flags include SSM_BWD_ACCUMULATE (ssm_bwd_flags).
  *  - Storage dtype: [batch, seqlen, *] activations and their gradients are
  *    SSM_F32 (float) or SSM_BF16 (bfloat16, round-to-nearest-even on store).
  *    Parameters (A_log, D, conv weight and bias, norm weight) and their
@@ -372,7 +374,8 @@ int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, const ssm_l
  * buffers, xs[0] the input projection's output, xs[l + 1] layer l's output
  * (xs[n_layers] is norm_f's input).  The forward writes xs, saved and out; the
  * backward reads them (the activations a training step keeps: per layer its
- * input and the four saved tensors, 1.3 GB per layer of the full layer shape).
+ * input and the four saved tensors, about 0.46 GB per layer of the full layer
+ * shape, see ssm_backbone_dims.keep).
  * flags: 0 or SSM_BWD_ACCUMULATE (every parameter gradient of the backbone and
  * of every layer is added into).  Workspaces: the *_workspace_size() calls
  * (one layer's workspace, shared by all layers in turn, plus two d_x buffers).
