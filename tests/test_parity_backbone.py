@@ -156,3 +156,29 @@ def test_backbone_keep_inputs_recomputes_the_same_gradients():
     for k in a:
         assert np.array_equal(a[k], i[k]), k
     assert torch.equal(ga["d_inp"], gi["d_inp"])
+
+
+def test_backbone_keep_inputs_accumulates_like_keep_all():
+    """Two micro-batches summed into one set of gradient buffers under SSM_KEEP_INPUTS
+    (each backward reruns the layer forwards into its workspace) equal the same sum
+    under SSM_KEEP_ALL bitwise; asking the inputs plan to keep scan states is refused."""
+    shape = SHAPES[1]
+    ssm = _ssm()
+    print(f"case: backbone keep inputs, two accumulated micro-batches {shape}", flush=True)
+    sums = {}
+    for keep in ("all", "inputs"):
+        acc = None
+        for seed in (93, 94):
+            bp, layers = _inputs(shape, seed=seed)
+            tb, tl = _dev(bp, layers)
+            _, kept = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, keep=keep)
+            args = (tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"])
+            acc = ssm.mamba_backbone_bwd(*args) if acc is None else ssm.mamba_backbone_bwd(*args, out=acc,
+                                                                                          accumulate=True)
+        torch.cuda.synchronize()
+        sums[keep] = _grads(acc)
+    for k in sums["all"]:
+        assert np.array_equal(sums["all"][k], sums["inputs"][k]), k
+    with pytest.raises(Exception):
+        ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, keep="inputs",
+                               keep_scan_states=True)
