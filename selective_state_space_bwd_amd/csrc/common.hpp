@@ -15,10 +15,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // bfloat16 storage is a raw 16-bit pattern; conversion is exact on load and
-// round-to-nearest-even on store.
+// round-to-nearest-even on store (gfx950's v_cvt_pk_bf16_f32, which also turns
+// a NaN into a quiet NaN).
 struct bf16 {
   uint16_t bits;
 };
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
@@ -29,10 +32,12 @@ template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
-  uint32_t b = __float_as_uint(x);
-  if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x007fffffu)) return bf16{uint16_t((b >> 16) | 0x40u)};
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return bf16{uint16_t(b >> 16)};
+  return bf16{__builtin_bit_cast(uint16_t, (__bf16)x)};
+}
+// two values rounded by one instruction: lo in bits 0-15, hi in bits 16-31
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T>

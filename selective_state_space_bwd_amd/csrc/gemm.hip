@@ -173,7 +173,7 @@ __device__ __forceinline__ void write_row16(T* __restrict__ rowp, int col, int n
             lo += __uint_as_float(pw[e] << 16);
             hi += __uint_as_float(pw[e] & 0xffff0000u);
           }
-          ow[e] = uint32_t(from_f32<bf16>(lo).bits) | (uint32_t(from_f32<bf16>(hi).bits) << 16);
+          ow[e] = pack_bf16x2(lo, hi);
         }
         *reinterpret_cast<uint4*>(p) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }

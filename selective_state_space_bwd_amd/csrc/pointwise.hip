@@ -40,7 +40,7 @@ struct Vec16 {
       uint32_t u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        u[i] = uint32_t(from_f32<bf16>(v[2 * i]).bits) | (uint32_t(from_f32<bf16>(v[2 * i + 1]).bits) << 16);
+        u[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
       w = make_uint4(u[0], u[1], u[2], u[3]);
     }
     *reinterpret_cast<uint4*>(p) = w;

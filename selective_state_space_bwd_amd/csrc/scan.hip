@@ -71,6 +71,18 @@ __device__ __forceinline__ float bc_element(const T* __restrict__ Bb, const T* _
   return k < NS ? ld(Bb, row + k) : ld(Cb, row + (k - NS));
 }
 
+// One element of a row whose address is the same in every lane of the wave,
+// at a 32-bit per-lane element offset (the row pointer is scalar, the lane's
+// part a 32-bit byte offset).
+template <typename T>
+__device__ __forceinline__ float ld_row(const T* __restrict__ row, uint32_t col) {
+  return to_f32(*reinterpret_cast<const T*>(reinterpret_cast<const char*>(row) + col * (uint32_t)sizeof(T)));
+}
+template <typename T>
+__device__ __forceinline__ void st_row(T* __restrict__ row, uint32_t col, float v) {
+  *reinterpret_cast<T*>(reinterpret_cast<char*>(row) + col * (uint32_t)sizeof(T)) = from_f32<T>(v);
+}
+
 template <int NS>
 __device__ __forceinline__ void bc_row(const float (&bcs)[kChunk][2 * NS], int j, float (&Bv)[NS], float (&Cv)[NS]) {
   const float4* p = reinterpret_cast<const float4*>(&bcs[j][0]);
@@ -414,6 +426,11 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
   // registers it no longer needs (measured: 2-3 % off the sweep); a sweep that
   // rebuilds its states issues them at the chunk's start (earlier costs bf16 a
   // tenth and float nothing).
+  // Per-step rows addressed as scalar row pointer + 32-bit lane offset: fewer
+  // VALU address operations in bf16 and with given states (measured in the ISA:
+  // 6 % and 4 % fewer VALU instructions); the float sweep that rebuilds its
+  // states keeps 64-bit lane addresses, which spill less there.
+  constexpr bool kRowAddr = sizeof(T) == 2 || GCK;
   float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
   float hg[NS];
   const auto load_chunk = [&](int c) {
@@ -427,11 +444,19 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       if (j < nv) {
-        const size_t i = (row0 + tc + j) * Di + dc;
-        dl[j] = ld(delta, i);
-        uu[j] = ld(u, i);
-        zr[j] = ld(z, (row0 + tc + j) * sh.ld_z + dc);
-        gr[j] = ld(dout, i);
+        if (kRowAddr) {
+          const size_t r = (row0 + tc + j) * Di;
+          dl[j] = ld_row(delta + r, dc);
+          uu[j] = ld_row(u + r, dc);
+          zr[j] = ld_row(z + (row0 + tc + j) * sh.ld_z, dc);
+          gr[j] = ld_row(dout + r, dc);
+        } else {
+          const size_t i = (row0 + tc + j) * Di + dc;
+          dl[j] = ld(delta, i);
+          uu[j] = ld(u, i);
+          zr[j] = ld(z, (row0 + tc + j) * sh.ld_z + dc);
+          gr[j] = ld(dout, i);
+        }
       }
     }
   };
@@ -496,7 +521,10 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
 #pragma unroll
           for (int n = 0; n < NS; ++n) ah[j >= kLds ? j - kLds : 0][n] = aj[n];
         }
-        if (active) st(d_z, (row0 + tc + j) * sh.ld_z + d, y * dzf);
+        if (active) {
+          if (kRowAddr) st_row(d_z + (row0 + tc + j) * sh.ld_z, d, y * dzf);
+          else st(d_z, (row0 + tc + j) * sh.ld_z + d, y * dzf);
+        }
         wave_reduce_scatter<NS>(dC, lane);
         if ((lane & (kRep - 1)) == 0) red[buf][wave][j][NS + (lane >> (6 - kLogNS))] = dC[0];
       }
@@ -543,9 +571,14 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
         if (SOFTPLUS) ddl = dl[j] > 20.f ? ddl : ddl * (1.f - fast_exp2(-dl[j] * kLog2e));
         dD = fmaf(dy[j], uu[j], dD);
         if (active) {
-          const size_t i = (row0 + tc + j) * Di + d;
-          st(d_u, i, fmaf(Dd, dy[j], dl[j] * sgb));
-          st(d_delta, i, ddl);
+          const size_t r = (row0 + tc + j) * Di;
+          if (kRowAddr) {
+            st_row(d_u + r, d, fmaf(Dd, dy[j], dl[j] * sgb));
+            st_row(d_delta + r, d, ddl);
+          } else {
+            st(d_u, r + d, fmaf(Dd, dy[j], dl[j] * sgb));
+            st(d_delta, r + d, ddl);
+          }
         }
         wave_reduce_scatter<NS>(dB, lane);
         if ((lane & (kRep - 1)) == 0) red[buf][wave][j][lane >> (6 - kLogNS)] = dB[0];
