@@ -384,6 +384,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
   __shared__ float red[2][kBlock / kWave][kChunk][2 * NS];
   __shared__ float4 lds_ah[kLds > 0 ? kLds : 1][NS / 4][kBlock];
   __shared__ __align__(16) float bcs[2][kChunk][2 * NS];
+  __shared__ float red_sink[kBlock];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int d = blockIdx.x * kBlock + tid;
@@ -441,22 +442,22 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
 #pragma unroll
       for (int n = 0; n < NS; ++n) hg[n] = ckpt[(cc * NS + n) * Di + dc];
     }
+    // steps past a ragged chunk's end read its last step again (unused)
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      if (j < nv) {
-        if (kRowAddr) {
-          const size_t r = (row0 + tc + j) * Di;
-          dl[j] = ld_row(delta + r, dc);
-          uu[j] = ld_row(u + r, dc);
-          zr[j] = ld_row(z + (row0 + tc + j) * sh.ld_z, dc);
-          gr[j] = ld_row(dout + r, dc);
-        } else {
-          const size_t i = (row0 + tc + j) * Di + dc;
-          dl[j] = ld(delta, i);
-          uu[j] = ld(u, i);
-          zr[j] = ld(z, (row0 + tc + j) * sh.ld_z + dc);
-          gr[j] = ld(dout, i);
-        }
+      const size_t tj = row0 + tc + min(j, nv - 1);
+      if (kRowAddr) {
+        const size_t r = tj * Di;
+        dl[j] = ld_row(delta + r, dc);
+        uu[j] = ld_row(u + r, dc);
+        zr[j] = ld_row(z + tj * sh.ld_z, dc);
+        gr[j] = ld_row(dout + r, dc);
+      } else {
+        const size_t i = tj * Di + dc;
+        dl[j] = ld(delta, i);
+        uu[j] = ld(u, i);
+        zr[j] = ld(z, tj * sh.ld_z + dc);
+        gr[j] = ld(dout, i);
       }
     }
   };
@@ -526,9 +527,15 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
           else st(d_z, (row0 + tc + j) * sh.ld_z + d, y * dzf);
         }
         wave_reduce_scatter<NS>(dC, lane);
-        if ((lane & (kRep - 1)) == 0) red[buf][wave][j][NS + (lane >> (6 - kLogNS))] = dC[0];
+        // one lane of each group of kRep holds the sum; the others write to
+        // their own sink slot (an address select instead of a lane branch)
+        *((lane & (kRep - 1)) == 0 ? &red[buf][wave][j][NS + (lane >> (6 - kLogNS))] : &red_sink[tid]) = dC[0];
       }
     }
+    // The reverse walk reads B | C again rather than keeping the forward's
+    // values: without this compiler barrier they would be reused, live across
+    // the walks (8 steps x 2N registers).
+    asm volatile("" ::: "memory");
     // reverse: adjoint through the chunk
 #pragma unroll
     for (int j = kChunk - 1; j >= 0; --j) {
@@ -554,7 +561,11 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
 #pragma unroll
           for (int n = 0; n < NS; ++n) aj[n] = ah[j >= kLds ? j - kLds : 0][n];
         }
-        const float du = active ? dl[j] * uu[j] : 0.f;
+        // delta of the step, opaque to the compiler: a_t is recomputed here
+        // rather than kept from the forward walk (8 steps x N live registers)
+        float dlr = dl[j];
+        asm volatile("" : "+v"(dlr));
+        const float du = active ? dlr * uu[j] : 0.f;
         float sgb = 0.f, saw = 0.f;
         float dB[NS];
 #pragma unroll
@@ -565,7 +576,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
           dA[n] = fmaf(dl[j], w, dA[n]);
           sgb = fmaf(gn, Bv[n], sgb);
           dB[n] = gn * du;
-          g[n] = fast_exp2(dl[j] * A2[n]) * gn;
+          g[n] = fast_exp2(dlr * A2[n]) * gn;
         }
         float ddl = fmaf(saw, kLn2, uu[j] * sgb);
         if (SOFTPLUS) ddl = dl[j] > 20.f ? ddl : ddl * (1.f - fast_exp2(-dl[j] * kLog2e));
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
           }
         }
         wave_reduce_scatter<NS>(dB, lane);
-        if ((lane & (kRep - 1)) == 0) red[buf][wave][j][lane >> (6 - kLogNS)] = dB[0];
+        *((lane & (kRep - 1)) == 0 ? &red[buf][wave][j][lane >> (6 - kLogNS)] : &red_sink[tid]) = dB[0];
       }
     }
     if (GCK && c > c_first) load_chunk(c - 1);
