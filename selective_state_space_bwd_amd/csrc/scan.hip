@@ -264,18 +264,33 @@ __global__ __launch_bounds__(kBlock) void scan_gsum(const T* __restrict__ delta,
   const T* __restrict__ gb = dout + bo;
   const T* __restrict__ zb = z + (size_t)b * sh.T * sh.ld_z;
   const T* __restrict__ Cb = Cm + (size_t)b * sh.T * sh.ld_bc;
+  // bf16: each chunk's delta, d_out and z are loaded one chunk ahead (without
+  // it the kernel spent 78 % of its wave time waiting on these loads); float
+  // loads them at the chunk's start (its prefetch measured slower).  A ragged
+  // last chunk reads its last step again, with zero weight.
+  constexpr bool kPre = sizeof(T) == 2;
+  float ldl[kChunk], lgr[kChunk], lzz[kChunk];
+  const auto load = [&](int tc) {
+    const int nv = min(kChunk, t1 - tc);
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const unsigned tj = (unsigned)(tc + min(j, nv - 1));
+      ldl[j] = ld(db, tj * Di + d);
+      lgr[j] = ld(gb, tj * Di + d);
+      lzz[j] = ld(zb, tj * sh.ld_z + d);
+    }
+  };
+  if (kPre) load(t0);
   for (int tc = t0; tc < t1; tc += kChunk) {
     const int nv = min(kChunk, t1 - tc);
+    if (!kPre) load(tc);
     float dl[kChunk], dy[kChunk];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {  // a ragged last chunk reads its last step again, with zero weight
-      const unsigned tj = (unsigned)(tc + min(j, nv - 1));
-      dl[j] = ld(db, tj * Di + d);
-      dy[j] = ld(gb, tj * Di + d);
-      const float zz = ld(zb, tj * sh.ld_z + d);
-      dy[j] *= zz * sigmoid(zz);
-      if (j >= nv) dl[j] = dy[j] = 0.f;
+    for (int j = 0; j < kChunk; ++j) {
+      dl[j] = j < nv ? ldl[j] : 0.f;
+      dy[j] = j < nv ? lgr[j] * lzz[j] * sigmoid(lzz[j]) : 0.f;
     }
+    if (kPre && tc + kChunk < t1) load(tc + kChunk);
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       float Cv[NS];
@@ -766,7 +781,11 @@ long device_cus() {
 // (its float variant holds the next chunk's values in registers)
 long summary_blocks_per_cu(int dtype) { return dtype == SSM_F32 ? 2 : 3; }
 constexpr long kMainBlocksPerCU = 2;
-constexpr long kGsumBlocksPerCU = 7;  // the adjoint-only summary holds seven waves per SIMD
+// The adjoint-only summary holds seven waves per SIMD in float and five in bf16
+// (its prefetch registers); the model keeps seven for both, which picks the
+// measured best segment length on the mamba-2.8b shape (216 steps; five picks
+// 328, where the main sweep runs 3 % slower).
+constexpr long kGsumBlocksPerCU = 7;
 
 int check_dims(const ssm_dims* dm, int dtype) {
   if (!dm) return fail(SSM_ERR_INVALID_ARG, "dims is null");
