@@ -698,28 +698,83 @@ __global__ __launch_bounds__(kBlock) void scan_fwd_main(
 #pragma unroll
   for (int n = 0; n < NS; ++n) h[n] = (s == 0) ? 0.f : seg_h[(sg * NS + n) * Di + d];
   const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
-  for (int t = t0; t < t1; ++t) {
-    if (h_ckpt && t % ckpt_every == 0) {
-      const size_t k = (size_t)b * nckpt + t / ckpt_every;
+  if constexpr (sizeof(T) == 2) {
+    // bf16: one step at a time (the chunked, prefetching loop below measured
+    // 11 % slower here, while it takes float 15 % less time)
+    for (int t = t0; t < t1; ++t) {
+      if (h_ckpt && t % ckpt_every == 0) {
+        const size_t k = (size_t)b * nckpt + t / ckpt_every;
 #pragma unroll
-      for (int n = 0; n < NS; ++n) h_ckpt[(k * NS + n) * Di + d] = h[n];
-    }
-    const size_t i = (row0 + t) * Di + d;
-    const float dl = ld(delta, i), uu = ld(u, i);
-    float Bv[NS], Cv[NS];
-    load_row<NS>(Bm + (row0 + t) * sh.ld_bc, Bv);
-    load_row<NS>(Cm + (row0 + t) * sh.ld_bc, Cv);
-    const float du = dl * uu;
-    float yy = Dd * uu;
+        for (int n = 0; n < NS; ++n) h_ckpt[(k * NS + n) * Di + d] = h[n];
+      }
+      const size_t i = (row0 + t) * Di + d;
+      const float dl = ld(delta, i), uu = ld(u, i);
+      float Bv[NS], Cv[NS];
+      load_row<NS>(Bm + (row0 + t) * sh.ld_bc, Bv);
+      load_row<NS>(Cm + (row0 + t) * sh.ld_bc, Cv);
+      const float du = dl * uu;
+      float yy = Dd * uu;
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      h[n] = fmaf(fast_exp2(dl * A2[n]), h[n], du * Bv[n]);
-      yy = fmaf(Cv[n], h[n], yy);
+      for (int n = 0; n < NS; ++n) {
+        h[n] = fmaf(fast_exp2(dl * A2[n]), h[n], du * Bv[n]);
+        yy = fmaf(Cv[n], h[n], yy);
+      }
+      if (y) st(y, i, yy);
+      if (out) {
+        const float zz = ld(z, (row0 + t) * sh.ld_z + d);
+        st(out, i, yy * zz * sigmoid(zz));
+      }
     }
-    if (y) st(y, i, yy);
-    if (out) {
-      const float zz = ld(z, (row0 + t) * sh.ld_z + d);
-      st(out, i, yy * zz * sigmoid(zz));
+    return;
+  }
+  // float: steps go in chunks of kChunk whose delta, u (and z) are loaded one
+  // chunk ahead; a ragged last chunk reads its last step again for the unused
+  // slots.
+  float ndl[kChunk], nuu[kChunk], nzz[kChunk];
+  const auto load = [&](int tc) {
+    const int nv = min(kChunk, t1 - tc);
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const size_t tj = row0 + tc + min(j, nv - 1);
+      ndl[j] = ld(delta, tj * Di + d);
+      nuu[j] = ld(u, tj * Di + d);
+      if (out) nzz[j] = ld(z, tj * sh.ld_z + d);
+    }
+  };
+  if (t0 < t1) load(t0);
+  for (int tc = t0; tc < t1; tc += kChunk) {
+    const int nv = min(kChunk, t1 - tc);
+    float dl[kChunk], uu[kChunk], zz[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      dl[j] = ndl[j];
+      uu[j] = nuu[j];
+      zz[j] = out ? nzz[j] : 0.f;
+    }
+    if (tc + kChunk < t1) load(tc + kChunk);
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        const int t = tc + j;
+        if (h_ckpt && t % ckpt_every == 0) {
+          const size_t k = (size_t)b * nckpt + t / ckpt_every;
+#pragma unroll
+          for (int n = 0; n < NS; ++n) h_ckpt[(k * NS + n) * Di + d] = h[n];
+        }
+        const size_t i = (row0 + t) * Di + d;
+        float Bv[NS], Cv[NS];
+        load_row<NS>(Bm + (row0 + t) * sh.ld_bc, Bv);
+        load_row<NS>(Cm + (row0 + t) * sh.ld_bc, Cv);
+        const float du = dl[j] * uu[j];
+        float yy = Dd * uu[j];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          h[n] = fmaf(fast_exp2(dl[j] * A2[n]), h[n], du * Bv[n]);
+          yy = fmaf(Cv[n], h[n], yy);
+        }
+        if (y) st(y, i, yy);
+        if (out) st(out, i, yy * zz[j] * sigmoid(zz[j]));
+      }
     }
   }
 }
