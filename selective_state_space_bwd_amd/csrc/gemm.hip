@@ -204,7 +204,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Blocks go to the 8 XCDs round-robin by linear id, and each XCD has its own
+  // L2: when the tile count allows, XCD x takes the x-th contiguous run of
+  // tiles (row-major, column tiles fastest), so the blocks that share a row
+  // tile of A run on one XCD.
+  const int gx = gridDim.x, ntile = gx * gridDim.y;
+  const int pid = blockIdx.y * gx + blockIdx.x;
+  const int tile = (ntile % 8 == 0) ? (pid % 8) * (ntile / 8) + pid / 8 : pid;
+  const int m0 = (tile / gx) * BM, n0 = (tile % gx) * BN;
   const int kb = blockIdx.z * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
   const int nk = (ke - kb + kBK - 1) / kBK;
