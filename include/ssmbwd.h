@@ -13,7 +13,8 @@
  *  - Memory: all tensor pointers are DEVICE pointers to contiguous row-major
  *    storage owned by the caller.  The library never allocates or frees device
  *    memory; scratch space is a caller-provided workspace whose size the
- *    matching *_workspace_size() call returns.  Gradients are overwritten
+ *    matching *_workspace_size() call returns, at a 256-byte aligned address
+ *    (hipMalloc's alignment).  Gradients are overwritten
  *    unless the call's flags include SSM_BWD_ACCUMULATE (ssm_bwd_flags).
  *  - Storage dtype: [batch, seqlen, *] activations and their gradients are
  *    SSM_F32 (float) or SSM_BF16 (bfloat16, round-to-nearest-even on store).
@@ -45,7 +46,7 @@ typedef enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent stride */
   SSM_ERR_UNSUPPORTED = 2,  /* e.g. d_state outside {4, 8, 16}, misaligned bf16 rows */
-  SSM_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
+  SSM_ERR_WORKSPACE = 3,    /* workspace pointer null, smaller than required or not 256-byte aligned */
   SSM_ERR_LAUNCH = 4        /* a kernel launch failed */
 } ssm_status;
 

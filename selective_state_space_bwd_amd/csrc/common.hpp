@@ -141,6 +141,8 @@ int check_launch(const char* what);
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// workspaces are carved into 256-byte aligned regions from an aligned base
+inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 // ---- launchers shared between translation units (arguments already checked) --
 // gemm.hip: C = opA * opB on bf16 operands (k contiguous or strided per operand)

@@ -315,9 +315,30 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
     }
 }
 
+// Four consecutive outputs of a row per thread (N a multiple of 4: one 16-byte
+// load per split), summed over the splits in split order.
 template <typename OutT>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, OutT* __restrict__ C,
                                                      long long ldc, int M, int N, int splits, int accumulate) {
+  const long long idx = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+  const long long plane = (long long)M * N;
+  if (idx >= plane) return;
+  const int row = (int)(idx / N), col = (int)(idx - (long long)row * N);
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float4 t = *reinterpret_cast<const float4*>(part + s * plane + idx);
+    a[0] += t.x; a[1] += t.y; a[2] += t.z; a[3] += t.w;
+  }
+  OutT* c = C + (long long)row * ldc + col;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = from_f32<OutT>((accumulate ? to_f32(c[e]) : 0.f) + a[e]);
+}
+
+// the same for any N, one output per thread
+template <typename OutT>
+__global__ __launch_bounds__(256) void splitk_reduce1(const float* __restrict__ part, OutT* __restrict__ C,
+                                                      long long ldc, int M, int N, int splits, int accumulate) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)M * N) return;
   const int row = (int)(idx / N), col = (int)(idx - (long long)row * N);
@@ -436,8 +457,12 @@ int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) 
     hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT, 128, 128>), grid, dim3(kGemmThreads), 0, st, g);
   if (nsplit > 1) {
     const long long n = (long long)g.M * g.N;
-    hipLaunchKernelGGL((splitk_reduce<OutT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
-                       static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
+    if (g.N % 4 == 0)  // partial rows are N floats from a 256-byte aligned workspace: 16-byte loads
+      hipLaunchKernelGGL((splitk_reduce<OutT>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, partial,
+                         static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
+    else
+      hipLaunchKernelGGL((splitk_reduce1<OutT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
+                         static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
   }
   return SSM_OK;
 }
@@ -457,7 +482,8 @@ int gemm_check(const void* A, long long lda, const void* B, long long ldb, const
   if (!aligned16(A) || !aligned16(B) || (lda & 7) || (ldb & 7))
     return fail(SSM_ERR_UNSUPPORTED, "gemm: operands must be 16-byte aligned with row strides multiple of 8");
   const size_t need = K > 0 ? gemm_workspace_bytes(M, N, K) : 0;
-  if (need && (!workspace || ws_bytes < need)) return fail(SSM_ERR_WORKSPACE, "gemm: workspace too small for split-k");
+  if (need && (!workspace || ws_bytes < need || !aligned256(workspace)))
+    return fail(SSM_ERR_WORKSPACE, "gemm: workspace for split-k missing, too small or not 256-byte aligned");
   return SSM_OK;
 }
 
@@ -538,8 +564,8 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   if (dX && (rc = gemm_check(dY, lddy, W, K, dX, m, K, N, ws_bytes, workspace)) != SSM_OK) return rc;
   // dW[N, K] = dY^T X: A(i = n, k = m) = dY[m * lddy + n], B(k = m, j) = X[m * ldx + j]
   if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
-  if (db && (!workspace || ws_bytes < column_sum_workspace_bytes(m, N)))
-    return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace too small for the bias sums");
+  if (db && (!workspace || ws_bytes < column_sum_workspace_bytes(m, N) || !aligned256(workspace)))
+    return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the bias sums missing, too small or not 256-byte aligned");
   if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, acc_x, workspace, st);
   if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, acc_w, workspace, st);
   if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, acc_w, workspace, st);

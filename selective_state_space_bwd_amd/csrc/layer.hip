@@ -176,8 +176,9 @@ extern "C" int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* 
   const ssm_layer_dims& d = *dims;
   size_t need = 0;
   const FwdBufs b = carve_fwd(d, workspace, &need);
-  if (!workspace || ws_bytes < need)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!workspace || ws_bytes < need || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t M = (int64_t)d.batch * d.seqlen;
   const int dm = d.d_model, di = d.d_inner, R = d.dt_rank, N = d.d_state, R2 = R + 2 * N;
@@ -228,8 +229,9 @@ extern "C" int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, 
   const ssm_layer_dims& d = *dims;
   size_t need = 0;
   const BwdBufs b = carve_bwd(d, workspace, &need);
-  if (!workspace || ws_bytes < need)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!workspace || ws_bytes < need || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t M = (int64_t)d.batch * d.seqlen;
   const int dm = d.d_model, di = d.d_inner, R = d.dt_rank, N = d.d_state, R2 = R + 2 * N;
@@ -382,8 +384,9 @@ extern "C" int mamba_backbone_fwd(const void* inp, const void* W_ip, const float
   const int dm = bd.layer.d_model, L = bd.n_layers;
   const size_t kb = keep_bytes(bd);
   const size_t need = kb + backbone_fwd_scratch(bd);
-  if (!workspace || ws_bytes < need)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!workspace || ws_bytes < need || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   size_t unused = 0;
   const LayerKeep keep = carve_keep(bd.layer, workspace, &unused);   // used with SSM_KEEP_INPUTS only
   void* sc = static_cast<char*>(workspace) + kb;
@@ -427,8 +430,9 @@ extern "C" int mamba_backbone_bwd(const void* inp, const void* W_ip, const float
   const size_t grad = align_up((size_t)M * dm * 2);
   const size_t kb = keep_bytes(bd);
   const size_t need = 2 * grad + kb + backbone_bwd_scratch(bd);
-  if (!workspace || ws_bytes < need)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!workspace || ws_bytes < need || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   char* base = static_cast<char*>(workspace);
   void* dbuf[2] = {base, base + grad};
   size_t unused = 0;

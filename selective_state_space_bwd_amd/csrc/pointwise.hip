@@ -842,8 +842,9 @@ extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, cons
   }
   if (!x || !d_u || !d_x) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
   const size_t need = conv1d_bwd_workspace_size(batch, seqlen, d_inner, d_conv);
-  if (!workspace || ws_bytes < need)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!workspace || ws_bytes < need || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   float* part = static_cast<float*>(workspace);
   const int V = dtype == SSM_F32 ? 4 : 8;
   const bool vec = d_inner % V == 0 && ld_x % V == 0 && ld_du % V == 0 && ld_dx % V == 0 && aligned16(x) &&
@@ -900,8 +901,9 @@ extern "C" int rmsnorm_bwd(const void* x, const float* w, const void* dy, const 
   }
   if (!x || !w || !dy || !dx) return fail(SSM_ERR_INVALID_ARG, "a tensor pointer is null");
   const size_t need = rmsnorm_bwd_workspace_size(rows, dim);
-  if (!workspace || ws_bytes < need)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (!workspace || ws_bytes < need || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(workspace);
   int blocks = 0;

@@ -195,8 +195,9 @@ extern "C" int reverse_linear_scan(const void* a, const void* b, void* x, int ba
     return fail(SSM_ERR_INVALID_ARG, "batch %d x channels %d beyond the supported range", batch, channels);
   const RsShape sh = rs_plan(batch, seqlen, channels);
   const size_t need = rs_workspace(batch, sh, a != nullptr);
-  if (need && (!workspace || ws_bytes < need))
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, need);
+  if (need && (!workspace || ws_bytes < need || !aligned256(workspace)))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, need);
   float* V = static_cast<float*>(workspace);
   // decay products in the second half of the workspace when a is given
   float* Dp = (need && a) ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;

@@ -1036,8 +1036,9 @@ int run_bwd(const void* u, const void* delta, const float* A_log, const void* B,
   if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C) && aligned4(d_B) && aligned4(d_C)))
     return fail(SSM_ERR_UNSUPPORTED, "bf16 B, C, d_B and d_C must be 4-byte aligned");
   const Plan p = make_plan(dm, dtype, true, ckpt_given);
-  if (!workspace || ws_bytes < p.bytes)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
+  if (!workspace || ws_bytes < p.bytes || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, p.bytes);
   const ScanWs w = bind(p, workspace);
 #define SSM_BWD_CASE(TY, NSV)                                                                                    \
   return launch_bwd<TY, NSV>(u, delta, A_log, B, C, D, z, d_out, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z, \
@@ -1114,8 +1115,9 @@ extern "C" int ssm_scan_fwd(const void* u, const void* delta, const float* A_log
   if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C)))
     return fail(SSM_ERR_UNSUPPORTED, "bf16 B and C must be 4-byte aligned");
   const Plan p = make_plan(dm, dtype, false);
-  if (!workspace || ws_bytes < p.bytes)
-    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0, p.bytes);
+  if (!workspace || ws_bytes < p.bytes || !aligned256(workspace))
+    return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
+                workspace ? ws_bytes : 0, p.bytes);
   const ScanWs w = bind(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!h_ckpt) ckpt_every = 0;

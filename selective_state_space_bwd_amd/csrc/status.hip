@@ -36,7 +36,7 @@ extern "C" const char* ssm_status_string(int status) {
     case SSM_OK: return "ok";
     case SSM_ERR_INVALID_ARG: return "invalid argument";
     case SSM_ERR_UNSUPPORTED: return "unsupported configuration";
-    case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSM_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case SSM_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }

@@ -87,6 +87,26 @@ def test_bwd_ckpt_validates():
     assert _bwd_ckpt(_dims(), ws_bytes=16) == ssm.SSM_ERR_WORKSPACE
 
 
+MISALIGNED = ctypes.c_void_p(0x1000 + 64)  # 64-byte aligned, not 256
+
+
+def test_workspace_must_be_256_byte_aligned():
+    assert _bwd(_dims(), ws=MISALIGNED) == ssm.SSM_ERR_WORKSPACE
+    assert _bwd_ckpt(_dims(), ws=MISALIGNED) == ssm.SSM_ERR_WORKSPACE
+    assert L.ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, MISALIGNED, 1 << 40,
+                          ctypes.byref(_dims()), 0, None) == ssm.SSM_ERR_WORKSPACE
+    assert L.reverse_linear_scan(FAKE, FAKE, FAKE, 2, 4096, 64, 0, MISALIGNED, 1 << 30, 0,
+                                 None) == ssm.SSM_ERR_WORKSPACE
+    assert L.conv1d_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 4, 4, 4, 4, 0, MISALIGNED, 1 << 30, 0,
+                        None) == ssm.SSM_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 64, ctypes.c_float(1e-5), 0, MISALIGNED, 1 << 30,
+                         0, None) == ssm.SSM_ERR_WORKSPACE
+    # split-k product (dt_proj shape): its partial sums need the aligned workspace
+    assert L.linear_bwd(FAKE, 96, FAKE, FAKE, 3072, None, 0, 0, FAKE, None, 16384, 96, 3072, MISALIGNED, 1 << 40,
+                        1, None) == ssm.SSM_ERR_WORKSPACE
+    assert L.ssm_status_string(ssm.SSM_ERR_WORKSPACE).decode().endswith("misaligned")
+
+
 def test_other_entry_points_validate():
     assert L.gating_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 0, None) == ssm.SSM_ERR_INVALID_ARG
     assert L.gating_bwd(None, FAKE, FAKE, FAKE, FAKE, 10, 0, None) == ssm.SSM_ERR_INVALID_ARG
