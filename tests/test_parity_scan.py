@@ -207,19 +207,25 @@ def test_empty_inputs(nb, T):
     assert g["d_u"].numel() == 0
 
 
+# (seqlen, ckpt_every, seg_len): whole chunks; a ragged last chunk in the last
+# segment with the layer's ckpt_every; a single short segment
+FWD_CASES = [(200, 16, 24), (203, 8, 24), (37, 8, 0)]
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_forward_outputs_and_checkpoints(dt):
-    nb, T, di, N = 2, 200, 72, 16
+@pytest.mark.parametrize("T,ce,seg", FWD_CASES, ids=[f"T{c[0]}-ck{c[1]}-seg{c[2]}" for c in FWD_CASES])
+def test_forward_outputs_and_checkpoints(dt, T, ce, seg):
+    nb, di, N = 2, 72, 16
     p = _random_params(scan_inputs(nb, T, di, N, dt, seed=41, variant="long_memory"), 5)
     t = _to_dev(p, dt)
-    print(f"case: ssm_scan_fwd B{nb} T{T} Di{di} N{N} {dt} ckpt_every 16 seg_len 24", flush=True)
-    f = _ssm().ssm_scan_fwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], ckpt_every=16,
-                            seg_len=24)
+    print(f"case: ssm_scan_fwd B{nb} T{T} Di{di} N{N} {dt} ckpt_every {ce} seg_len {seg}", flush=True)
+    f = _ssm().ssm_scan_fwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], ckpt_every=ce,
+                            seg_len=seg)
     torch.cuda.synchronize()
     y, out = orc.ssm_forward(p["u"], p["delta"], p["A_log"], p["B"], p["C"], p["D"], p["z"])
     assert norm_err(_np(f["y"]), y) < TOL[dt]
     assert norm_err(_np(f["out"]), out) < TOL[dt]
-    steps = [k * 16 - 1 for k in range(1, (T + 15) // 16)]
+    steps = [k * ce - 1 for k in range(1, (T + ce - 1) // ce)]
     hs = orc.ssm_states_at(p["u"], p["delta"], p["A_log"], p["B"], steps)      # [B, K-1, N, Di]
     ck = _np(f["h_ckpt"])
     assert np.all(ck[:, 0] == 0)
