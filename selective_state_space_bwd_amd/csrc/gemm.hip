@@ -39,7 +39,7 @@ struct GemmArgs {
   long long lda, ldb, ldc;
   int M, N, K;
   int k_per_split;  // multiple of kBK
-  int accumulate;   // add into C instead of overwriting (single split only)
+  int accumulate;   // add into C instead of overwriting (the split-k sum adds it)
   int vec_out;      // C rows allow 16-byte vectors (aligned base, ldc a multiple of the vector)
 };
 
@@ -189,30 +189,36 @@ __device__ __forceinline__ void write_row16(T* __restrict__ rowp, int col, int n
   }
 }
 
+// LDS elements of one product's double-buffered A and B tiles; after the k loop
+// the same space stages the output tiles (4 waves x 32 rows x kStageLd floats)
+template <bool A_K, bool B_K, int BM, int BN>
+constexpr int gemm_lds_elems() {
+  return 2 * (OperandTile<A_K, BM>::kElems + OperandTile<B_K, BN>::kElems);
+}
+
+// Blocks go to the 8 XCDs round-robin by linear id, and each XCD has its own L2:
+// when a product's tile count allows, XCD x takes the x-th contiguous run of its
+// tiles (row-major, column tiles fastest), so the blocks that share a row tile
+// of A run on one XCD.  pid: the block's index among the product's gx x gy
+// tiles (of one k split); the caller's linear ids keep pid % 8 = XCD.
+__device__ __forceinline__ int xcd_tile(int pid, int ntile) {
+  return (ntile % 8 == 0) ? (pid % 8) * (ntile / 8) + pid / 8 : pid;
+}
+
+// One output tile of C at rows m0.., columns n0.., over k split `split`.
 template <bool A_K, bool B_K, typename OutT, int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, int split, uint16_t* __restrict__ lds) {
   using TA = OperandTile<A_K, BM>;
   using TB = OperandTile<B_K, BN>;
   constexpr int TM = BM / 64, TN = BN / 64;  // 32 x 32 tiles per wave
-  // double-buffered A and B tiles; after the k loop the same space stages the
-  // output tiles (4 waves x 32 rows x kStageLd floats)
-  constexpr int kLdsElems = 2 * (TA::kElems + TB::kElems);
-  static_assert(4 * 32 * kStageLd * 2 <= kLdsElems, "epilogue staging must fit in the tile buffers");
-  __shared__ __align__(16) uint16_t lds[kLdsElems];
+  static_assert(4 * 32 * kStageLd * 2 <= gemm_lds_elems<A_K, B_K, BM, BN>(),
+                "epilogue staging must fit in the tile buffers");
   uint16_t(*lds_a)[TA::kElems] = reinterpret_cast<uint16_t(*)[TA::kElems]>(lds);
   uint16_t(*lds_b)[TB::kElems] = reinterpret_cast<uint16_t(*)[TB::kElems]>(lds + 2 * TA::kElems);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  // Blocks go to the 8 XCDs round-robin by linear id, and each XCD has its own
-  // L2: when the tile count allows, XCD x takes the x-th contiguous run of
-  // tiles (row-major, column tiles fastest), so the blocks that share a row
-  // tile of A run on one XCD.
-  const int gx = gridDim.x, ntile = gx * gridDim.y;
-  const int pid = blockIdx.y * gx + blockIdx.x;
-  const int tile = (ntile % 8 == 0) ? (pid % 8) * (ntile / 8) + pid / 8 : pid;
-  const int m0 = (tile / gx) * BM, n0 = (tile % gx) * BN;
-  const int kb = blockIdx.z * g.k_per_split;
+  const int kb = split * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
   const int nk = (ke - kb + kBK - 1) / kBK;
 
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
   // + 15, written (or read, added and written) as 16-byte vectors.
   // the k loop ended with a barrier: no wave reads the tile buffers any more
   float(*stage)[32][kStageLd] = reinterpret_cast<float(*)[32][kStageLd]>(lds);
-  float* out_f = g.partial ? g.partial + (long long)blockIdx.z * g.M * g.N : nullptr;
+  float* out_f = g.partial ? g.partial + (long long)split * g.M * g.N : nullptr;
   const long long ldo = g.partial ? g.N : g.ldc;
   const bool vec_ok = g.partial ? (g.N % 4 == 0) : g.vec_out;
 #pragma unroll
@@ -313,6 +319,35 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) 
         write_row16<OutT>(static_cast<OutT*>(g.C) + (long long)row * ldo, col, g.N, v, g.accumulate != 0, vec_ok);
       }
     }
+}
+
+// grid (column tiles, row tiles, k splits)
+template <bool A_K, bool B_K, typename OutT, int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __align__(16) uint16_t lds[gemm_lds_elems<A_K, B_K, BM, BN>()];
+  const int gx = gridDim.x;
+  const int tile = xcd_tile(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
+  gemm_tile<A_K, B_K, OutT, BM, BN>(g, (tile / gx) * BM, (tile % gx) * BN, blockIdx.z, lds);
+}
+
+// Two independent products in one launch (a linear layer's dX and dW): blocks
+// [0, nb1) take product 1's tiles (one k split), the rest product 2's tiles
+// over its k splits, so the last round of one product's blocks shares the chip
+// with the other's instead of leaving CUs idle.  Both use BM x 128 tiles.
+template <bool A1, bool B1, typename O1, bool A2, bool B2, typename O2, int BM>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_pair_kernel(GemmArgs g1, GemmArgs g2, int gx1, int nb1,
+                                                                    int gx2, int nt2) {
+  constexpr int L1 = gemm_lds_elems<A1, B1, BM, 128>(), L2 = gemm_lds_elems<A2, B2, BM, 128>();
+  __shared__ __align__(16) uint16_t lds[L1 > L2 ? L1 : L2];
+  const int id = blockIdx.x;
+  if (id < nb1) {
+    const int tile = xcd_tile(id, nb1);
+    gemm_tile<A1, B1, O1, BM, 128>(g1, (tile / gx1) * BM, (tile % gx1) * 128, 0, lds);
+  } else {
+    const int local = id - nb1, split = local / nt2;
+    const int tile = xcd_tile(local - split * nt2, nt2);
+    gemm_tile<A2, B2, O2, BM, 128>(g2, (tile / gx2) * BM, (tile % gx2) * 128, split, lds);
+  }
 }
 
 // Four consecutive outputs of a row per thread (N a multiple of 4: one 16-byte
@@ -442,28 +477,39 @@ TilePick pick_tiles(int M, int N, int K) {
 int pick_bm(int M, int N, int K) { return pick_tiles(M, N, K).bm; }
 int pick_splits(int M, int N, int K) { return K > 0 ? pick_tiles(M, N, K).splits : 1; }
 
-template <bool A_K, bool B_K, typename OutT>
-int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) {
-  GemmArgs g = g0;
+// k range per split (a multiple of kBK) and the partial buffer; returns the
+// number of splits that get k
+int gemm_prep(GemmArgs& g, int splits, float* partial) {
   const int ksplit = max(kBK, ((g.K + splits - 1) / splits + kBK - 1) / kBK * kBK);
   g.k_per_split = ksplit;
   const int nsplit = (g.K + ksplit - 1) / ksplit;
+  g.partial = nsplit > 1 ? partial : nullptr;
+  return nsplit;
+}
+
+template <typename OutT>
+void gemm_reduce(const GemmArgs& g, int nsplit, float* partial, hipStream_t st) {
+  if (nsplit <= 1) return;
+  const long long n = (long long)g.M * g.N;
+  if (g.N % 4 == 0)  // partial rows are N floats from a 256-byte aligned workspace: 16-byte loads
+    hipLaunchKernelGGL((splitk_reduce<OutT>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, partial,
+                       static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
+  else
+    hipLaunchKernelGGL((splitk_reduce1<OutT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
+                       static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
+}
+
+template <bool A_K, bool B_K, typename OutT>
+int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) {
+  GemmArgs g = g0;
+  const int nsplit = gemm_prep(g, splits, partial);
   const int bm = pick_bm(g.M, g.N, g.K);
   dim3 grid((g.N + 127) / 128, (g.M + bm - 1) / bm, nsplit);
-  g.partial = nsplit > 1 ? partial : nullptr;
   if (bm == 256)
     hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT, 256, 128>), grid, dim3(kGemmThreads), 0, st, g);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT, 128, 128>), grid, dim3(kGemmThreads), 0, st, g);
-  if (nsplit > 1) {
-    const long long n = (long long)g.M * g.N;
-    if (g.N % 4 == 0)  // partial rows are N floats from a 256-byte aligned workspace: 16-byte loads
-      hipLaunchKernelGGL((splitk_reduce<OutT>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, partial,
-                         static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
-    else
-      hipLaunchKernelGGL((splitk_reduce1<OutT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial,
-                         static_cast<OutT*>(g.C), g.ldc, g.M, g.N, nsplit, g.accumulate);
-  }
+  gemm_reduce<OutT>(g, nsplit, partial, st);
   return SSM_OK;
 }
 
@@ -510,6 +556,105 @@ int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool 
   return fail(SSM_ERR_INVALID_ARG, "gemm: layout");
 }
 
+// Finish time, in k steps, of n1 blocks of d1 k steps followed by n2 blocks of d2
+// on `slots` block slots, each block starting on the earliest free slot in
+// launch order (the dispatcher's order).  Slots that free together stay one
+// group, so the walk takes a few steps per round.
+double pair_makespan(long slots, long n1, double d1, long n2, double d2) {
+  struct Group { double t; long n; };
+  Group g[64];
+  int ng = 1;
+  g[0] = Group{0.0, slots};
+  double end = 0.0;
+  long left[2] = {n1, n2};
+  const double dur[2] = {d1, d2};
+  for (int p = 0; p < 2; ++p) {
+    while (left[p] > 0) {
+      int e = 0;  // earliest free group
+      for (int i = 1; i < ng; ++i)
+        if (g[i].t < g[e].t) e = i;
+      const long take = left[p] < g[e].n ? left[p] : g[e].n;
+      const double t = g[e].t + dur[p];
+      end = t > end ? t : end;
+      left[p] -= take;
+      g[e].n -= take;
+      if (g[e].n == 0) g[e] = g[--ng];
+      int m = -1;
+      for (int i = 0; i < ng; ++i)
+        if (g[i].t == t) m = i;
+      if (m >= 0) g[m].n += take;
+      else if (ng < 64) g[ng++] = Group{t, take};
+      else return -1.0;  // cannot happen for the shapes here (groups stay few)
+    }
+  }
+  return end;
+}
+
+// dW's k split in the paired launch of linear_bwd_products (0: the products are
+// not paired), for an m x N output gradient and an N x K weight.  The products
+// pair when dX needs no k split and both pick the same tile height; the split
+// is then picked for the two products' blocks together: the modelled finish
+// time of the block schedule (a k step per block costing the same in both, 8
+// k steps of set-up per block, the tile rate of the single-product model) plus
+// the split-k partial traffic.
+int pair_dw_splits(int m, int K, int N) {
+  const int bm = pick_bm(m, K, N);
+  if (pick_splits(m, K, N) != 1 || pick_bm(N, K, m) != bm) return 0;
+  const int gx = (K + 127) / 128;
+  const long nb1 = (long)gx * ((m + bm - 1) / bm), nt2 = (long)gx * ((N + bm - 1) / bm);
+  const long slots = gemm_device_cus() * (bm == 256 ? 2 : 3);
+  const double kstep_s = (double)bm * 128 * kBK * 2 / ((bm == 256 ? 650e12 : 500e12) / slots);
+  int best = pick_splits(N, K, m);
+  double best_t = -1.0;
+  for (int sp : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
+    if (sp > 1 && m / sp < 4 * kBK) break;
+    const int ks = ((m + sp - 1) / sp + kBK - 1) / kBK * kBK;
+    const int used = (m + ks - 1) / ks;
+    const double ms = pair_makespan(slots, nb1, (N + kBK - 1) / kBK + 8.0, nt2 * used, ks / kBK + 8.0);
+    if (ms < 0) continue;
+    double t = ms * kstep_s;
+    if (used > 1) t += 2.0 * used * (double)N * K * 4.0 / 3e12;
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+// dX[M, K] = dY W and dW[N, K] = dY^T X of one linear layer: one launch for both
+// when pair_dw_splits allows (dW's split-k partials then own the workspace),
+// otherwise one launch each.
+void linear_bwd_products(const void* X, long long ldx, const void* W, const void* dY, long long lddy, void* dX,
+                         long long lddx, float* dW, int m, int K, int N, int acc_x, int acc_w, void* workspace,
+                         hipStream_t st) {
+  const int s2 = (dX && dW) ? pair_dw_splits(m, K, N) : 0;
+  if (s2 == 0) {
+    if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, acc_x, workspace, st);
+    if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, acc_w, workspace, st);
+    return;
+  }
+  const int bm = pick_bm(m, K, N);
+  const uint16_t* y16 = static_cast<const uint16_t*>(dY);
+  GemmArgs g1{y16, static_cast<const uint16_t*>(W), dX, nullptr, lddy, K, lddx, m, K, N, 0, acc_x,
+              aligned16(dX) && lddx % 8 == 0};
+  GemmArgs g2{y16, static_cast<const uint16_t*>(X), dW, nullptr, lddy, ldx, K, N, K, m, 0, acc_w,
+              aligned16(dW) && K % 4 == 0};
+  float* part = static_cast<float*>(workspace);
+  gemm_prep(g1, 1, nullptr);
+  const int nsplit2 = gemm_prep(g2, s2, part);
+  const int gx = (K + 127) / 128;
+  const int nb1 = gx * ((m + bm - 1) / bm), nt2 = gx * ((N + bm - 1) / bm);
+  const dim3 grid((unsigned)(nb1 + nt2 * nsplit2));
+  if (bm == 256)
+    hipLaunchKernelGGL((gemm_pair_kernel<true, false, bf16, false, false, float, 256>), grid, dim3(kGemmThreads), 0,
+                       st, g1, g2, gx, nb1, gx, nt2);
+  else
+    hipLaunchKernelGGL((gemm_pair_kernel<true, false, bf16, false, false, float, 128>), grid, dim3(kGemmThreads), 0,
+                       st, g1, g2, gx, nb1, gx, nt2);
+  gemm_reduce<float>(g2, nsplit2, part, st);
+}
+
 size_t column_sum_workspace_bytes(int M, int N) {
   return align_up((size_t)((M + kColRows - 1) / kColRows) * N * sizeof(float));
 }
@@ -536,7 +681,12 @@ extern "C" size_t linear_bwd_workspace_size(int64_t M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0 || M >= (1LL << 31)) return 0;
   // dX = dY W (M x K, reduction N), dW = dY^T X (N x K, reduction M) and the db
   // column sums run one after another and share the space
-  const size_t a = gemm_workspace_bytes((int)M, K, N), b = gemm_workspace_bytes(N, K, (int)M);
+  size_t a = gemm_workspace_bytes((int)M, K, N), b = gemm_workspace_bytes(N, K, (int)M);
+  const int s2 = pair_dw_splits((int)M, K, N);  // dW's split when paired with dX
+  if (s2 > 1) {
+    const size_t bp = align_up((size_t)s2 * N * K * sizeof(float));
+    b = bp > b ? bp : b;
+  }
   const size_t c = column_sum_workspace_bytes((int)M, N);
   return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
@@ -564,10 +714,15 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   if (dX && (rc = gemm_check(dY, lddy, W, K, dX, m, K, N, ws_bytes, workspace)) != SSM_OK) return rc;
   // dW[N, K] = dY^T X: A(i = n, k = m) = dY[m * lddy + n], B(k = m, j) = X[m * ldx + j]
   if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
+  if (dX && dW) {  // dX and dW in one launch: dW's split-k partials for the paired split
+    const int s2 = pair_dw_splits(m, K, N);
+    if (s2 > 1 && (!workspace || ws_bytes < align_up((size_t)s2 * N * K * sizeof(float)) || !aligned256(workspace)))
+      return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the split-k partials missing, too small or not "
+                                     "256-byte aligned");
+  }
   if (db && (!workspace || ws_bytes < column_sum_workspace_bytes(m, N) || !aligned256(workspace)))
     return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the bias sums missing, too small or not 256-byte aligned");
-  if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, acc_x, workspace, st);
-  if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, acc_w, workspace, st);
+  linear_bwd_products(X, ldx, W, dY, lddy, dX, lddx, dW, m, K, N, acc_x, acc_w, workspace, st);
   if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, acc_w, workspace, st);
   return check_launch("linear_bwd");
 }
