@@ -443,21 +443,32 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_wave(const T* __restrict
   }
   const float inv_dim = 1.f / (float)dim;
   const int64_t r0 = (int64_t)blockIdx.x * 4 * kRmsFwdWaveRows, r1 = min(rows, r0 + 4 * kRmsFwdWaveRows);
-  for (int64_t r = r0 + wave; r < r1; r += 4) {
+  // all of the wave's rows are loaded (as raw 16-byte words) before the first
+  // is reduced, so their memory latencies overlap
+  uint4 raw[kRmsFwdWaveRows][J];
+#pragma unroll
+  for (int q = 0; q < kRmsFwdWaveRows; ++q) {
+    const int64_t r = r0 + wave + 4 * q;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      raw[q][j] = (r < r1 && lane + kWave * j < nvec)
+                      ? *reinterpret_cast<const uint4*>(x + r * dim + (lane + kWave * j) * V)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int q = 0; q < kRmsFwdWaveRows; ++q) {
+    const int64_t r = r0 + wave + 4 * q;
+    if (r >= r1) break;
     Vec16<T> xv[J];
-    float ss = 0.f;
+    float ss[1] = {0.f};
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (lane + kWave * j < nvec) {
-        xv[j].load(x + r * dim + (lane + kWave * j) * V);
-      } else {
+      xv[j].set(raw[q][j]);
 #pragma unroll
-        for (int i = 0; i < V; ++i) xv[j].v[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < V; ++i) ss = fmaf(xv[j].v[i], xv[j].v[i], ss);
+      for (int i = 0; i < V; ++i) ss[0] = fmaf(xv[j].v[i], xv[j].v[i], ss[0]);
     }
-    const float inv_r = 1.f / sqrtf(wave_sum(ss) * inv_dim + eps);
+    wave_reduce_scatter<1>(ss, lane);  // the row's sum of squares in every lane
+    const float inv_r = 1.f / sqrtf(ss[0] * inv_dim + eps);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (lane + kWave * j < nvec) {
