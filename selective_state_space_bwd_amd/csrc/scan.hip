@@ -157,25 +157,38 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
       r.gr[j] = ld(gb, tj * Di + dc);
     }
   };
-  __shared__ __align__(16) float bcs[2][kChunk][2 * NS];
-  const int tid = threadIdx.x;
+  // Each wave stages its own copy of the chunk's B | C rows (kBcPer elements
+  // per lane), so no block barrier is needed: one wave's LDS accesses take
+  // effect in program order, and the fences around a wave barrier keep the
+  // compiler from moving the reads of the next chunk's rows above their stores.
+  constexpr int kBcPer = kChunk * 2 * NS / kWave;
+  __shared__ __align__(16) float bcs[kBlock / kWave][kChunk][2 * NS];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  float* const mybc = &bcs[wave][0][0];
+  const auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   Raw cur;
   load_du(t0, cur);
   if (kPipe) {
     if (need_g) load_zg(t0, cur);
-    if (tid < kChunk * 2 * NS)
-      (&bcs[0][0][0])[tid] = bc_element<T, NS>(Bb, Cb, sh.ld_bc, t0, min(kChunk, t1 - t0), tid);
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kBcPer; ++q)
+      mybc[lane + kWave * q] = bc_element<T, NS>(Bb, Cb, sh.ld_bc, t0, min(kChunk, t1 - t0), lane + kWave * q);
+    wave_sync();
   }
-  int buf = 0;
-  for (int tc = t0; tc < t1; tc += kChunk, buf ^= 1) {
+  for (int tc = t0; tc < t1; tc += kChunk) {
     const bool more = tc + kChunk < t1;
     Raw nxt;
-    float bc_next = 0.f;
+    float bc_next[kBcPer];
     if (more) load_du(tc + kChunk, nxt);
     if (kPipe && more) {
       if (need_g) load_zg(tc + kChunk, nxt);
-      bc_next = bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc + kChunk, min(kChunk, t1 - tc - kChunk), tid);
+#pragma unroll
+      for (int q = 0; q < kBcPer; ++q)
+        bc_next[q] = bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc + kChunk, min(kChunk, t1 - tc - kChunk), lane + kWave * q);
     }
     if (BWD && tc > t0 && active) {
       const size_t c = (size_t)b * sh.nchunk + tc / kChunk;
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
       const float dlj = ok ? cur.dl[j] : 0.f;
       float Bv[NS], Cv[NS];
       if (kPipe) {
-        bc_row<NS>(bcs[buf], j, Bv, Cv);
+        bc_row<NS>(bcs[wave], j, Bv, Cv);
       } else {
         const size_t row = (size_t)(tc + min(j, nv - 1)) * sh.ld_bc;
         load_row<NS>(Bb + row, Bv);
@@ -214,10 +227,12 @@ __global__ __launch_bounds__(kBlock) void scan_summary(
       sd += dlj;
     }
     if (kPipe) {
-      // the buffer written here was last read before the previous chunk's barrier
-      if (more && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
-      __syncthreads();
-      if (more) cur = nxt;
+      if (more) {
+#pragma unroll
+        for (int q = 0; q < kBcPer; ++q) mybc[lane + kWave * q] = bc_next[q];
+        wave_sync();
+        cur = nxt;
+      }
     } else if (more) {
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
