@@ -584,7 +584,7 @@ double pair_makespan(long slots, long n1, double d1, long n2, double d2) {
         if (g[i].t == t) m = i;
       if (m >= 0) g[m].n += take;
       else if (ng < 64) g[ng++] = Group{t, take};
-      else return -1.0;  // cannot happen for the shapes here (groups stay few)
+      else return -1.0;  // more than 64 distinct free times: the caller skips this split
     }
   }
   return end;
