@@ -183,7 +183,7 @@ def timed(step, n_events: int, steps: int, warmup: int):
     torch.cuda.synchronize()
     hip = HipEvents()
     every = max(1, steps // STAGE_SAMPLES)
-    sampled = [k for k in range(steps) if k % every == 0][:STAGE_SAMPLES]
+    sampled = [k for k in range(steps) if k % every == every - 1][:STAGE_SAMPLES]
     evs = {k: hip.create(n_events) for k in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
