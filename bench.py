@@ -196,25 +196,6 @@ def timed(step, n_events: int, steps: int, warmup: int):
     return elapsed / steps * 1e3, stages
 
 
-def cold_cache_ms(step, reps: int = 4) -> float:
-    """Step time with the 256 MB Infinity Cache cleared first: after the timed
-    region, each of `reps` further steps follows a 1 GiB buffer write and is
-    timed alone by events on torch's current stream (the library's stream)."""
-    import torch
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
-    times = []
-    for _ in range(reps):
-        scratch.fill_(1.0)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        step(None)
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    del scratch
-    return float(np.mean(times))
-
-
 def run_scan(args, cfg):
     import torch
 
@@ -248,7 +229,6 @@ def run_scan(args, cfg):
                              out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
 
     ms_step, stages = timed(step, 5, args.steps, args.warmup)
-    cold_ms = cold_cache_ms(step)
     se = cfg.state_elements
     el = 4 if cfg.dtype == "f32" else 2
     rows = cfg.batch * cfg.seqlen
@@ -282,7 +262,6 @@ def run_scan(args, cfg):
                    "chunk_states": "given by the forward" if args.ckpt else "rebuilt"},
         "hbm": {"algorithmic_bytes": alg_bytes, "effective_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "cold_cache_ms_per_step": round(cold_ms, 4),
         "stages_ms": {"summary": round(float(stages[:, 0].mean()), 4), "carry": round(float(stages[:, 1].mean()), 4),
                       "main": round(main_ms, 4), "finalize": round(float(stages[:, 3].mean()), 4)},
         "roofline": roof,
