@@ -101,6 +101,23 @@ def test_linear_bwd_3d_and_skips():
     assert norm_err(_np(dW2), rw) < TOL_F32
 
 
+@pytest.mark.parametrize("M,K,N", [(777, 1536, 640), (2048, 3072, 128), (4096, 1536, 6144)])
+def test_paired_launch_matches_single_products(M, K, N):
+    """dX and dW requested together run as one launch (and dW's k split is chosen
+    for the pair); dX must equal the dX-only call bit for bit (same tiles, no k
+    split), dW the dW-only call to float rounding (its split may differ)."""
+    X, W, dY = _mats(M, K, N, seed=11 + M)
+    print(f"case: paired linear_bwd M {M} K {K} N {N}", flush=True)
+    Xg, Wg, dYg = _bf(X), _bf(W), _bf(dY)
+    dX, dW, _ = _ssm().linear_bwd(Xg, Wg, dYg)
+    dX1, _, _ = _ssm().linear_bwd(None, Wg, dYg, need_dw=False)
+    _, dW1, _ = _ssm().linear_bwd(Xg, Wg, dYg, need_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX1)
+    assert norm_err(_np(dW), _np(dW1)) < 1e-6
+    assert norm_err(_np(dW), orc.linear_bwd(X, W, dY)[1]) < TOL_F32
+
+
 def test_linear_bwd_empty_rows():
     """M = 0: dW and db are zero (sums over no rows)."""
     W = _bf(np.ones((24, 16)))
