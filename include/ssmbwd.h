@@ -247,6 +247,10 @@ int rmsnorm_bwd(const void* x, const float* w, const void* dy, const void* d_res
  * X may be null when dW is.  X, W, dY need 16-byte aligned bases and row strides
  * that are multiples of 8.  Workspace: linear_bwd_workspace_size() (split-k
  * partial sums; 0 bytes when no split is used).
+ * Repeatability: a call repeated with the same shapes and the same set of
+ * requested outputs gives the same bits.  When dX and dW are both requested the
+ * two products share one launch and dW's split over M is chosen for the pair, so
+ * dW may then differ from a dW-only call by float rounding; dX never does.
  * ------------------------------------------------------------------------- */
 size_t linear_bwd_workspace_size(int64_t M, int K, int N);
 int linear_bwd(const void* X, int64_t ldx, const void* W, const void* dY, int64_t lddy,
