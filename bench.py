@@ -45,8 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload, DEFAULT_STEPS)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps before them (default: per workload)")
     ap.add_argument("--workload", default="mamba370m")
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -497,8 +497,21 @@ def copy_probe(args):
             "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}
 
 
+# Default (warmup, steps) per workload.  The GPU comes to the timed region from
+# seconds of idling while the host draws the inputs, and its first few tens of
+# milliseconds of work run slower (clocks ramping up): on the mamba-370m-shaped
+# scan 5 warm-up steps (4 ms) time 0.739 ms per step, 100 (70 ms) 0.665 ms, the
+# same kernels.  So every workload warms up for at least ~70 ms and times at
+# least ~130 ms.
+DEFAULT_STEPS = {"tiny": (100, 200), "mamba130m": (200, 400), "mamba370m": (100, 200), "mamba2p8b": (40, 80),
+                 "layer": (30, 60), "backbone": (10, 20), "revscan": (500, 1000)}
+
+
 def main():
     args = parse()
+    w0, k0 = DEFAULT_STEPS.get(args.workload, (5, 20)) if not args.copy_probe else (5, 20)
+    args.warmup = w0 if args.warmup is None else args.warmup
+    args.steps = k0 if args.steps is None else args.steps
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
               "of this path is a design note, not a measured configuration.", file=sys.stderr)
