@@ -158,7 +158,33 @@ int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A_log, cons
                       void* stream, void* const* stage_events);
 
 /* ---------------------------------------------------------------------------
- * ssm_scan_fwd — the forward recurrence above (the page's forward is implied
+ * ssm_scan_bwd_ckpt_noalloc — ssm_scan_bwd_ckpt without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc.
+ * Same kernels, arguments and outputs as ssm_scan_bwd_ckpt (no stage events).
+ * Its scratch is a static device array of ssm_scan_bwd_ckpt_noalloc_capacity()
+ * bytes (64 MiB), one copy per GPU that runs the call, held from the first
+ * call on that GPU until the process ends.  A shape whose
+ * ssm_scan_bwd_ckpt_workspace_size() exceeds it is rejected with
+ * SSM_ERR_WORKSPACE before anything is launched (the mamba-370m shape, batch 8,
+ * seqlen 2048, d_inner 2048, d_state 16, needs about 35 MB).
+ * The call itself allocates nothing: on its first call on a device it looks up
+ * the array's device address (hipGetSymbolAddress) and keeps it.  `stream`
+ * must belong to the current device (SSM_ERR_INVALID_ARG otherwise).
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind (nothing in it needs to start at zero): two calls whose executions
+ * overlap on one GPU, on different streams or from different threads, race
+ * and give wrong results.  Serialise them on one stream.
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan_bwd_ckpt_noalloc_capacity(void);
+int ssm_scan_bwd_ckpt_noalloc(const void* u, const void* delta, const float* A_log, const void* B,
+                              const void* C, const float* D, const void* z, const void* d_out,
+                              const float* h_ckpt, void* d_u, void* d_delta, float* d_A_log,
+                              void* d_B, void* d_C, float* d_D, void* d_z, int flags,
+                              const ssm_dims* dims, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan_fwd —the forward recurrence above (the page's forward is implied
  * by the states Phase B3 reads back).  Writes y (nullable), out = y * SiLU(z)
  * (nullable; requires z) and, if h_ckpt is not null, the state before every
  * ckpt_every-th step: h_ckpt[b, k, n, d] = h_{k*ckpt_every - 1} (zero for k = 0),

@@ -84,6 +84,9 @@ _SIGS = {
     "ssm_scan_bwd_ckpt_workspace_size": (_sz, [_dims_p, _i]),
     "ssm_scan_bwd_ckpt": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _i,
                                _vp, _sz, _dims_p, _i, _vp, ctypes.POINTER(ctypes.c_void_p)]),
+    "ssm_scan_bwd_ckpt_noalloc_capacity": (_sz, []),
+    "ssm_scan_bwd_ckpt_noalloc": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _fp,
+                                       _vp, _i, _dims_p, _i, _vp]),
     "ssm_scan_fwd_workspace_size": (_sz, [_dims_p, _i]),
     "ssm_scan_fwd": (_i, [_vp, _vp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _i, _vp, _sz, _dims_p, _i, _vp]),
     "gating_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _vp]),
@@ -232,12 +235,25 @@ def ssm_scan_bwd_ckpt(u, delta, A_log, B, C, D, z, d_out, h_ckpt, *, softplus_ep
                      seg_len, out, workspace, stage_events)
 
 
+def ssm_scan_bwd_ckpt_noalloc(u, delta, A_log, B, C, D, z, d_out, h_ckpt, *, softplus_epilogue: bool = False,
+                              accumulate: bool = False, seg_len: int = 0, out: dict | None = None) -> dict:
+    """ssm_scan_bwd_ckpt whose scratch is the library's static device array (no workspace
+    argument; shapes needing more than ``ssm_scan_bwd_ckpt_noalloc_capacity()`` bytes are
+    rejected).  Pass every output in ``out`` for a call that allocates nothing."""
+    return _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, _bwd_flags(softplus_epilogue, accumulate),
+                     seg_len, out, None, None, noalloc=True)
+
+
+def ssm_scan_bwd_ckpt_noalloc_capacity() -> int:
+    return int(lib().ssm_scan_bwd_ckpt_noalloc_capacity())
+
+
 def _bwd_flags(softplus_epilogue: bool = False, accumulate: bool = False) -> int:
     return (SSM_BWD_SOFTPLUS if softplus_epilogue else 0) | (SSM_BWD_ACCUMULATE if accumulate else 0)
 
 
 def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, flags, seg_len, out, workspace,
-              stage_events) -> dict:
+              stage_events, noalloc: bool = False) -> dict:
     dt = _dtype_code(u)
     batch, seqlen, d_inner = u.shape
     n = A_log.shape[1]
@@ -272,6 +288,14 @@ def _scan_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, flags, seg_len, out, w
         nk = (seqlen + 7) // 8
         _need(h_ckpt.dtype == torch.float32 and tuple(h_ckpt.shape) == (batch, nk, n, d_inner)
               and h_ckpt.is_contiguous(), f"h_ckpt must be float32 [{batch}, {nk}, {n}, {d_inner}], contiguous")
+        if noalloc:
+            rc = lib().ssm_scan_bwd_ckpt_noalloc(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                                 _ptr(z), _ptr(d_out), _ptr(h_ckpt), _ptr(o["d_u"]),
+                                                 _ptr(o["d_delta"]), _ptr(o["d_A_log"]), _ptr(o["d_B"]),
+                                                 _ptr(o["d_C"]), _ptr(o["d_D"]), _ptr(o["d_z"]), int(flags),
+                                                 ctypes.byref(dims), dt, _stream(u))
+            _check("ssm_scan_bwd_ckpt_noalloc", rc)
+            return o
         nbytes = int(lib().ssm_scan_bwd_ckpt_workspace_size(ctypes.byref(dims), dt))
         ws, wsb = _workspace(nbytes, dev, workspace)
         rc = lib().ssm_scan_bwd_ckpt(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

@@ -28,6 +28,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1031,10 +1032,56 @@ using namespace ssm;
 
 namespace ssm {
 namespace {
+// The allocation-free variant of ssm_scan_bwd_ckpt takes its workspace from
+// this file-scope device array: one copy per GPU, held until the process ends.
+// In host code `scratch` only names the array; its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that runs `stream`, which must be
+// the current device.
+int scratch_address(void* stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SSM_ERR_LAUNCH, "hipGetDevice failed");
+  }
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(SSM_ERR_INVALID_ARG, "the stream's device cannot be queried");
+    }
+    if (sdev != dev)
+      return fail(SSM_ERR_INVALID_ARG, "the stream runs on device %d but device %d is current", sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(SSM_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(SSM_ERR_LAUNCH, "device address of the static scratch: %s", hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
+}
+
+// use_scratch: the workspace is the static device scratch above (workspace and
+// ws_bytes are ignored); the call is rejected if its plan needs more.
 int run_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C, const float* D,
             const void* z, const void* d_out, const float* h_ckpt, bool ckpt_given, void* d_u, void* d_delta,
             float* d_A_log, void* d_B, void* d_C, float* d_D, void* d_z, int flags, void* workspace,
-            size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream, void* const* stage_events) {
+            size_t ws_bytes, const ssm_dims* dims, int dtype, void* stream, void* const* stage_events,
+            bool use_scratch = false) {
   int rc = check_dims(dims, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1051,6 +1098,14 @@ int run_bwd(const void* u, const void* delta, const float* A_log, const void* B,
   if (dtype == SSM_BF16 && !(aligned4(B) && aligned4(C) && aligned4(d_B) && aligned4(d_C)))
     return fail(SSM_ERR_UNSUPPORTED, "bf16 B, C, d_B and d_C must be 4-byte aligned");
   const Plan p = make_plan(dm, dtype, true, ckpt_given);
+  if (use_scratch) {
+    if (p.bytes > kScratchBytes)
+      return fail(SSM_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu",
+                  p.bytes, kScratchBytes);
+    rc = scratch_address(stream, &workspace);
+    if (rc != SSM_OK) return rc;
+    ws_bytes = kScratchBytes;
+  }
   if (!workspace || ws_bytes < p.bytes || !aligned256(workspace))
     return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (256-byte aligned)",
                 workspace ? ws_bytes : 0, p.bytes);
@@ -1114,6 +1169,17 @@ extern "C" int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* 
                                  int dtype, void* stream, void* const* stage_events) {
   return run_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, true, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
                  flags, workspace, ws_bytes, dims, dtype, stream, stage_events);
+}
+
+extern "C" size_t ssm_scan_bwd_ckpt_noalloc_capacity(void) { return kScratchBytes; }
+
+extern "C" int ssm_scan_bwd_ckpt_noalloc(const void* u, const void* delta, const float* A_log, const void* B,
+                                         const void* C, const float* D, const void* z, const void* d_out,
+                                         const float* h_ckpt, void* d_u, void* d_delta, float* d_A_log, void* d_B,
+                                         void* d_C, float* d_D, void* d_z, int flags, const ssm_dims* dims,
+                                         int dtype, void* stream) {
+  return run_bwd(u, delta, A_log, B, C, D, z, d_out, h_ckpt, true, d_u, d_delta, d_A_log, d_B, d_C, d_D, d_z,
+                 flags, nullptr, 0, dims, dtype, stream, nullptr, true);
 }
 
 extern "C" int ssm_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
