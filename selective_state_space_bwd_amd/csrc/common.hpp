@@ -151,6 +151,9 @@ int gemm_check(const void* A, long long lda, const void* B, long long ldb, const
                size_t ws_bytes, const void* workspace);
 int gemm_bf16(const void* A, bool a_kcontig, long long lda, const void* B, bool b_kcontig, long long ldb, void* C,
               long long ldc, int out_dtype, int M, int N, int K, int accumulate, void* workspace, hipStream_t st);
+// scan.hip: the scan entry points' argument check (sizes, strides, segment
+// length), for callers that must reject a call before their first launch
+int scan_check_dims(const ssm_dims* dm, int dtype);
 // pointwise.hip: zero fill and the layer's forward pieces
 void launch_fill_zero(float* p, int64_t n, hipStream_t st);
 void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, int dim, float eps, hipStream_t st);

@@ -30,6 +30,19 @@ struct Carver {
   }
 };
 
+ssm_dims scan_dims_of(const ssm_layer_dims& d) {
+  ssm_dims s{};
+  s.batch = d.batch;
+  s.seqlen = d.seqlen;
+  s.d_inner = d.d_inner;
+  s.d_state = d.d_state;
+  s.ld_bc = d.dt_rank + 2 * d.d_state;
+  s.ld_dbc = s.ld_bc;
+  s.seg_len = d.seg_len;
+  s.ld_z = 2 * d.d_inner;
+  return s;
+}
+
 int check_layer(const ssm_layer_dims* d) {
   if (!d) return fail(SSM_ERR_INVALID_ARG, "dims is null");
   if (d->batch <= 0 || d->seqlen <= 0 || d->d_model <= 0 || d->d_inner <= 0 || d->dt_rank <= 0 || d->d_conv <= 0)
@@ -44,7 +57,10 @@ int check_layer(const ssm_layer_dims* d) {
   if (!(d->eps >= 0.f)) return fail(SSM_ERR_INVALID_ARG, "eps must be >= 0");
   if ((double)d->batch * d->seqlen * 2.0 * d->d_inner >= 9.0e15 || (double)d->batch * d->seqlen >= 2147483648.0)
     return fail(SSM_ERR_INVALID_ARG, "layer too large");
-  return SSM_OK;
+  // the scan's own checks (segment length, row strides inside the layer's rows),
+  // so that no stage has launched when one of them fails
+  const ssm_dims sd = scan_dims_of(*d);
+  return scan_check_dims(&sd, SSM_BF16);
 }
 
 int check_weights(const ssm_layer_weights* w) {
@@ -63,18 +79,6 @@ int check_saved(const ssm_layer_saved* s) {
   return SSM_OK;
 }
 
-ssm_dims scan_dims_of(const ssm_layer_dims& d) {
-  ssm_dims s{};
-  s.batch = d.batch;
-  s.seqlen = d.seqlen;
-  s.d_inner = d.d_inner;
-  s.d_state = d.d_state;
-  s.ld_bc = d.dt_rank + 2 * d.d_state;
-  s.ld_dbc = s.ld_bc;
-  s.seg_len = d.seg_len;
-  s.ld_z = 2 * d.d_inner;
-  return s;
-}
 
 size_t max_of(std::initializer_list<size_t> v) {
   size_t m = 0;

@@ -1026,6 +1026,9 @@ int zero_params(float* d_A_log, float* d_D, int n_a, int n_d, hipStream_t st) {
 }
 
 }  // namespace
+
+int scan_check_dims(const ssm_dims* dm, int dtype) { return check_dims(dm, dtype); }
+
 }  // namespace ssm
 
 using namespace ssm;

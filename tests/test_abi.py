@@ -228,10 +228,32 @@ def test_layer_entry_points_validate():
     assert bwd(_layer_dims(), x=ctypes.c_void_p(0x1002)) == ssm.SSM_ERR_INVALID_ARG   # misaligned x
     assert bwd(_layer_dims(), w=ssm.ssm_layer_weights(*([FAKE.value] * 9 + [None]))) == ssm.SSM_ERR_INVALID_ARG
     assert bwd(_layer_dims(), g=ssm.ssm_layer_grads(*([None] + [FAKE.value] * 9))) == ssm.SSM_ERR_INVALID_ARG
+    # the scan's checks run with the layer's, before any stage launches
+    assert bwd(_layer_dims(seg_len=12)) == ssm.SSM_ERR_INVALID_ARG
+    assert bwd(_layer_dims(seqlen=1 << 20, d_inner=4096)) == ssm.SSM_ERR_UNSUPPORTED   # rows past 2^32 elements
     misaligned = ssm.ssm_layer_saved(FAKE.value, 0x1008, FAKE.value, FAKE.value)
     assert bwd(_layer_dims(), sv=misaligned) == ssm.SSM_ERR_UNSUPPORTED
     assert L.mamba_layer_fwd(FAKE, ctypes.byref(w), FAKE, ctypes.byref(sv), FAKE, 16, ctypes.byref(_layer_dims()),
                              None) == ssm.SSM_ERR_WORKSPACE
+
+
+def test_layer_bad_segment_length_leaves_accumulated_gradients_alone():
+    """A segment length the scan rejects fails the whole layer call before its first stage: with
+    accumulate set, d_W_out (here host memory, which no launch could reach) keeps its contents."""
+    import numpy as np
+    buf = np.full(64, 7.0, np.float32)
+    w = ssm.ssm_layer_weights(*([FAKE.value] * 10))
+    sv = ssm.ssm_layer_saved(*([FAKE.value] * 4))
+    g = ssm.ssm_layer_grads(*([FAKE.value] * 9 + [buf.ctypes.data]), 1)
+    dims = _layer_dims(seg_len=20)
+    big = L.mamba_layer_bwd_workspace_size(ctypes.byref(_layer_dims()))
+    rc = L.mamba_layer_bwd(FAKE, ctypes.byref(w), ctypes.byref(sv), FAKE, FAKE, ctypes.byref(g), FAKE, big,
+                           ctypes.byref(dims), None)
+    assert rc == ssm.SSM_ERR_INVALID_ARG
+    assert "seg_len" in L.ssm_last_error().decode()
+    assert np.all(buf == 7.0)
+    assert L.mamba_layer_fwd(FAKE, ctypes.byref(w), FAKE, ctypes.byref(sv), FAKE, big, ctypes.byref(dims),
+                             None) == ssm.SSM_ERR_INVALID_ARG
 
 
 def test_binding_has_no_cpu_path():
