@@ -164,8 +164,8 @@ def test_full_layer_sampled():
     bench runs it.  Sampled against the oracle: batch elements 0 and 7 (their d_x,
     output and saved activations depend on nothing else), each run by the oracle
     alone.  The parameter gradients, sums over the batch, are checked by the oracle
-    on element 0 run alone on the GPU, and at full batch by additivity: the full
-    launch equals the sum of eight one-element launches."""
+    on elements 0 and 7 each run alone on the GPU, and at full batch by additivity:
+    the full launch equals the sum of eight one-element launches."""
     c = CONFIGS["layer"]
     p = layer_inputs(c.batch, c.seqlen, c.d_model, c.d_inner, c.d_state, c.dt_rank, c.d_conv, "bf16", seed=c.seed)
     t = _dev(p)
@@ -174,6 +174,7 @@ def test_full_layer_sampled():
     out, saved = _ssm().mamba_layer_fwd(t["x"], W)
     g = _ssm().mamba_layer_bwd(t["x"], W, saved, t["d_out"])
     torch.cuda.synchronize()
+    refs = {}
     for b in (0, c.batch - 1):
         pb = _element(p, b)
         act = orc.layer_forward(pb, c.d_state, c.dt_rank)
@@ -181,8 +182,7 @@ def test_full_layer_sampled():
         _check(fwd, act, ("out", "xz", "xdbl", "delta", "y"), f"forward element {b}")
         ref = orc.layer_bwd(pb, pb["d_out"], c.d_state, c.dt_rank)
         _check({"d_x": _np(g["d_x"][b:b + 1])}, ref, ("d_x",), f"d_x element {b}")
-        if b == 0:
-            ref0 = ref
+        refs[b] = ref
     params = [k for k in GRADS if k != "d_x"]
     acc = {k: torch.zeros_like(g[k]) for k in params}
     for b in range(c.batch):
@@ -191,8 +191,8 @@ def test_full_layer_sampled():
         gb = _ssm().mamba_layer_bwd(xb, W, sb, db)
         for k in params:
             acc[k] += gb[k]
-        if b == 0:
+        if b in refs:
             torch.cuda.synchronize()
-            _check({k: _np(gb[k]) for k in params}, ref0, params, "parameter gradients, element 0")
+            _check({k: _np(gb[k]) for k in params}, refs[b], params, f"parameter gradients, element {b}")
     torch.cuda.synchronize()
     _check({k: _np(g[k]) for k in params}, {k: _np(acc[k]) for k in params}, params, "batch additivity")

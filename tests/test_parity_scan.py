@@ -240,7 +240,8 @@ FULL = ["mamba130m", "mamba370m", "mamba2p8b"]
 def test_full_size_sampled(name):
     """Full workload on the GPU in the bench's launch configuration; the oracle
     recomputes 48 sampled channels (every per-channel output and the parameter
-    gradients of those channels) and batch element 0 in full (d_B, d_C)."""
+    gradients of those channels) and the first and last batch elements in full
+    (d_B, d_C, sums over every channel)."""
     c = CONFIGS[name]
     print(f"case: {c.name} seed {c.seed}: generating inputs", flush=True)
     p = scan_inputs(c.batch, c.seqlen, c.d_inner, c.d_state, c.dtype, c.seed)
@@ -257,8 +258,9 @@ def test_full_size_sampled(name):
     sub = {k: g[k][:, :, ch] for k in ("d_u", "d_delta", "d_z")}
     sub["d_A_log"], sub["d_D"] = g["d_A_log"][ch], g["d_D"][ch]
     _check(sub, r, TOL[c.dtype], keys=("d_u", "d_delta", "d_z", "d_A_log", "d_D"), label="channels")
-    print(f"case: {c.name}: oracle on batch element 0", flush=True)
-    q = {k: (v[:1] if v.ndim == 3 else v) for k, v in p.items()}
-    r = oracle_bwd(q)
-    sub = {"d_B": g["d_B"][:1], "d_C": g["d_C"][:1]}
-    _check(sub, r, TOL[c.dtype], keys=("d_B", "d_C"), label="batch 0")
+    for b in sorted({0, c.batch - 1}):
+        print(f"case: {c.name}: oracle on batch element {b}", flush=True)
+        q = {k: (v[b:b + 1] if v.ndim == 3 else v) for k, v in p.items()}
+        r = oracle_bwd(q)
+        sub = {"d_B": g["d_B"][b:b + 1], "d_C": g["d_C"][b:b + 1]}
+        _check(sub, r, TOL[c.dtype], keys=("d_B", "d_C"), label=f"batch {b}")
