@@ -3,15 +3,22 @@
 One step of the default workload = one ``ssm_scan_bwd`` call (segment
 summaries, carries, the main backward sweep, final reductions) over the
 mamba-370m-shaped problem (batch 8, T 2048, d_inner 2048, d_state 16, float32),
-inputs resident in HBM.  ``--workload layer`` times one ``mamba_layer_bwd``
-call (the whole layer backward, bf16, batch 8, T 2048, d_model 1536, d_inner
-3072) instead.  Prints one JSON line.  Only one GPU is supported.
+inputs resident in HBM.  The same run then times the other workloads of the
+benchmark (mamba-130m-shaped and mamba-2.8b-shaped scans, the full layer; the
+tiny case is parity-only) and reports them under ``configs``.  Prints one JSON
+line.  Only one GPU is supported.
 
-    python bench.py [--steps K] [--warmup W] [--workload mamba370m|mamba130m|mamba2p8b|layer]
-                    [--no-cpu-baseline] [--copy-probe]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-configs]
+                    [--copy-probe] [--ckpt] [--recompute] [--seg-len L]
 
-``--copy-probe`` only copies a 1 GiB device buffer ``steps`` times: the plain
-copy of known size that calibrates the HBM byte counters of rocprofv3.
+``--workload`` times one other workload instead (mamba130m, mamba2p8b, layer,
+backbone, revscan, tiny).  ``--copy-probe`` only copies a 1 GiB device buffer
+``steps`` times: the plain copy of known size that calibrates the HBM byte
+counters of rocprofv3.
+
+The CPU baseline is the fp64 oracle (test infrastructure) run on the host's
+cores, sharded over (batch, 256-channel block) in a process pool; it runs before
+any GPU work, so the pool forks a process that has not touched the GPU.
 """
 from __future__ import annotations
 
@@ -19,6 +26,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -30,16 +38,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "SSM-bwd state-elements/s (B·T·d_inner·d_state) + HBM GB/s as % of MI355X peak"
-HBM_PEAK_GBPS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
-# fp32 vector peak without packed instructions: 256 CUs x 64 lanes x 2 flop (FMA) x 2.4 GHz
-VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0         # dense bf16 matrix cores, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3        # published fp32 vector peak (packed FMA)
+# the same vector units without packed instructions, which this library does not
+# use: 256 CUs x 64 lanes x 2 flop (FMA) x 2.4 GHz
+FP32_NONPACKED_CEILING_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 # algorithmic flops per state element of the backward's definition (mul, add, exp = 1 each):
 # forward  a = exp(delta A) 2, h = a h + (delta u) B 3, y += C h 2             -> 7
 # adjoint  g = dy C + a g 3, w = g (a h_prev) 1, d_delta += A w 2, d_A_log += delta w 2,
 #          d_u's sum g B 2, d_B = sum_d g delta u 2, d_C = sum_d dy h 2        -> 14
 FLOPS_PER_SE = 21
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CHANNEL_BLOCK = 1024  # channels per CPU-baseline shard (the oracle's own block size)
 
 
 def parse():
@@ -50,6 +61,8 @@ def parse():
     ap.add_argument("--workload", default="mamba370m")
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the named workload (skip the other workloads' summary)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--recompute", action="store_true",
                     help="backbone: keep only the layer inputs (SSM_KEEP_INPUTS); the backward reruns each layer's "
@@ -92,8 +105,8 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-# the sources each profiled kernel is compiled from
-KERNEL_SOURCES = {"scan_bwd_main": ("scan.hip", "common.hpp")}
+# the sources each profiled kernel (or whole call) is compiled from
+KERNEL_SOURCES = {"scan_bwd_main": ("scan.hip", "common.hpp"), "ssm_scan_bwd": ("scan.hip", "common.hpp")}
 
 
 def source_digest(kernel: str) -> str:
@@ -107,8 +120,8 @@ def source_digest(kernel: str) -> str:
 
 
 def recorded_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
-    taken on the current sources: lines `traffic <workload> <kernel> <bytes> <digest>`."""
+    """HBM bytes per launch of `kernel` (or per call, kernel "ssm_scan_bwd") from the committed counter
+    summary, if it was taken on the current sources: lines `traffic <workload> <kernel> <bytes> <digest>`."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     digest = source_digest(kernel)
@@ -120,53 +133,130 @@ def recorded_traffic(workload: str, kernel: str):
     return None
 
 
-CPU_SAMPLE_SECONDS = 10.0
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host's cores (fork pool, before any GPU use)
+
+_POOL_INPUTS: dict = {}
+
+
+def _pool_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def _scan_shard(task):
+    """The oracle on one (batch element, channel block) shard; returns its partial sums."""
+    from oracle import ssm as orc
+    b, d0, d1 = task
+    p = _POOL_INPUTS
+    t0 = time.process_time()
+    r = orc.ssm_scan_bwd(p["u"][b:b + 1, :, d0:d1], p["delta"][b:b + 1, :, d0:d1], p["A_log"][d0:d1],
+                         p["B"][b:b + 1], p["C"][b:b + 1], p["D"][d0:d1], p["z"][b:b + 1, :, d0:d1],
+                         p["d_out"][b:b + 1, :, d0:d1])
+    return task, r["d_B"][0], r["d_C"][0], r["d_A_log"], r["d_D"], time.process_time() - t0
+
+
+def _layer_shard(b):
+    from oracle import layer as orc
+    p = _POOL_INPUTS
+    q = {k: (v[b:b + 1] if k in ("x", "d_out") else v) for k, v in p.items() if not k.startswith("_")}
+    t0 = time.process_time()
+    r = orc.layer_bwd(q, q["d_out"], p["_d_state"], p["_dt_rank"])
+    return b, {k: v for k, v in r.items() if k != "d_x"}, time.process_time() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _pool_workers() -> int:
+    # the host share of one GPU is 16 cores at most on the GPU hosts
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+MIN_CPU_SECONDS = 10.0
 
 
 def cpu_baseline_scan(cfg):
-    """The fp64 oracle, single-threaded, one whole sequence of the workload at a time until
-    CPU_SAMPLE_SECONDS have passed (or the batch is done)."""
-    from threadpoolctl import threadpool_limits
+    """The fp64 oracle over the whole workload, sharded over (batch element, 256-channel block) on a
+    fork pool of all host cores (BLAS threads 1 per worker).  The shards' partial sums of d_B, d_C
+    (over channel blocks) and d_A_log, d_D (over batch) are added in shard order.  The whole workload
+    is repeated until the workers have spent MIN_CPU_SECONDS of CPU time."""
+    import multiprocessing as mp
 
-    from oracle import ssm as orc
     from synth import scan_inputs
-    p = scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
-    dt, done = 0.0, 0
-    with threadpool_limits(1):
-        while done < cfg.batch and dt < CPU_SAMPLE_SECONDS:
-            q = {k: (v[done:done + 1] if v.ndim == 3 else v) for k, v in p.items()}
+    global _POOL_INPUTS
+    _POOL_INPUTS = scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
+    tasks = [(b, d0, min(d0 + CHANNEL_BLOCK, cfg.d_inner)) for b in range(cfg.batch)
+             for d0 in range(0, cfg.d_inner, CHANNEL_BLOCK)]
+    n = _pool_workers()
+    passes, wall, cpu = 0, 0.0, 0.0
+    with mp.get_context("fork").Pool(n, initializer=_pool_init) as pool:
+        while cpu < MIN_CPU_SECONDS and passes < 8:
             t0 = time.perf_counter()
-            orc.ssm_scan_bwd(q["u"], q["delta"], q["A_log"], q["B"], q["C"], q["D"], q["z"], q["d_out"])
-            dt += time.perf_counter() - t0
-            done += 1
-    se = done * cfg.seqlen * cfg.d_inner * cfg.d_state
-    return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} sequences of the same workload, one at a time ({se} state elements, "
-                      f"{dt:.1f} s, fp64 NumPy, 1 thread)"}
+            res = pool.map(_scan_shard, tasks, chunksize=1)
+            d_B = np.zeros((cfg.batch, cfg.seqlen, cfg.d_state))
+            d_C = np.zeros_like(d_B)
+            d_A = np.zeros((cfg.d_inner, cfg.d_state))
+            d_D = np.zeros(cfg.d_inner)
+            for (b, d0, d1), pb, pc, pa, pd, _ in res:      # fixed order: batch, then channel block
+                d_B[b] += pb
+                d_C[b] += pc
+                d_A[d0:d1] += pa
+                d_D[d0:d1] += pd
+            wall += time.perf_counter() - t0
+            cpu += sum(r[-1] for r in res)
+            passes += 1
+    _POOL_INPUTS = {}
+    se = passes * cfg.state_elements
+    return {"value": se / wall, "unit": "state-elements/s", "cores": n, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"the whole workload x {passes} ({se} state elements) as {len(tasks)} shards of "
+                      f"(batch element, {CHANNEL_BLOCK} channels) on {n} worker processes, fp64 NumPy, "
+                      f"1 BLAS thread each; {wall:.2f} s wall, {cpu:.1f} s CPU"}
 
 
 def cpu_baseline_layer(cfg):
-    """The fp64 oracle's whole-layer forward + backward, single-threaded, one whole sequence of the
-    workload at a time until CPU_SAMPLE_SECONDS have passed (or the batch is done)."""
-    from threadpoolctl import threadpool_limits
+    """The fp64 oracle's whole-layer forward + backward, one sequence per task on a fork pool of all host
+    cores, until the workers have spent MIN_CPU_SECONDS of CPU time or the batch is done; parameter
+    gradients summed over the sequences in order."""
+    import multiprocessing as mp
 
-    from oracle import layer as orc
     from synth import layer_inputs
+    global _POOL_INPUTS
     p = layer_inputs(cfg.batch, cfg.seqlen, cfg.d_model, cfg.d_inner, cfg.d_state, cfg.dt_rank, cfg.d_conv,
                      cfg.dtype, cfg.seed)
-    dt, done = 0.0, 0
-    with threadpool_limits(1):
-        while done < cfg.batch and dt < CPU_SAMPLE_SECONDS:
-            q = {k: (v[done:done + 1] if k in ("x", "d_out") else v) for k, v in p.items()}
-            t0 = time.perf_counter()
-            orc.layer_bwd(q, q["d_out"], cfg.d_state, cfg.dt_rank)
-            dt += time.perf_counter() - t0
-            done += 1
+    p["_d_state"], p["_dt_rank"] = cfg.d_state, cfg.dt_rank
+    _POOL_INPUTS = p
+    n = _pool_workers()
+    with mp.get_context("fork").Pool(n, initializer=_pool_init) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_layer_shard, list(range(min(cfg.batch, n))), chunksize=1)
+        wall = time.perf_counter() - t0
+    tot = {}
+    for _, g, _ in sorted(res, key=lambda r: r[0]):
+        for k, v in g.items():
+            tot[k] = tot.get(k, 0) + v
+    cpu = sum(r[-1] for r in res)
+    _POOL_INPUTS = {}
+    done = len(res)
     se = done * cfg.seqlen * cfg.d_inner * cfg.d_state
-    return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} sequences of the same workload, one at a time ({se} state elements, "
-                      f"{dt:.1f} s, fp64 NumPy forward + backward, 1 thread)"}
+    return {"value": se / wall, "unit": "state-elements/s", "cores": n, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"{done} of {cfg.batch} sequences of the same workload, one per worker process ({se} state "
+                      f"elements), fp64 NumPy forward + backward, 1 BLAS thread each; {wall:.2f} s wall, "
+                      f"{cpu:.1f} s CPU"}
 
+
+# ---------------------------------------------------------------------------
+# timing
 
 STAGE_SAMPLES = 4  # timed steps that also record the per-stage HIP events
 
@@ -196,7 +286,64 @@ def timed(step, n_events: int, steps: int, warmup: int):
     return elapsed / steps * 1e3, stages
 
 
-def run_scan(args, cfg):
+def step_stats(step, steps: int):
+    """Per-step times of `steps` more steps, each bracketed by events on the stream the library
+    runs on (torch's current stream): median, 10th and 90th percentile in ms.  A separate pass
+    after the timed one, so the timed region carries no per-step event records."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(steps):
+        step(None)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    ms = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
+    return {"ms_median": round(float(np.median(ms)), 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
+            "ms_p90": round(float(np.percentile(ms, 90)), 4), "steps": steps,
+            "note": "per-step HIP events in a second pass of the same length after the timed region; "
+                    "the Infinity Cache is not flushed between steps"}
+
+
+# ---------------------------------------------------------------------------
+# scan workloads
+
+def scan_bytes(cfg, ckpt: bool):
+    el = 4 if cfg.dtype == "f32" else 2
+    rows = cfg.batch * cfg.seqlen
+    # with given chunk states, the float32 states before every 8-step chunk are one more input
+    ckpt_bytes = 4 * cfg.batch * ((cfg.seqlen + 7) // 8) * cfg.d_state * cfg.d_inner if ckpt else 0
+    call = ((7 * rows * cfg.d_inner + 4 * rows * cfg.d_state) * el + (2 * cfg.d_inner * (cfg.d_state + 1)) * 4
+            + ckpt_bytes)
+    # the main sweep reads u, delta, z, d_out, B, C (and the given chunk states) and writes d_u, d_delta,
+    # d_z (d_B, d_C go out as partials)
+    main = (7 * rows * cfg.d_inner + 2 * rows * cfg.d_state) * el + ckpt_bytes
+    return call, main
+
+
+def scan_roofline(cfg, main_ms, ms_step, main_bytes, call_bytes, traffic_main, traffic_call):
+    """Roofline of the main sweep against the published HBM peak (the metric's bound), with its
+    arithmetic against the published fp32 vector peak and the non-packed issue ceiling beside it."""
+    se = cfg.state_elements
+    gbps = main_bytes / (main_ms * 1e-3) / 1e9
+    tflops = FLOPS_PER_SE * se / (main_ms * 1e-3) / 1e12
+    return {
+        "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_main,
+        "kernel": "scan_bwd_main", "kernel_ms": round(main_ms, 4), "algorithmic_bytes": main_bytes,
+        "alu": {"flops_per_state_element": FLOPS_PER_SE, "achieved_TFLOPs": round(tflops, 3),
+                "published_fp32_peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
+                "frac_of_published_peak": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+                "nonpacked_issue_ceiling_TFLOPs": round(FP32_NONPACKED_CEILING_TFLOPS, 1),
+                "frac_of_nonpacked_ceiling": round(tflops / FP32_NONPACKED_CEILING_TFLOPS, 4)},
+        "step": {"algorithmic_bytes": call_bytes,
+                 "frac_of_hbm_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "counted_bytes": traffic_call,
+                 "counted_over_algorithmic": round(traffic_call / call_bytes, 3) if traffic_call else None},
+    }
+
+
+def measure_scan(args, cfg, steps, warmup, want_stats=True):
     import torch
 
     import selective_state_space_bwd_amd as ssm
@@ -228,31 +375,21 @@ def run_scan(args, cfg):
             ssm.ssm_scan_bwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
                              out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
 
-    ms_step, stages = timed(step, 5, args.steps, args.warmup)
+    ms_step, stages = timed(step, 5, steps, warmup)
+    stats = step_stats(step, steps) if want_stats else None
+    del t, out, ws
+    torch.cuda.empty_cache()
+    return ms_step, stages, stats
+
+
+def run_scan(args, cfg):
+    ms_step, stages, stats = measure_scan(args, cfg, args.steps, args.warmup)
     se = cfg.state_elements
-    el = 4 if cfg.dtype == "f32" else 2
-    rows = cfg.batch * cfg.seqlen
-    # with given chunk states, the float32 states before every 8-step chunk are one more input
-    ckpt_bytes = 4 * cfg.batch * ((cfg.seqlen + 7) // 8) * cfg.d_state * cfg.d_inner if args.ckpt else 0
-    alg_bytes = ((7 * rows * cfg.d_inner + 4 * rows * cfg.d_state) * el + (2 * cfg.d_inner * (cfg.d_state + 1)) * 4
-                 + ckpt_bytes)
+    call_bytes, main_bytes = scan_bytes(cfg, args.ckpt)
     main_ms = float(stages[:, 2].mean())
-    # the main sweep reads u, delta, z, d_out, B, C (and the given chunk states) and writes d_u, d_delta, d_z
-    # (d_B, d_C go out as partials)
-    main_bytes = (7 * rows * cfg.d_inner + 2 * rows * cfg.d_state) * el + ckpt_bytes
-    main_gbps = main_bytes / (main_ms * 1e-3) / 1e9
-    main_tflops = FLOPS_PER_SE * se / (main_ms * 1e-3) / 1e12
-    hbm_frac = main_gbps / HBM_PEAK_GBPS
-    alu_frac = main_tflops / VALU_PEAK_TFLOPS
-    if alu_frac >= hbm_frac:
-        roof = {"bound": "alu", "achieved": round(main_tflops, 3), "peak": round(VALU_PEAK_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(alu_frac, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(main_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(hbm_frac, 4)}
-    roof["traffic"] = None if args.ckpt else recorded_traffic(args.workload, "scan_bwd_main")
-    roof.update({"kernel": "scan_bwd_main", "kernel_ms": round(main_ms, 4), "hbm_frac": round(hbm_frac, 4),
-                 "alu_frac": round(alu_frac, 4), "algorithmic_bytes": main_bytes})
+    roof = scan_roofline(cfg, main_ms, ms_step, main_bytes, call_bytes,
+                         None if args.ckpt else recorded_traffic(args.workload, "scan_bwd_main"),
+                         None if args.ckpt else recorded_traffic(args.workload, "ssm_scan_bwd"))
     line = {
         "metric": METRIC, "value": se / (ms_step * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -260,22 +397,42 @@ def run_scan(args, cfg):
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_inner": cfg.d_inner,
                    "d_state": cfg.d_state, "seg_len": args.seg_len or "auto", "storage": cfg.dtype,
                    "chunk_states": "given by the forward" if args.ckpt else "rebuilt"},
-        "hbm": {"algorithmic_bytes": alg_bytes, "effective_GBps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
-                "frac_of_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "hbm": {"algorithmic_bytes": call_bytes, "effective_GBps": round(call_bytes / (ms_step * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "timing": stats,
         "stages_ms": {"summary": round(float(stages[:, 0].mean()), 4), "carry": round(float(stages[:, 1].mean()), 4),
                       "main": round(main_ms, 4), "finalize": round(float(stages[:, 3].mean()), 4)},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_scan(cfg)
     return line
 
+
+def config_entry_scan(args, key, cfg):
+    """One other scan workload of the benchmark, timed in the same run."""
+    ms_step, stages, stats = measure_scan(args, cfg, args.steps, args.warmup)
+    call_bytes, main_bytes = scan_bytes(cfg, False)
+    main_ms = float(stages[:, 2].mean())
+    med = stats["ms_median"]
+    roof = scan_roofline(cfg, main_ms, med, main_bytes, call_bytes, recorded_traffic(key, "scan_bwd_main"),
+                         recorded_traffic(key, "ssm_scan_bwd"))
+    return {"workload": cfg.name, "dtype": cfg.dtype, "ms_per_step": round(ms_step, 4), **{k: stats[k] for k in
+            ("ms_median", "ms_p10", "ms_p90")},
+            "state_elements_per_s": round(cfg.state_elements / (med * 1e-3), 1),
+            "hbm_effective_frac": round(call_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "stages_ms": {"summary": round(float(stages[:, 0].mean()), 4),
+                          "carry": round(float(stages[:, 1].mean()), 4), "main": round(main_ms, 4),
+                          "finalize": round(float(stages[:, 3].mean()), 4)},
+            "dominant_kernel": roof}
+
+
+# ---------------------------------------------------------------------------
+# layer
 
 LAYER_STAGES = ("gate_fwd", "out_proj", "conv_silu_fwd", "scan_bwd", "dt_proj", "x_proj", "conv_bwd",
                 "rmsnorm_fwd", "in_proj", "rmsnorm_bwd")
 
 
-def run_layer(args, cfg):
+def measure_layer(args, cfg, steps, warmup, want_stats=True):
     import torch
 
     import selective_state_space_bwd_amd as ssm
@@ -296,38 +453,110 @@ def run_layer(args, cfg):
         ssm.mamba_layer_bwd(t["x"], W, saved, t["d_out"], workspace=ws, out=out, seg_len=args.seg_len,
                             stage_events=ev)
 
-    ms_step, stages = timed(step, 11, args.steps, args.warmup)
-    st = {name: float(stages[:, i].mean()) for i, name in enumerate(LAYER_STAGES)}
+    ms_step, stages = timed(step, 11, steps, warmup)
+    stats = step_stats(step, steps) if want_stats else None
+    del t, W, saved, ws, out
+    torch.cuda.empty_cache()
+    return ms_step, {name: float(stages[:, i].mean()) for i, name in enumerate(LAYER_STAGES)}, stats
+
+
+def layer_gemm_flops(cfg):
     M = cfg.batch * cfg.seqlen
     dm, di, R2 = cfg.d_model, cfg.d_inner, cfg.dt_rank + 2 * cfg.d_state
-    gemm_flops = {"out_proj": 4 * M * dm * di, "dt_proj": 4 * M * di * cfg.dt_rank, "x_proj": 4 * M * di * R2,
-                  "in_proj": 4 * M * 2 * di * dm}
+    return {"out_proj": 4 * M * dm * di, "dt_proj": 4 * M * di * cfg.dt_rank, "x_proj": 4 * M * di * R2,
+            "in_proj": 4 * M * 2 * di * dm}
+
+
+def layer_scan_bytes(cfg):
+    """Algorithmic bytes of the layer's scan stage (bf16 activations: u, delta, z, d_out read, d_u, d_delta
+    written, d_z written; B, C read and d_B, d_C written; A_log, D and their gradients)."""
+    rows = cfg.batch * cfg.seqlen
+    return (7 * rows * cfg.d_inner + 4 * rows * cfg.d_state) * 2 + 2 * cfg.d_inner * (cfg.d_state + 1) * 4
+
+
+def run_layer(args, cfg):
+    ms_step, st, stats = measure_layer(args, cfg, args.steps, args.warmup)
+    gemm_flops = layer_gemm_flops(cfg)
     in_tf = gemm_flops["in_proj"] / (st["in_proj"] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(in_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(in_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel": "gemm_pair_kernel, in_proj dX + dW in one launch, then the split-k sum of dW", "kernel_ms": round(st["in_proj"], 4)}
+            "kernel": "gemm_pair_kernel, in_proj dX + dW in one launch, then the split-k sum of dW",
+            "kernel_ms": round(st["in_proj"], 4)}
     gemm_ms = sum(st[k] for k in gemm_flops)
     line = {
         "metric": METRIC, "value": cfg.state_elements / (ms_step * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di,
-                   "d_state": cfg.d_state, "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv,
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_model": cfg.d_model,
+                   "d_inner": cfg.d_inner, "d_state": cfg.d_state, "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv,
                    "seg_len": args.seg_len or "auto", "storage": "bf16",
                    "scan_states": "kept by the forward" if args.ckpt else "rebuilt"},
+        "timing": stats,
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "gemm": {"TFLOP": round(sum(gemm_flops.values()) / 1e12, 4), "ms": round(gemm_ms, 4),
                  "TFLOPs": round(sum(gemm_flops.values()) / (gemm_ms * 1e-3) / 1e12, 1),
                  "per_stage_TFLOPs": {k: round(v / (st[k] * 1e-3) / 1e12, 1) for k, v in gemm_flops.items()}},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_layer(cfg)
     return line
 
 
+def config_entry_layer(args, cfg):
+    ms_step, st, stats = measure_layer(args, cfg, args.steps, args.warmup)
+    gemm_flops = layer_gemm_flops(cfg)
+    med = stats["ms_median"]
+    dom = max(st, key=st.get)
+    if dom in gemm_flops:
+        tf = gemm_flops[dom] / (st[dom] * 1e-3) / 1e12
+        droof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        nbytes = layer_scan_bytes(cfg) if dom == "scan_bwd" else None
+        gbps = nbytes / (st[dom] * 1e-3) / 1e9 if nbytes else None
+        droof = {"bound": "hbm", "achieved": round(gbps, 1) if gbps else None, "peak": HBM_PEAK_GBPS,
+                 "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
+                 "algorithmic_bytes": nbytes}
+    droof.update({"kernel": f"{dom} stage" + (" (summary, carry, main sweep, finalize)" if dom == "scan_bwd" else ""),
+                  "kernel_ms": round(st[dom], 4)})
+    return {"workload": cfg.name, "dtype": "bf16", "ms_per_step": round(ms_step, 4),
+            **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
+            "state_elements_per_s": round(cfg.state_elements / (med * 1e-3), 1),
+            "stages_ms": {k: round(v, 4) for k, v in st.items()},
+            "gemm_TFLOPs": {k: round(v / (st[k] * 1e-3) / 1e12, 1) for k, v in gemm_flops.items()},
+            "dominant_kernel": droof}
+
+
+def config_entry_tiny(args, cfg):
+    ms_step, _, stats = measure_scan(args, cfg, args.steps, args.warmup)
+    return {"workload": cfg.name, "dtype": cfg.dtype,
+            "role": "parity case (checked against the fp64 oracle and finite differences by the tests); "
+                    "launch-bound, timed here only for completeness",
+            "ms_per_step": round(ms_step, 4), **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")}}
+
+
+def run_configs(args):
+    """The benchmark's other workloads, timed in this run (same steps and warm-up)."""
+    from synth import CONFIGS
+    out = {}
+    for key in ("tiny", "mamba130m", "mamba2p8b", "layer"):
+        if key == args.workload:
+            continue
+        cfg = CONFIGS[key]
+        print(f"bench: timing {cfg.name}", file=sys.stderr, flush=True)
+        if key == "tiny":
+            out[key] = config_entry_tiny(args, cfg)
+        elif key == "layer":
+            out[key] = config_entry_layer(args, cfg)
+        else:
+            out[key] = config_entry_scan(args, key, cfg)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# reverse linear recurrence
+
 def cpu_baseline_recurrence(cfg):
-    """The fp64 oracle, single-threaded, one whole sequence at a time until CPU_SAMPLE_SECONDS have passed."""
+    """The fp64 oracle, single-threaded, one whole sequence at a time until 10 s have passed."""
     from threadpoolctl import threadpool_limits
 
     from oracle import recurrence as orc
@@ -335,13 +564,13 @@ def cpu_baseline_recurrence(cfg):
     p = recurrence_inputs(cfg.batch, cfg.seqlen, cfg.channels, cfg.dtype, seed=cfg.seed, decay="ssm")
     dt, done = 0.0, 0
     with threadpool_limits(1):
-        while done < cfg.batch and dt < CPU_SAMPLE_SECONDS:
+        while done < cfg.batch and dt < MIN_CPU_SECONDS:
             t0 = time.perf_counter()
             orc.reverse_linear_scan(p["a"][done:done + 1], p["b"][done:done + 1])
             dt += time.perf_counter() - t0
             done += 1
     n = done * cfg.seqlen * cfg.channels
-    return {"value": n / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+    return {"value": n / dt, "unit": "elements/s", "cores": 1, "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{done} of {cfg.batch} sequences of the same workload, one at a time ({n} elements, "
                       f"{dt:.1f} s, fp64 NumPy, 1 thread)"}
 
@@ -378,7 +607,7 @@ def run_recurrence(args, cfg):
     el = 4 if cfg.dtype == "f32" else 2
     alg = 3 * cfg.elements * el          # a, b read, x written
     gbps = alg / (ms * 1e-3) / 1e9
-    line = {
+    return {
         "metric": "reverse linear scan elements/s (B·T·C)", "value": cfg.elements / (ms * 1e-3),
         "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
@@ -391,10 +620,10 @@ def run_recurrence(args, cfg):
                      "kernel": "reverse_linear_scan (summary + carry + final sweep, one call)",
                      "kernel_ms": round(ms, 4), "algorithmic_bytes": alg},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_recurrence(cfg)
-    return line
 
+
+# ---------------------------------------------------------------------------
+# backbone
 
 def cpu_baseline_backbone(cfg, steps: int = 0):
     """The fp64 oracle's backbone forward + backward, single-threaded, on the first `steps` steps (default: all)
@@ -411,7 +640,7 @@ def cpu_baseline_backbone(cfg, steps: int = 0):
         orc.backbone_bwd(bp, layers, bp["d_out"], cfg.d_state, cfg.dt_rank, cfg.eps)
         dt = time.perf_counter() - t0
     se = cfg.n_layers * steps * cfg.d_inner * cfg.d_state
-    return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle",
+    return {"value": se / dt, "unit": "state-elements/s", "cores": 1, "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"the first {steps} steps of 1 sequence at the workload's widths ({se} state elements, "
                       f"{dt:.1f} s, fp64 NumPy forward + backward, 1 thread)"}
 
@@ -438,7 +667,7 @@ def run_backbone(args, cfg):
     out = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws,
                                  seg_len=args.seg_len)
 
-    def step():
+    def step(_=None):
         ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws, out=out,
                                seg_len=args.seg_len)
 
@@ -452,6 +681,7 @@ def run_backbone(args, cfg):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    stats = step_stats(step, args.steps)
     M = cfg.batch * cfg.seqlen
     dm, di, R2 = cfg.d_model, cfg.d_inner, cfg.dt_rank + 2 * cfg.d_state
     layer_flops = 4 * M * (dm * di + di * cfg.dt_rank + di * R2 + 2 * di * dm)
@@ -459,7 +689,7 @@ def run_backbone(args, cfg):
     tf = flops / (ms * 1e-3) / 1e12
     kept_bytes = (sum(x.numel() * x.element_size() for x in kept["xs"])
                   + sum(v.numel() * v.element_size() for s_ in (kept["saved"] or []) for v in s_.values()))
-    line = {
+    return {
         "metric": METRIC, "value": cfg.state_elements / (ms * 1e-3), "unit": "state-elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -468,15 +698,13 @@ def run_backbone(args, cfg):
                    "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv, "seg_len": args.seg_len or "auto",
                    "scan_states": "kept by the forward" if args.ckpt else "rebuilt",
                    "kept": "layer inputs only (activations recomputed)" if args.recompute else "all activations"},
+        "timing": stats,
         "memory": {"kept_activations_bytes": kept_bytes, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "every product of the step (GEMM flops over the whole step time: a lower bound)",
                      "kernel_ms": round(ms, 4)},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_backbone(cfg)
-    return line
 
 
 def copy_probe(args):
@@ -521,6 +749,17 @@ def main():
         return
     from synth import CONFIGS, BackboneConfig, LayerConfig, RecurrenceConfig
     cfg = CONFIGS[args.workload]
+    # the CPU baseline runs first: its fork pool must not inherit a process that has used the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        if isinstance(cfg, LayerConfig):
+            cpu = cpu_baseline_layer(cfg)
+        elif isinstance(cfg, BackboneConfig):
+            cpu = cpu_baseline_backbone(cfg)
+        elif isinstance(cfg, RecurrenceConfig):
+            cpu = cpu_baseline_recurrence(cfg)
+        else:
+            cpu = cpu_baseline_scan(cfg)
     if isinstance(cfg, BackboneConfig):
         line = run_backbone(args, cfg)
     elif isinstance(cfg, LayerConfig):
@@ -529,6 +768,10 @@ def main():
         line = run_recurrence(args, cfg)
     else:
         line = run_scan(args, cfg)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    if args.workload == "mamba370m" and not args.no_configs and not args.ckpt:
+        line["configs"] = run_configs(args)
     print(json.dumps(line), flush=True)
 
 

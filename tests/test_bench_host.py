@@ -25,14 +25,33 @@ def test_every_workload_has_default_steps():
         assert warmup >= 10 and steps >= 2 * warmup, name
 
 
-def test_recorded_traffic_line_parses():
-    """profiles/hbm_traffic.md holds one machine-readable line for the default
-    workload's main sweep; the bench reports its bytes only while the digest
-    matches the kernel sources."""
+def test_recorded_traffic_lines_parse():
+    """profiles/hbm_traffic.md holds machine-readable lines for the default workload's main sweep
+    and whole call; the bench reports their bytes only while the digest matches the kernel sources."""
     lines = [ln for ln in open(bench.TRAFFIC_FILE) if ln.startswith("traffic ")]
-    assert len(lines) == 1
-    m = re.match(r"^traffic (\S+) (\S+) (\d+) ([0-9a-f]{16})\s*$", lines[0])
-    assert m and m.group(1) == "mamba370m" and m.group(2) == "scan_bwd_main"
-    got = bench.recorded_traffic("mamba370m", "scan_bwd_main")
-    assert got is None or got == int(m.group(3))
-    assert got == (int(m.group(3)) if m.group(4) == bench.source_digest("scan_bwd_main") else None)
+    assert 1 <= len(lines) <= 2
+    for ln in lines:
+        m = re.match(r"^traffic (\S+) (\S+) (\d+) ([0-9a-f]{16})\s*$", ln)
+        assert m and m.group(1) == "mamba370m" and m.group(2) in ("scan_bwd_main", "ssm_scan_bwd")
+        got = bench.recorded_traffic("mamba370m", m.group(2))
+        assert got == (int(m.group(3)) if m.group(4) == bench.source_digest(m.group(2)) else None)
+
+
+def test_roofline_fields_follow_the_published_peaks():
+    """The scan roofline: HBM bound against 8 TB/s from the algorithmic bytes and the kernel time;
+    the arithmetic against 157.3 TFLOP/s (published fp32) and the 78.6 TFLOP/s non-packed ceiling."""
+    cfg = CONFIGS["mamba370m"]
+    call, main = bench.scan_bytes(cfg, False)
+    assert call == 943996928 and main == 941621248
+    r = bench.scan_roofline(cfg, 0.5, 0.7, main, call, 1_400_000_000, 2_300_000_000)
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - main / 0.5e-3 / 1e9) < 0.1
+    assert abs(r["frac"] - main / 0.5e-3 / 8e12) < 1e-4
+    assert r["traffic"] == 1_400_000_000
+    alu = r["alu"]
+    tf = 21 * cfg.state_elements / 0.5e-3 / 1e12
+    assert abs(alu["achieved_TFLOPs"] - tf) < 1e-3
+    assert alu["published_fp32_peak_TFLOPs"] == 157.3 and abs(alu["frac_of_published_peak"] - tf / 157.3) < 1e-4
+    assert abs(alu["nonpacked_issue_ceiling_TFLOPs"] - 78.6) < 0.05
+    assert abs(r["step"]["frac_of_hbm_peak"] - call / 0.7e-3 / 8e12) < 1e-4
+    assert r["step"]["counted_over_algorithmic"] == round(2_300_000_000 / call, 3)
