@@ -321,6 +321,321 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, int
     }
 }
 
+// ---- 256 x 256 tiles for products made of whole tiles ----------------------
+// Four waves, each owning a 128 x 128 quarter of the block tile as 4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles (256 accumulator registers per lane, which the
+// gfx950 register file holds at one wave per SIMD).  Operand tiles reach LDS by
+// direct global -> LDS loads (global_load_lds_dwordx4: lane i of an instruction
+// writes 16 bytes at the instruction's LDS base + 16 i), so no registers stage
+// them; each lane picks which 16-byte chunk of the tile it fetches, and that
+// choice sets the LDS layout.  kBigNst LDS stages: the loads of tile k +
+// kBigNst - 1 are issued while the matrix cores work on tile k, so a load has
+// kBigNst - 1 k steps to arrive.  Against the 256 x 128 tile this halves the
+// operand bytes per flop and cuts the LDS operand reads per flop by a quarter.
+constexpr int kBigT = 256;                              // block tile rows and columns
+constexpr int kBigK = 32;                               // k per step
+constexpr int kBigNst = 4;                              // LDS stages
+constexpr int kBigOpBytes = kBigT * kBigK * 2;          // one operand's tile in one stage
+constexpr int kBigStageBytes = 2 * kBigOpBytes;         // A and B
+constexpr int kBigLdsBytes = kBigNst * kBigStageBytes;  // 128 KB
+constexpr int kBigInstPerOp = kBigOpBytes / 1024;       // 1 KB direct loads per operand tile
+constexpr int kBigInstPerWave = kBigInstPerOp / 4;      // ... per wave
+static_assert(kBigK % 16 == 0 && (kBigK == 32 || kBigK == 64) && kBigInstPerOp % 4 == 0, "big tile shape");
+static_assert(kBigLdsBytes <= 160 * 1024 && kBigNst >= 2, "big tile stages");
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
+
+// s_waitcnt with only the vector memory count: vmcnt(n), n < 64
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// One operand's 256 x kBigK tile.  Direct load q (0 .. kBigInstPerOp - 1 over
+// the block) fills LDS bytes [1024 q, 1024 q + 1024) of the operand's area.
+// KC (k contiguous): LDS [row][k], kRowBytes per row; 16-byte chunk c of row r
+//   sits in slot c ^ ((r >> kShift) & (kChunks - 1)).  A fragment read takes one
+//   chunk of 16 consecutive rows per 16 lanes, which then hit 16 different
+//   16-byte bank groups (the row's place in a 256-byte line and the XOR
+//   together enumerate them).
+// Otherwise: LDS [k][row], 512 bytes per k row; chunk c (8 tile rows) of k row
+//   k sits in slot c ^ ((k & 3) << 2).  A transposing read takes four k rows x
+//   four chunks per 32 lanes, which land in 16 different bank groups.
+template <bool KC>
+struct BigOperand {
+  static constexpr int kRowBytes = kBigK * 2;             // KC
+  static constexpr int kChunks = kBigK / 8;               // KC: 16-byte chunks per row
+  static constexpr int kShift = kChunks == 8 ? 1 : 2;     // KC: rows sharing a 256-byte line
+  static constexpr int kRowsPerInst = KC ? 1024 / kRowBytes : 2;
+  static __device__ __forceinline__ int kc_swz(int r) { return (r >> kShift) & (kChunks - 1); }
+  // byte offset (from the tile origin) of the chunk lane `lane` fetches for a
+  // direct load of parity `odd`; the rest of the offset is uniform: q x
+  // kRowsPerInst x the row stride
+  static __device__ __forceinline__ unsigned lane_src(long long ld, int lane, int odd) {
+    if (KC) {
+      const int r = odd * kRowsPerInst + lane / kChunks;  // the swizzle of row q * kRowsPerInst + r
+      return (unsigned)(((lane / kChunks) * ld + (((lane % kChunks) ^ kc_swz(r)) << 3)) * 2);
+    } else {
+      const int s = lane & 31, x = (odd * 2 + (lane >> 5)) << 2;
+      return (unsigned)(((lane >> 5) * ld + ((s ^ x) << 3)) * 2);
+    }
+  }
+  // the tile origin's element offset in the matrix
+  static __device__ __forceinline__ long long origin(long long ld, int row0, int k0) {
+    return KC ? (long long)row0 * ld + k0 : (long long)k0 * ld + row0;
+  }
+  // Per-lane byte offset (inside the operand area) of the MFMA operand of tile
+  // rows base + t * 32 .. + 31 at k 16 ks .. + 15; see OperandTile::frag for
+  // the lane -> (row, k) map.  KC: one 16-byte read, and t only adds 32 rows,
+  // so a lane keeps one offset per ks.  Otherwise: two 8-byte transposing
+  // reads, the second 4 k rows (2048 bytes) further, and ks only adds 8192
+  // bytes, so a lane keeps one offset per t.
+  static __device__ __forceinline__ unsigned lane_frag(int base, int i, int lane) {
+    if (KC) {  // i = ks
+      const int r = base + (lane & 31);
+      const int c = i * 2 + (lane >> 5);
+      return (unsigned)(r * kRowBytes + ((c ^ kc_swz(r)) << 4));
+    } else {   // i = t
+      const int grp = lane >> 4, j = lane & 15;
+      const int k = 8 * (grp >> 1) + (j >> 2);
+      const int r = base + i * 32 + 16 * (grp & 1) + 4 * (j & 3);
+      return (unsigned)(k * 512 + (((r >> 3) ^ ((k & 3) << 2)) << 4) + (r & 7) * 2);
+    }
+  }
+  static __device__ __forceinline__ bf16x8_t frag(const char* __restrict__ area, const unsigned (&off)[4], int t,
+                                                  int ks) {
+    if (KC) {
+      return *reinterpret_cast<const bf16x8_t*>(area + off[ks] + t * 32 * kRowBytes);
+    } else {
+      typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+      const char* p = area + off[t] + ks * 8192;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 2048));
+      const v4i16_t lohi[2] = {lo, hi};
+      return *reinterpret_cast<const bf16x8_t*>(lohi);
+    }
+  }
+};
+
+// the wave's direct loads of one operand tile into `area` (an LDS stage's
+// operand area); src: the tile origin in the matrix (wave-uniform), the lane's
+// byte offsets for even and odd loads
+template <bool KC>
+__device__ __forceinline__ void big_load(const uint16_t* src, long long ld, char* area, int wave, unsigned off_even,
+                                         unsigned off_odd) {
+  using Op = BigOperand<KC>;
+#pragma unroll
+  for (int q = 0; q < kBigInstPerWave; ++q) {
+    const int qb = wave * kBigInstPerWave + q;  // load index in the block
+    const char* p = reinterpret_cast<const char*>(src + (long long)qb * Op::kRowsPerInst * ld);
+    __builtin_amdgcn_global_load_lds((gbl_void_t)(p + ((qb & 1) ? off_odd : off_even)),
+                                     (lds_void_t)(area + qb * 1024), 16, 0, 0);
+  }
+}
+
+// 16 consecutive outputs of one row from a 16-byte aligned column: the big
+// tiles' epilogue (whole tiles, rows that take 16-byte vectors)
+template <typename T>
+__device__ __forceinline__ void write_row16_vec(T* __restrict__ p, const float (&v)[16], bool accumulate) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 o = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      if (accumulate) {
+        const float4 prev = reinterpret_cast<const float4*>(p)[q];
+        o.x += prev.x; o.y += prev.y; o.z += prev.z; o.w += prev.w;
+      }
+      reinterpret_cast<float4*>(p)[q] = o;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint4 prev = make_uint4(0, 0, 0, 0);
+      if (accumulate) prev = reinterpret_cast<const uint4*>(p)[q];
+      const uint32_t pw[4] = {prev.x, prev.y, prev.z, prev.w};
+      uint32_t ow[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float lo = v[8 * q + 2 * e], hi = v[8 * q + 2 * e + 1];
+        if (accumulate) {
+          lo += __uint_as_float(pw[e] << 16);
+          hi += __uint_as_float(pw[e] & 0xffff0000u);
+        }
+        ow[e] = pack_bf16x2(lo, hi);
+      }
+      reinterpret_cast<uint4*>(p)[q] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+  }
+}
+
+// Block barrier for the big tiles' k loop.  The caller has waited for what the
+// other waves must see (its direct loads, through vmcnt); the compiler fences
+// keep memory accesses from moving across, and no wait for the direct loads
+// still in flight for later stages is implied (a __syncthreads would add one).
+__device__ __forceinline__ void big_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool A_K, bool B_K, typename OutT>
+__device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0, int split, char* __restrict__ lds) {
+  using OA = BigOperand<A_K>;
+  using OB = BigOperand<B_K>;
+  constexpr int kInFlight = (kBigNst - 2) * 2 * kBigInstPerWave;  // loads of later stages allowed outstanding
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kb = split * g.k_per_split;
+  const int nk = min(g.k_per_split, g.K - kb) / kBigK;  // whole k steps (checked by the dispatcher)
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const unsigned a_even = OA::lane_src(g.lda, lane, 0), a_odd = OA::lane_src(g.lda, lane, 1);
+  const unsigned b_even = OB::lane_src(g.ldb, lane, 0), b_odd = OB::lane_src(g.ldb, lane, 1);
+  const uint16_t* a0 = g.A + OA::origin(g.lda, m0, kb);
+  const uint16_t* b0 = g.B + OB::origin(g.ldb, n0, kb);
+  // k step kt's tile origin: KC operands move along the row, the others down k rows
+  const long long a_step = A_K ? kBigK : kBigK * g.lda;
+  const long long b_step = B_K ? kBigK : kBigK * g.ldb;
+  // tile kt (clamped to the last one: the loads past the end refill a stage
+  // that nothing reads again) into its stage
+  const auto load_tile = [&](int kt, int stage) {
+    kt = min(kt, nk - 1);
+    char* st = lds + stage * kBigStageBytes;
+    big_load<A_K>(a0 + kt * a_step, g.lda, st, wave, a_even, a_odd);
+    big_load<B_K>(b0 + kt * b_step, g.ldb, st + kBigOpBytes, wave, b_even, b_odd);
+  };
+  unsigned fa_off[4], fb_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa_off[i] = OA::lane_frag(wm * 128, i, lane);
+    fb_off[i] = OB::lane_frag(wn * 128, i, lane);
+  }
+
+  static_assert(kBigK == 32, "the k loop below takes two 16-wide k slices per step");
+  constexpr int kReads = (A_K ? 4 : 8) + (B_K ? 4 : 8);  // LDS reads of one slice's operands
+  bf16x8_t fa[2][4], fb[2][4];
+  const auto read_slice = [&](const char* st, int ks, int set) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      fa[set][t] = OA::frag(st, fa_off, t, ks);
+      fb[set][t] = OB::frag(st + kBigOpBytes, fb_off, t, ks);
+    }
+  };
+  const auto mfma_slice = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  // a slice's 16 products with the other set's reads woven in, two after each
+  // of the first products, so the reads land while the matrix cores work
+  const auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one MFMA
+      if (2 * i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < kBigNst - 1; ++s) load_tile(s, s);
+  wait_vmcnt<kInFlight>();  // tile 0 is in LDS
+  big_barrier();
+  read_slice(lds, 0, 0);
+  // One k step per iteration, with no branch inside, so the accumulators stay
+  // in their registers across iterations.  Software pipelined over the two
+  // k slices of a step: slice 1's operand reads run under slice 0's products,
+  // and after the barrier the next step's slice-0 reads run under slice 1's.
+  int stage = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = stage == 0 ? kBigNst - 1 : stage - 1;  // (kt + kBigNst - 1) % kBigNst
+    const int next = stage == kBigNst - 1 ? 0 : stage + 1;
+    load_tile(kt + kBigNst - 1, ahead);
+    __builtin_amdgcn_sched_barrier(0);
+    read_slice(lds + stage * kBigStageBytes, 1, 1);
+    mfma_slice(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kInFlight>();  // tile kt + 1 is in LDS (later tiles may still be in flight)
+    big_barrier();            // ... for every wave, and every read of this stage is done
+    // (past the last step this reads a stage that nothing uses)
+    read_slice(lds + next * kBigStageBytes, 0, 0);
+    mfma_slice(1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    stage = next;
+  }
+  wait_vmcnt<0>();                       // the loads past the end have landed ...
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // ... and so have the unused last reads (lgkmcnt(0))
+  big_barrier();                         // before LDS is reused
+  // Epilogue as in gemm_tile: each 32 x 32 accumulator tile goes through a
+  // per-wave LDS area and leaves as rows.
+  float(*stage_f)[32][kStageLd] = reinterpret_cast<float(*)[32][kStageLd]>(lds);
+  float* out_f = g.partial ? g.partial + (long long)split * g.M * g.N : nullptr;
+  const long long ldo = g.partial ? g.N : g.ldc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage_f[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(&stage_f[wave][lane >> 1][16 * (lane & 1) + 4 * q]);
+        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const long long row = m0 + wm * 128 + i * 32 + (lane >> 1);
+      const int col = n0 + wn * 128 + j * 32 + 16 * (lane & 1);
+      if (out_f)
+        write_row16_vec<float>(out_f + row * ldo + col, v, false);
+      else
+        write_row16_vec<OutT>(static_cast<OutT*>(g.C) + row * ldo + col, v, g.accumulate != 0);
+    }
+}
+
+// grid (column tiles x row tiles x k splits), linear; tiles of one split go
+// to the XCDs in contiguous runs as in gemm_bf16_kernel
+template <bool A_K, bool B_K, typename OutT>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_kernel(GemmArgs g, int gx, int ntile) {
+  __shared__ __align__(1024) char lds[kBigLdsBytes];
+  const int split = blockIdx.x / ntile;
+  const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
+  gemm_big_tile<A_K, B_K, OutT>(g, (tile / gx) * kBigT, (tile % gx) * kBigT, split, lds);
+}
+
+// dX and dW of one linear layer in one launch with big tiles: blocks [0, nb1)
+// take product 1's tiles (one k split), the rest product 2's over its splits
+template <bool A1, bool B1, typename O1, bool A2, bool B2, typename O2>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_pair_kernel(GemmArgs g1, GemmArgs g2, int gx1, int nb1,
+                                                                        int gx2, int nt2) {
+  __shared__ __align__(1024) char lds[kBigLdsBytes];
+  const int id = blockIdx.x;
+  if (id < nb1) {
+    const int tile = xcd_tile(id, nb1);
+    gemm_big_tile<A1, B1, O1>(g1, (tile / gx1) * kBigT, (tile % gx1) * kBigT, 0, lds);
+  } else {
+    const int local = id - nb1, split = local / nt2;
+    const int tile = xcd_tile(local - split * nt2, nt2);
+    gemm_big_tile<A2, B2, O2>(g2, (tile / gx2) * kBigT, (tile % gx2) * kBigT, split, lds);
+  }
+}
+
 // grid (column tiles, row tiles, k splits)
 template <bool A_K, bool B_K, typename OutT, int BM, int BN>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
@@ -437,29 +752,40 @@ long gemm_device_cus() {
   return cus;
 }
 
-// Block tile height (256 or 128 rows; two or three blocks per CU) and k splits,
-// picked together from a cost model fitted to measured times of the layer's
-// products on the chip: the product's flops at a per-tile-size rate, stretched
-// when the last round of blocks leaves CUs idle, plus the split-k partial
-// traffic.  256-row tiles need at least 1024 rows and 512 k to pay for their
-// set-up; a split keeps at least 128 k.
+// Block tile (256 x 128 or 128 x 128 with two or three blocks per CU, or the
+// 256 x 256 tile at one block per CU for products made of whole tiles) and k
+// splits, picked together from a cost model fitted to measured times of the
+// layer's products on the chip: the product's flops at a per-tile-size rate,
+// stretched when the last round of blocks leaves CUs idle, plus the split-k
+// partial traffic.  256-row tiles need at least 1024 rows and 512 k to pay for
+// their set-up; a split keeps at least 128 k.
 struct TilePick {
   int bm, splits;
+  bool big;
 };
+
+// the 256 x 256 x 64 kernel takes the product: whole tiles in m and n, whole k
+// steps in k
+bool big_fits(int M, int N, int K) { return M % kBigT == 0 && N % kBigT == 0 && K % kBigK == 0 && K > 0; }
+
+constexpr double kRate128 = 500e12, kRate256 = 650e12, kRateBig = 1000e12;  // flop/s of the whole chip per tile size
 
 TilePick pick_tiles(int M, int N, int K) {
   static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
   const long cus = gemm_device_cus();
-  TilePick best{128, 1};
+  TilePick best{128, 1, false};
   double best_t = -1.0;
-  for (int bm : {128, 256}) {
-    if (bm == 256 && (M < 1024 || K < 512)) continue;
-    const double rate = bm == 256 ? 650e12 : 500e12;  // flop/s of the whole chip at this tile size
-    const double slots = (double)cus * (bm == 256 ? 2 : 3);
-    const double tiles = (double)((M + bm - 1) / bm) * ((N + 127) / 128);
+  for (int kind = 0; kind < 3; ++kind) {
+    const bool big = kind == 2;
+    const int bm = kind == 0 ? 128 : 256, bn = big ? kBigT : 128, kstep = big ? kBigK : kBK;
+    if (kind == 1 && (M < 1024 || K < 512)) continue;
+    if (big && !big_fits(M, N, K)) continue;
+    const double rate = big ? kRateBig : bm == 256 ? kRate256 : kRate128;
+    const double slots = (double)cus * (big ? 1 : bm == 256 ? 2 : 3);
+    const double tiles = (double)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     for (int s : kSplits) {
       if (s > 1 && K / s < 4 * kBK) break;
-      const int ks = ((K + s - 1) / s + kBK - 1) / kBK * kBK;
+      const int ks = ((K + s - 1) / s + kstep - 1) / kstep * kstep;
       const int used = (K + ks - 1) / ks;  // splits that get k
       const double r = tiles * used / slots, rounds = ceil(r);
       const double work = 2.0 * M * N * K / rate;
@@ -467,7 +793,7 @@ TilePick pick_tiles(int M, int N, int K) {
       if (used > 1) t += 2.0 * used * (double)M * N * 4.0 / 3e12;
       if (best_t < 0 || t < best_t) {
         best_t = t;
-        best = TilePick{bm, s};
+        best = TilePick{bm, s, big};
       }
     }
   }
@@ -477,10 +803,10 @@ TilePick pick_tiles(int M, int N, int K) {
 int pick_bm(int M, int N, int K) { return pick_tiles(M, N, K).bm; }
 int pick_splits(int M, int N, int K) { return K > 0 ? pick_tiles(M, N, K).splits : 1; }
 
-// k range per split (a multiple of kBK) and the partial buffer; returns the
+// k range per split (a multiple of the k step) and the partial buffer; returns the
 // number of splits that get k
-int gemm_prep(GemmArgs& g, int splits, float* partial) {
-  const int ksplit = max(kBK, ((g.K + splits - 1) / splits + kBK - 1) / kBK * kBK);
+int gemm_prep(GemmArgs& g, int splits, float* partial, int kstep = kBK) {
+  const int ksplit = max(kstep, ((g.K + splits - 1) / splits + kstep - 1) / kstep * kstep);
   g.k_per_split = ksplit;
   const int nsplit = (g.K + ksplit - 1) / ksplit;
   g.partial = nsplit > 1 ? partial : nullptr;
@@ -502,8 +828,18 @@ void gemm_reduce(const GemmArgs& g, int nsplit, float* partial, hipStream_t st) 
 template <bool A_K, bool B_K, typename OutT>
 int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) {
   GemmArgs g = g0;
-  const int nsplit = gemm_prep(g, splits, partial);
-  const int bm = pick_bm(g.M, g.N, g.K);
+  const TilePick tp = pick_tiles(g.M, g.N, g.K);
+  const int nsplit = gemm_prep(g, splits, partial, tp.big ? kBigK : kBK);
+  // the big tiles write 16-byte vectors only: an output they cannot take goes
+  // to the 256 x 128 tiles with the same k split
+  if (tp.big && (nsplit > 1 || g.vec_out)) {
+    const int gx = g.N / kBigT, ntile = gx * (g.M / kBigT);
+    hipLaunchKernelGGL((gemm_big_kernel<A_K, B_K, OutT>), dim3((unsigned)(ntile * nsplit)), dim3(kGemmThreads), 0,
+                       st, g, gx, ntile);
+    gemm_reduce<OutT>(g, nsplit, partial, st);
+    return SSM_OK;
+  }
+  const int bm = tp.big ? 256 : tp.bm;
   dim3 grid((g.N + 127) / 128, (g.M + bm - 1) / bm, nsplit);
   if (bm == 256)
     hipLaunchKernelGGL((gemm_bf16_kernel<A_K, B_K, OutT, 256, 128>), grid, dim3(kGemmThreads), 0, st, g);
@@ -590,27 +926,37 @@ double pair_makespan(long slots, long n1, double d1, long n2, double d2) {
   return end;
 }
 
-// dW's k split in the paired launch of linear_bwd_products (0: the products are
-// not paired), for an m x N output gradient and an N x K weight.  The products
-// pair when dX needs no k split and both pick the same tile height; the split
-// is then picked for the two products' blocks together: the modelled finish
-// time of the block schedule (a k step per block costing the same in both, 8
-// k steps of set-up per block, the tile rate of the single-product model) plus
-// the split-k partial traffic.
-int pair_dw_splits(int m, int K, int N) {
-  const int bm = pick_bm(m, K, N);
-  if (pick_splits(m, K, N) != 1 || pick_bm(N, K, m) != bm) return 0;
-  const int gx = (K + 127) / 128;
+// dW's k split in the paired launch of linear_bwd_products (splits 0: the
+// products are not paired), for an m x N output gradient and an N x K weight.
+// With big tiles when both products are made of whole 256 x 256 tiles and
+// 64-wide k steps; otherwise the products pair when dX needs no k split and
+// both pick the same tile height.  The split is picked for the two products'
+// blocks together: the modelled finish time of the block schedule (a k step
+// per block costing the same in both, a fixed set-up per block, the tile rate
+// of the single-product model) plus the split-k partial traffic.
+struct PairPick {
+  int splits;
+  bool big;
+};
+
+PairPick pair_dw_splits(int m, int K, int N) {
+  const bool big = big_fits(m, K, N) && big_fits(N, K, m);
+  const int bm = big ? kBigT : pick_bm(m, K, N), bn = big ? kBigT : 128;
+  const int kstep = big ? kBigK : kBK;
+  if (!big && (pick_splits(m, K, N) != 1 || pick_bm(N, K, m) != bm)) return PairPick{0, false};
+  const int gx = (K + bn - 1) / bn;
   const long nb1 = (long)gx * ((m + bm - 1) / bm), nt2 = (long)gx * ((N + bm - 1) / bm);
-  const long slots = gemm_device_cus() * (bm == 256 ? 2 : 3);
-  const double kstep_s = (double)bm * 128 * kBK * 2 / ((bm == 256 ? 650e12 : 500e12) / slots);
-  int best = pick_splits(N, K, m);
+  const long slots = gemm_device_cus() * (big ? 1 : bm == 256 ? 2 : 3);
+  const double rate = big ? kRateBig : bm == 256 ? kRate256 : kRate128;
+  const double kstep_s = (double)bm * bn * kstep * 2 / (rate / slots);
+  const double setup = big ? 4.0 : 8.0;  // k steps' worth of prologue and epilogue per block
+  int best = big ? 1 : pick_splits(N, K, m);
   double best_t = -1.0;
   for (int sp : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
     if (sp > 1 && m / sp < 4 * kBK) break;
-    const int ks = ((m + sp - 1) / sp + kBK - 1) / kBK * kBK;
+    const int ks = ((m + sp - 1) / sp + kstep - 1) / kstep * kstep;
     const int used = (m + ks - 1) / ks;
-    const double ms = pair_makespan(slots, nb1, (N + kBK - 1) / kBK + 8.0, nt2 * used, ks / kBK + 8.0);
+    const double ms = pair_makespan(slots, nb1, (N + kstep - 1) / kstep + setup, nt2 * used, ks / kstep + setup);
     if (ms < 0) continue;
     double t = ms * kstep_s;
     if (used > 1) t += 2.0 * used * (double)N * K * 4.0 / 3e12;
@@ -619,7 +965,7 @@ int pair_dw_splits(int m, int K, int N) {
       best = sp;
     }
   }
-  return best;
+  return PairPick{best, big};
 }
 
 // dX[M, K] = dY W and dW[N, K] = dY^T X of one linear layer: one launch for both
@@ -628,30 +974,39 @@ int pair_dw_splits(int m, int K, int N) {
 void linear_bwd_products(const void* X, long long ldx, const void* W, const void* dY, long long lddy, void* dX,
                          long long lddx, float* dW, int m, int K, int N, int acc_x, int acc_w, void* workspace,
                          hipStream_t st) {
-  const int s2 = (dX && dW) ? pair_dw_splits(m, K, N) : 0;
-  if (s2 == 0) {
+  PairPick pp = (dX && dW) ? pair_dw_splits(m, K, N) : PairPick{0, false};
+  // the big tiles write 16-byte vectors only (dW's partials always take them)
+  if (pp.big && !((aligned16(dX) && lddx % 8 == 0) && (pp.splits > 1 || aligned16(dW)))) pp.splits = 0;
+  if (pp.splits == 0) {
     if (dX) gemm_bf16(dY, true, lddy, W, false, K, dX, lddx, SSM_BF16, m, K, N, acc_x, workspace, st);
     if (dW) gemm_bf16(dY, false, lddy, X, false, ldx, dW, K, SSM_F32, N, K, m, acc_w, workspace, st);
     return;
   }
-  const int bm = pick_bm(m, K, N);
   const uint16_t* y16 = static_cast<const uint16_t*>(dY);
   GemmArgs g1{y16, static_cast<const uint16_t*>(W), dX, nullptr, lddy, K, lddx, m, K, N, 0, acc_x,
               aligned16(dX) && lddx % 8 == 0};
   GemmArgs g2{y16, static_cast<const uint16_t*>(X), dW, nullptr, lddy, ldx, K, N, K, m, 0, acc_w,
               aligned16(dW) && K % 4 == 0};
   float* part = static_cast<float*>(workspace);
-  gemm_prep(g1, 1, nullptr);
-  const int nsplit2 = gemm_prep(g2, s2, part);
-  const int gx = (K + 127) / 128;
-  const int nb1 = gx * ((m + bm - 1) / bm), nt2 = gx * ((N + bm - 1) / bm);
-  const dim3 grid((unsigned)(nb1 + nt2 * nsplit2));
-  if (bm == 256)
-    hipLaunchKernelGGL((gemm_pair_kernel<true, false, bf16, false, false, float, 256>), grid, dim3(kGemmThreads), 0,
-                       st, g1, g2, gx, nb1, gx, nt2);
-  else
-    hipLaunchKernelGGL((gemm_pair_kernel<true, false, bf16, false, false, float, 128>), grid, dim3(kGemmThreads), 0,
-                       st, g1, g2, gx, nb1, gx, nt2);
+  const int kstep = pp.big ? kBigK : kBK;
+  gemm_prep(g1, 1, nullptr, kstep);
+  const int nsplit2 = gemm_prep(g2, pp.splits, part, kstep);
+  if (pp.big) {
+    const int gx = K / kBigT, nb1 = gx * (m / kBigT), nt2 = gx * (N / kBigT);
+    hipLaunchKernelGGL((gemm_big_pair_kernel<true, false, bf16, false, false, float>),
+                       dim3((unsigned)(nb1 + nt2 * nsplit2)), dim3(kGemmThreads), 0, st, g1, g2, gx, nb1, gx, nt2);
+  } else {
+    const int bm = pick_bm(m, K, N);
+    const int gx = (K + 127) / 128;
+    const int nb1 = gx * ((m + bm - 1) / bm), nt2 = gx * ((N + bm - 1) / bm);
+    const dim3 grid((unsigned)(nb1 + nt2 * nsplit2));
+    if (bm == 256)
+      hipLaunchKernelGGL((gemm_pair_kernel<true, false, bf16, false, false, float, 256>), grid, dim3(kGemmThreads),
+                         0, st, g1, g2, gx, nb1, gx, nt2);
+    else
+      hipLaunchKernelGGL((gemm_pair_kernel<true, false, bf16, false, false, float, 128>), grid, dim3(kGemmThreads),
+                         0, st, g1, g2, gx, nb1, gx, nt2);
+  }
   gemm_reduce<float>(g2, nsplit2, part, st);
 }
 
@@ -682,7 +1037,7 @@ extern "C" size_t linear_bwd_workspace_size(int64_t M, int K, int N) {
   // dX = dY W (M x K, reduction N), dW = dY^T X (N x K, reduction M) and the db
   // column sums run one after another and share the space
   size_t a = gemm_workspace_bytes((int)M, K, N), b = gemm_workspace_bytes(N, K, (int)M);
-  const int s2 = pair_dw_splits((int)M, K, N);  // dW's split when paired with dX
+  const int s2 = pair_dw_splits((int)M, K, N).splits;  // dW's split when paired with dX
   if (s2 > 1) {
     const size_t bp = align_up((size_t)s2 * N * K * sizeof(float));
     b = bp > b ? bp : b;
@@ -715,7 +1070,7 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   // dW[N, K] = dY^T X: A(i = n, k = m) = dY[m * lddy + n], B(k = m, j) = X[m * ldx + j]
   if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
   if (dX && dW) {  // dX and dW in one launch: dW's split-k partials for the paired split
-    const int s2 = pair_dw_splits(m, K, N);
+    const int s2 = pair_dw_splits(m, K, N).splits;
     if (s2 > 1 && (!workspace || ws_bytes < align_up((size_t)s2 * N * K * sizeof(float)) || !aligned256(workspace)))
       return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the split-k partials missing, too small or not "
                                      "256-byte aligned");
