@@ -346,11 +346,12 @@ static_assert(kBigLdsBytes <= 160 * 1024 && kBigNst >= 2, "big tile stages");
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
-// s_waitcnt with only the vector memory count: vmcnt(n), n < 64
-template <int N>
+// s_waitcnt vmcnt(n), n < 64, and lgkmcnt(0) when `lds` (no wait on the
+// export count)
+template <int N, bool LDS = false>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | (LDS ? 0 : 0x0F00));
 }
 
 // One operand's 256 x kBigK tile.  Direct load q (0 .. kBigInstPerOp - 1 over
@@ -419,20 +420,13 @@ struct BigOperand {
   }
 };
 
-// the wave's direct loads of one operand tile into `area` (an LDS stage's
-// operand area); src: the tile origin in the matrix (wave-uniform), the lane's
-// byte offsets for even and odd loads
+// direct load qb (0 .. kBigInstPerOp - 1 over the block) of one operand tile
 template <bool KC>
-__device__ __forceinline__ void big_load(const uint16_t* src, long long ld, char* area, int wave, unsigned off_even,
-                                         unsigned off_odd) {
-  using Op = BigOperand<KC>;
-#pragma unroll
-  for (int q = 0; q < kBigInstPerWave; ++q) {
-    const int qb = wave * kBigInstPerWave + q;  // load index in the block
-    const char* p = reinterpret_cast<const char*>(src + (long long)qb * Op::kRowsPerInst * ld);
-    __builtin_amdgcn_global_load_lds((gbl_void_t)(p + ((qb & 1) ? off_odd : off_even)),
-                                     (lds_void_t)(area + qb * 1024), 16, 0, 0);
-  }
+__device__ __forceinline__ void big_load_one(const uint16_t* src, long long ld, char* area, int qb, unsigned off_even,
+                                             unsigned off_odd) {
+  const char* p = reinterpret_cast<const char*>(src + (long long)qb * BigOperand<KC>::kRowsPerInst * ld);
+  __builtin_amdgcn_global_load_lds((gbl_void_t)(p + ((qb & 1) ? off_odd : off_even)), (lds_void_t)(area + qb * 1024),
+                                   16, 0, 0);
 }
 
 // 16 consecutive outputs of one row from a 16-byte aligned column: the big
@@ -506,13 +500,17 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0,
   // k step kt's tile origin: KC operands move along the row, the others down k rows
   const long long a_step = A_K ? kBigK : kBigK * g.lda;
   const long long b_step = B_K ? kBigK : kBigK * g.ldb;
-  // tile kt (clamped to the last one: the loads past the end refill a stage
-  // that nothing reads again) into its stage
-  const auto load_tile = [&](int kt, int stage) {
+  // direct load i (0 .. 2 kBigInstPerWave - 1: A's loads, then B's) of the
+  // wave's share of tile kt (clamped to the last one: the loads past the end
+  // refill a stage that nothing reads again) into its stage
+  const auto load_one = [&](int kt, int stage, int i) {
     kt = min(kt, nk - 1);
     char* st = lds + stage * kBigStageBytes;
-    big_load<A_K>(a0 + kt * a_step, g.lda, st, wave, a_even, a_odd);
-    big_load<B_K>(b0 + kt * b_step, g.ldb, st + kBigOpBytes, wave, b_even, b_odd);
+    if (i < kBigInstPerWave)
+      big_load_one<A_K>(a0 + kt * a_step, g.lda, st, wave * kBigInstPerWave + i, a_even, a_odd);
+    else
+      big_load_one<B_K>(b0 + kt * b_step, g.ldb, st + kBigOpBytes, wave * kBigInstPerWave + i - kBigInstPerWave,
+                        b_even, b_odd);
   };
   unsigned fa_off[4], fb_off[4];
 #pragma unroll
@@ -520,65 +518,69 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0,
     fa_off[i] = OA::lane_frag(wm * 128, i, lane);
     fb_off[i] = OB::lane_frag(wn * 128, i, lane);
   }
-
-  static_assert(kBigK == 32, "the k loop below takes two 16-wide k slices per step");
-  constexpr int kReads = (A_K ? 4 : 8) + (B_K ? 4 : 8);  // LDS reads of one slice's operands
+  static_assert(kBigK == 32 && kBigInstPerWave == 4, "the k loop below takes two 16-wide k slices per step");
   bf16x8_t fa[2][4], fb[2][4];
-  const auto read_slice = [&](const char* st, int ks, int set) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      fa[set][t] = OA::frag(st, fa_off, t, ks);
-      fb[set][t] = OB::frag(st + kBigOpBytes, fb_off, t, ks);
-    }
+  // operand f (0..3: A's row tiles, 4..7: B's) of k slice ks into register set `set`
+  const auto read_frag = [&](const char* st, int ks, int set, int f) {
+    if (f < 4)
+      fa[set][f] = OA::frag(st, fa_off, f, ks);
+    else
+      fb[set][f - 4] = OB::frag(st + kBigOpBytes, fb_off, f - 4, ks);
   };
-  const auto mfma_slice = [&](int set) {
+  // A k slice's 16 products as eight fenced chunks of two, the other register
+  // set's reads in the first four chunks (two operands each, so every read has
+  // at least four chunks to land before its first use) and, with `loads`, one
+  // direct load of the step per chunk (spread over the step, not one burst
+  // into the address unit).  Without the fences the compiler sinks the reads
+  // behind the products to save registers.
+  const auto slice = [&](int set, const char* rd_stage, int rd_ks, int load_kt, int load_stage, bool loads) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < 8; ++c) {
+      if (loads) load_one(load_kt, load_stage, c);
+      if (c < 4) {
+        read_frag(rd_stage, rd_ks, set ^ 1, 2 * c);
+        read_frag(rd_stage, rd_ks, set ^ 1, 2 * c + 1);
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int e = 0; e < 2; ++e) {
+        const int i = (2 * c + e) >> 2, j = (2 * c + e) & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
-  };
-  // a slice's 16 products with the other set's reads woven in, two after each
-  // of the first products, so the reads land while the matrix cores work
-  const auto interleave = [&]() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one MFMA
-      if (2 * i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
 #pragma unroll
-  for (int s = 0; s < kBigNst - 1; ++s) load_tile(s, s);
-  wait_vmcnt<kInFlight>();  // tile 0 is in LDS
-  big_barrier();
-  read_slice(lds, 0, 0);
+  for (int s = 0; s < kBigNst - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < 2 * kBigInstPerWave; ++i) load_one(s, s, i);
+  wait_vmcnt<kInFlight>();  // tile 0 is in LDS ...
+  big_barrier();            // ... for every wave
+#pragma unroll
+  for (int f = 0; f < 8; ++f) read_frag(lds, 0, 0, f);
   // One k step per iteration, with no branch inside, so the accumulators stay
-  // in their registers across iterations.  Software pipelined over the two
-  // k slices of a step: slice 1's operand reads run under slice 0's products,
-  // and after the barrier the next step's slice-0 reads run under slice 1's.
+  // in their registers across iterations.  Software pipelined over the two k
+  // slices of a step: slice 1's operand reads and the direct loads of tile kt +
+  // kBigNst - 1 run under slice 0's products, and after the barrier the next
+  // step's slice-0 reads run under slice 1's.  The stage those loads refill was
+  // last read before the previous barrier, where every wave arrived only after
+  // its own reads had landed.
   int stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = stage == 0 ? kBigNst - 1 : stage - 1;  // (kt + kBigNst - 1) % kBigNst
     const int next = stage == kBigNst - 1 ? 0 : stage + 1;
-    load_tile(kt + kBigNst - 1, ahead);
     __builtin_amdgcn_sched_barrier(0);
-    read_slice(lds + stage * kBigStageBytes, 1, 1);
-    mfma_slice(0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kInFlight>();  // tile kt + 1 is in LDS (later tiles may still be in flight)
-    big_barrier();            // ... for every wave, and every read of this stage is done
+    slice(0, lds + stage * kBigStageBytes, 1, kt + kBigNst - 1, ahead, true);
+    // tile kt + 1 is in LDS (later tiles may still be in flight) and this
+    // wave's reads of the stage are done; after the barrier, for every wave
+    wait_vmcnt<kInFlight, true>();
+    big_barrier();
     // (past the last step this reads a stage that nothing uses)
-    read_slice(lds + next * kBigStageBytes, 0, 0);
-    mfma_slice(1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
+    slice(1, lds + next * kBigStageBytes, 0, 0, 0, false);
     stage = next;
   }
-  wait_vmcnt<0>();                       // the loads past the end have landed ...
-  __builtin_amdgcn_s_waitcnt(0xC07F);    // ... and so have the unused last reads (lgkmcnt(0))
-  big_barrier();                         // before LDS is reused
+  wait_vmcnt<0, true>();  // the loads past the end and the unused last reads have landed
+  big_barrier();           // before LDS is reused
   // Epilogue as in gemm_tile: each 32 x 32 accumulator tile goes through a
   // per-wave LDS area and leaves as rows.
   float(*stage_f)[32][kStageLd] = reinterpret_cast<float(*)[32][kStageLd]>(lds);
