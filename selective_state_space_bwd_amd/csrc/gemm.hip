@@ -41,6 +41,7 @@ struct GemmArgs {
   int k_per_split;  // multiple of kBK
   int accumulate;   // add into C instead of overwriting (the split-k sum adds it)
   int vec_out;      // C rows allow 16-byte vectors (aligned base, ldc a multiple of the vector)
+  float* colsum;    // big tiles: sums of A over k per row, [splits, M] with partials (or null)
 };
 
 // one 16-byte chunk (8 bf16) of a matrix row, zero outside [0, rows) x [0, cols)
@@ -321,27 +322,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, int
     }
 }
 
-// ---- 256 x 256 tiles for products made of whole tiles ----------------------
-// Four waves, each owning a 128 x 128 quarter of the block tile as 4 x 4
-// v_mfma_f32_32x32x16_bf16 tiles (256 accumulator registers per lane, which the
-// gfx950 register file holds at one wave per SIMD).  Operand tiles reach LDS by
-// direct global -> LDS loads (global_load_lds_dwordx4: lane i of an instruction
-// writes 16 bytes at the instruction's LDS base + 16 i), so no registers stage
-// them; each lane picks which 16-byte chunk of the tile it fetches, and that
-// choice sets the LDS layout.  kBigNst LDS stages: the loads of tile k +
-// kBigNst - 1 are issued while the matrix cores work on tile k, so a load has
-// kBigNst - 1 k steps to arrive.  Against the 256 x 128 tile this halves the
+// ---- 256 x BN tiles with direct global -> LDS loads --------------------------
+// Block tile 256 x BN (BN 256 or 128), four waves in a 2 x 2 grid, each owning
+// a 128 x BN/2 part of it as v_mfma_f32_32x32x16_bf16 tiles (up to 256
+// accumulator registers per lane, which the gfx950 register file holds at one
+// wave per SIMD).  Operand tiles reach LDS by direct global -> LDS loads
+// (global_load_lds_dwordx4: lane i of an instruction writes 16 bytes at the
+// instruction's LDS base + 16 i), so no registers stage them; each lane picks
+// which 16-byte chunk of the tile it fetches, and that choice sets the LDS
+// layout.  Several LDS stages: the loads of tile k + stages - 1 are issued while
+// the matrix cores work on tile k, so a load has stages - 1 k steps to arrive;
+// the 128-wide tile, used for streaming products with a narrow side, gets six.
+// Against the 256 x 128 register-staged tile the 256 x 256 one halves the
 // operand bytes per flop and cuts the LDS operand reads per flop by a quarter.
-constexpr int kBigT = 256;                              // block tile rows and columns
-constexpr int kBigK = 32;                               // k per step
-constexpr int kBigNst = 4;                              // LDS stages
-constexpr int kBigOpBytes = kBigT * kBigK * 2;          // one operand's tile in one stage
-constexpr int kBigStageBytes = 2 * kBigOpBytes;         // A and B
-constexpr int kBigLdsBytes = kBigNst * kBigStageBytes;  // 128 KB
-constexpr int kBigInstPerOp = kBigOpBytes / 1024;       // 1 KB direct loads per operand tile
-constexpr int kBigInstPerWave = kBigInstPerOp / 4;      // ... per wave
-static_assert(kBigK % 16 == 0 && (kBigK == 32 || kBigK == 64) && kBigInstPerOp % 4 == 0, "big tile shape");
-static_assert(kBigLdsBytes <= 160 * 1024 && kBigNst >= 2, "big tile stages");
+constexpr int kBigT = 256;  // block tile rows (the A side)
+constexpr int kBigK = 32;   // k per step
+
+template <int BN>
+struct BigCfg {
+  static_assert(BN == 256 || BN == 128, "big tile width");
+  static constexpr int kNst = BN == 256 ? 4 : 6;                     // LDS stages
+  static constexpr int kABytes = kBigT * kBigK * 2;                  // A's tile in one stage
+  static constexpr int kBBytes = BN * kBigK * 2;                     // B's tile in one stage
+  static constexpr int kStageBytes = kABytes + kBBytes;
+  static constexpr int kOnesBytes = BN == 128 ? kBBytes : 0;        // constant B tile for column sums
+  static constexpr int kLdsBytes = kNst * kStageBytes + kOnesBytes;  // 128 KB / 152 KB
+  static constexpr int kAInst = kABytes / 1024 / 4;                  // direct loads per wave and stage
+  static constexpr int kBInst = kBBytes / 1024 / 4;
+  static constexpr int kTN = BN / 64;                                // 32-wide n tiles per wave
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
@@ -354,34 +364,34 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | (LDS ? 0 : 0x0F00));
 }
 
-// One operand's 256 x kBigK tile.  Direct load q (0 .. kBigInstPerOp - 1 over
-// the block) fills LDS bytes [1024 q, 1024 q + 1024) of the operand's area.
-// KC (k contiguous): LDS [row][k], kRowBytes per row; 16-byte chunk c of row r
-//   sits in slot c ^ ((r >> kShift) & (kChunks - 1)).  A fragment read takes one
-//   chunk of 16 consecutive rows per 16 lanes, which then hit 16 different
-//   16-byte bank groups (the row's place in a 256-byte line and the XOR
-//   together enumerate them).
-// Otherwise: LDS [k][row], 512 bytes per k row; chunk c (8 tile rows) of k row
-//   k sits in slot c ^ ((k & 3) << 2).  A transposing read takes four k rows x
+// One operand's R x 32 tile (R tile rows, 32 k).  Direct load q (0 .. kInst - 1
+// over the block) fills LDS bytes [1024 q, 1024 q + 1024) of the operand's area.
+// KC (k contiguous): LDS [row][k], 64 bytes per row; 16-byte chunk c of row r
+//   sits in slot c ^ ((r >> 2) & 3).  A fragment read takes one chunk of 16
+//   consecutive rows per 16 lanes, which then hit 16 different 16-byte bank
+//   groups (the row's place in a 256-byte line and the XOR together
+//   enumerate them).
+// Otherwise: LDS [k][row], 2R bytes per k row; chunk c (8 tile rows) of k row k
+//   sits in slot c ^ ((k & 3) << 2).  A transposing read takes four k rows x
 //   four chunks per 32 lanes, which land in 16 different bank groups.
-template <bool KC>
+template <bool KC, int R>
 struct BigOperand {
-  static constexpr int kRowBytes = kBigK * 2;             // KC
-  static constexpr int kChunks = kBigK / 8;               // KC: 16-byte chunks per row
-  static constexpr int kShift = kChunks == 8 ? 1 : 2;     // KC: rows sharing a 256-byte line
-  static constexpr int kRowsPerInst = KC ? 1024 / kRowBytes : 2;
-  static __device__ __forceinline__ int kc_swz(int r) { return (r >> kShift) & (kChunks - 1); }
-  // byte offset (from the tile origin) of the chunk lane `lane` fetches for a
-  // direct load of parity `odd`; the rest of the offset is uniform: q x
-  // kRowsPerInst x the row stride
-  static __device__ __forceinline__ unsigned lane_src(long long ld, int lane, int odd) {
-    if (KC) {
-      const int r = odd * kRowsPerInst + lane / kChunks;  // the swizzle of row q * kRowsPerInst + r
-      return (unsigned)(((lane / kChunks) * ld + (((lane % kChunks) ^ kc_swz(r)) << 3)) * 2);
-    } else {
-      const int s = lane & 31, x = (odd * 2 + (lane >> 5)) << 2;
-      return (unsigned)(((lane >> 5) * ld + ((s ^ x) << 3)) * 2);
-    }
+  static constexpr int kChunksPerRow = KC ? kBigK / 8 : R / 8;  // 16-byte chunks per LDS row
+  static constexpr int kRowBytes = kChunksPerRow * 16;
+  static constexpr int kRowsPerInst = 1024 / kRowBytes;
+  static constexpr int kInst = R * kBigK * 2 / 1024;
+  static __device__ __forceinline__ int swz(int row) { return KC ? ((row >> 2) & 3) : ((row & 3) << 2); }
+  // Byte offset (from the tile origin) of the chunk that lane `lane` fetches
+  // for a direct load of parity `odd`; the rest of the offset is uniform: q x
+  // kRowsPerInst x the row stride.  Otherwise-layout tiles with only `valid`
+  // rows (a multiple of 8) in the matrix fetch chunk 0 of their k row in place
+  // of the chunks past it: the loads stay inside the matrix, and the LDS rows
+  // past `valid` hold values that only reach outputs the epilogue drops.
+  static __device__ __forceinline__ unsigned lane_src(long long ld, int lane, int odd, int valid) {
+    const int row = odd * kRowsPerInst + lane / kChunksPerRow;  // same swizzle as row q * kRowsPerInst + ...
+    int c = (lane % kChunksPerRow) ^ swz(row);
+    if (!KC && c * 8 >= valid) c = 0;
+    return (unsigned)(((lane / kChunksPerRow) * ld + (c << 3)) * 2);
   }
   // the tile origin's element offset in the matrix
   static __device__ __forceinline__ long long origin(long long ld, int row0, int k0) {
@@ -391,18 +401,18 @@ struct BigOperand {
   // rows base + t * 32 .. + 31 at k 16 ks .. + 15; see OperandTile::frag for
   // the lane -> (row, k) map.  KC: one 16-byte read, and t only adds 32 rows,
   // so a lane keeps one offset per ks.  Otherwise: two 8-byte transposing
-  // reads, the second 4 k rows (2048 bytes) further, and ks only adds 8192
-  // bytes, so a lane keeps one offset per t.
+  // reads, the second 4 k rows further, and ks only adds 16 k rows, so a lane
+  // keeps one offset per t.
   static __device__ __forceinline__ unsigned lane_frag(int base, int i, int lane) {
     if (KC) {  // i = ks
       const int r = base + (lane & 31);
       const int c = i * 2 + (lane >> 5);
-      return (unsigned)(r * kRowBytes + ((c ^ kc_swz(r)) << 4));
+      return (unsigned)(r * kRowBytes + ((c ^ swz(r)) << 4));
     } else {   // i = t
       const int grp = lane >> 4, j = lane & 15;
       const int k = 8 * (grp >> 1) + (j >> 2);
       const int r = base + i * 32 + 16 * (grp & 1) + 4 * (j & 3);
-      return (unsigned)(k * 512 + (((r >> 3) ^ ((k & 3) << 2)) << 4) + (r & 7) * 2);
+      return (unsigned)(k * kRowBytes + (((r >> 3) ^ swz(k)) << 4) + (r & 7) * 2);
     }
   }
   static __device__ __forceinline__ bf16x8_t frag(const char* __restrict__ area, const unsigned (&off)[4], int t,
@@ -411,26 +421,33 @@ struct BigOperand {
       return *reinterpret_cast<const bf16x8_t*>(area + off[ks] + t * 32 * kRowBytes);
     } else {
       typedef __attribute__((address_space(3))) v4i16_t lds_v4;
-      const char* p = area + off[t] + ks * 8192;
+      const char* p = area + off[t] + ks * 16 * kRowBytes;
       const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p));
-      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 2048));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 4 * kRowBytes));
       const v4i16_t lohi[2] = {lo, hi};
       return *reinterpret_cast<const bf16x8_t*>(lohi);
     }
   }
+  // value the otherwise-layout byte offset p of a tile holds in the constant
+  // tile whose row `one` is 1 and the rest 0 (bf16 bit patterns, as a 16-bit
+  // element of the tile's LDS image)
+  static __device__ __forceinline__ uint16_t ones_image(int p, int one) {
+    const int k = p / kRowBytes, c = ((p % kRowBytes) >> 4) ^ swz(k);
+    return (c * 8 + ((p & 15) >> 1)) == one ? uint16_t(0x3F80) : uint16_t(0);
+  }
 };
 
-// direct load qb (0 .. kBigInstPerOp - 1 over the block) of one operand tile
-template <bool KC>
+// direct load qb (0 .. kInst - 1 over the block) of one operand tile
+template <bool KC, int R>
 __device__ __forceinline__ void big_load_one(const uint16_t* src, long long ld, char* area, int qb, unsigned off_even,
                                              unsigned off_odd) {
-  const char* p = reinterpret_cast<const char*>(src + (long long)qb * BigOperand<KC>::kRowsPerInst * ld);
+  const char* p = reinterpret_cast<const char*>(src + (long long)qb * BigOperand<KC, R>::kRowsPerInst * ld);
   __builtin_amdgcn_global_load_lds((gbl_void_t)(p + ((qb & 1) ? off_odd : off_even)), (lds_void_t)(area + qb * 1024),
                                    16, 0, 0);
 }
 
 // 16 consecutive outputs of one row from a 16-byte aligned column: the big
-// tiles' epilogue (whole tiles, rows that take 16-byte vectors)
+// tiles' epilogue (rows that take 16-byte vectors)
 template <typename T>
 __device__ __forceinline__ void write_row16_vec(T* __restrict__ p, const float (&v)[16], bool accumulate) {
   if constexpr (sizeof(T) == 4) {
@@ -474,109 +491,152 @@ __device__ __forceinline__ void big_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool A_K, bool B_K, typename OutT>
+// One 256 x BN output tile at rows m0.., columns n0.., over k split `split`.
+// Rows and k are whole tiles and steps (checked by the dispatcher); columns
+// may end inside the tile (g.N a multiple of 16, B not k-contiguous).  With
+// g.colsum, the B operand's column g.N (past the last output) is taken as all
+// ones, so that output column is the sum of A over k: written to
+// g.colsum[split * M + row].
+template <bool A_K, bool B_K, typename OutT, int BN>
 __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0, int split, char* __restrict__ lds) {
-  using OA = BigOperand<A_K>;
-  using OB = BigOperand<B_K>;
-  constexpr int kInFlight = (kBigNst - 2) * 2 * kBigInstPerWave;  // loads of later stages allowed outstanding
+  using Cfg = BigCfg<BN>;
+  using OA = BigOperand<A_K, kBigT>;
+  using OB = BigOperand<B_K, BN>;
+  constexpr int TN = Cfg::kTN;
+  constexpr int kLoads = Cfg::kAInst + Cfg::kBInst;          // per wave and stage
+  constexpr int kInFlight = (Cfg::kNst - 2) * kLoads;        // loads of later stages allowed outstanding
+  static_assert(kLoads <= 8 && kInFlight < 64, "loads per step");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int kb = split * g.k_per_split;
   const int nk = min(g.k_per_split, g.K - kb) / kBigK;  // whole k steps (checked by the dispatcher)
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][TN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const unsigned a_even = OA::lane_src(g.lda, lane, 0), a_odd = OA::lane_src(g.lda, lane, 1);
-  const unsigned b_even = OB::lane_src(g.ldb, lane, 0), b_odd = OB::lane_src(g.ldb, lane, 1);
+  const int b_valid = min(BN, g.N - n0);
+  const unsigned a_even = OA::lane_src(g.lda, lane, 0, kBigT), a_odd = OA::lane_src(g.lda, lane, 1, kBigT);
+  const unsigned b_even = OB::lane_src(g.ldb, lane, 0, b_valid), b_odd = OB::lane_src(g.ldb, lane, 1, b_valid);
   const uint16_t* a0 = g.A + OA::origin(g.lda, m0, kb);
   const uint16_t* b0 = g.B + OB::origin(g.ldb, n0, kb);
   // k step kt's tile origin: KC operands move along the row, the others down k rows
   const long long a_step = A_K ? kBigK : kBigK * g.lda;
   const long long b_step = B_K ? kBigK : kBigK * g.ldb;
-  // direct load i (0 .. 2 kBigInstPerWave - 1: A's loads, then B's) of the
-  // wave's share of tile kt (clamped to the last one: the loads past the end
-  // refill a stage that nothing reads again) into its stage
+  // direct load i (A's loads, then B's) of the wave's share of tile kt (clamped
+  // to the last one: the loads past the end refill a stage that nothing reads
+  // again) into its stage
   const auto load_one = [&](int kt, int stage, int i) {
     kt = min(kt, nk - 1);
-    char* st = lds + stage * kBigStageBytes;
-    if (i < kBigInstPerWave)
-      big_load_one<A_K>(a0 + kt * a_step, g.lda, st, wave * kBigInstPerWave + i, a_even, a_odd);
+    char* st = lds + stage * Cfg::kStageBytes;
+    if (i < Cfg::kAInst)
+      big_load_one<A_K, kBigT>(a0 + kt * a_step, g.lda, st, wave * Cfg::kAInst + i, a_even, a_odd);
     else
-      big_load_one<B_K>(b0 + kt * b_step, g.ldb, st + kBigOpBytes, wave * kBigInstPerWave + i - kBigInstPerWave,
-                        b_even, b_odd);
+      big_load_one<B_K, BN>(b0 + kt * b_step, g.ldb, st + Cfg::kABytes, wave * Cfg::kBInst + i - Cfg::kAInst, b_even,
+                            b_odd);
   };
   unsigned fa_off[4], fb_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     fa_off[i] = OA::lane_frag(wm * 128, i, lane);
-    fb_off[i] = OB::lane_frag(wn * 128, i, lane);
+    fb_off[i] = OB::lane_frag(wn * (BN / 2), i, lane);
   }
-  static_assert(kBigK == 32 && kBigInstPerWave == 4, "the k loop below takes two 16-wide k slices per step");
-  bf16x8_t fa[2][4], fb[2][4];
-  // operand f (0..3: A's row tiles, 4..7: B's) of k slice ks into register set `set`
+  // the column-sum tile: the n tile of this wave that holds column g.N reads its
+  // B operand from the constant tile instead of the stage
+  char* ones = lds + Cfg::kNst * Cfg::kStageBytes;
+  int ones_t = -1;
+  if constexpr (Cfg::kOnesBytes > 0) {
+    if (g.colsum) {
+      const int t = (g.N - n0 - wn * (BN / 2)) / 32;
+      if (g.N - n0 - wn * (BN / 2) >= 0 && t < TN) ones_t = t;
+      for (int p = 2 * tid; p < Cfg::kOnesBytes; p += 2 * kGemmThreads)
+        *reinterpret_cast<uint16_t*>(ones + p) = OB::ones_image(p, g.N - n0);
+    }
+  }
+  bf16x8_t fa[2][4], fb[2][TN];
+  // operand f (0..3: A's row tiles, 4..: B's) of k slice ks into register set `set`
   const auto read_frag = [&](const char* st, int ks, int set, int f) {
-    if (f < 4)
+    if (f < 4) {
       fa[set][f] = OA::frag(st, fa_off, f, ks);
-    else
-      fb[set][f - 4] = OB::frag(st + kBigOpBytes, fb_off, f - 4, ks);
+    } else if (f - 4 < TN) {
+      const char* area = (f - 4 == ones_t) ? ones : st + Cfg::kABytes;
+      fb[set][f - 4] = OB::frag(area, fb_off, f - 4, ks);
+    }
   };
-  // A k slice's 16 products as eight fenced chunks of two, the other register
-  // set's reads in the first four chunks (two operands each, so every read has
-  // at least four chunks to land before its first use) and, with `loads`, one
+  // A k slice's 4 x TN products as eight fenced chunks, the other register
+  // set's reads in the first chunks (two operands each, so every read has at
+  // least half the slice to land before its first use) and, with `loads`, one
   // direct load of the step per chunk (spread over the step, not one burst
   // into the address unit).  Without the fences the compiler sinks the reads
   // behind the products to save registers.
   const auto slice = [&](int set, const char* rd_stage, int rd_ks, int load_kt, int load_stage, bool loads) {
+    constexpr int P = 4 * TN / 8;  // products per chunk
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if (loads) load_one(load_kt, load_stage, c);
-      if (c < 4) {
-        read_frag(rd_stage, rd_ks, set ^ 1, 2 * c);
-        read_frag(rd_stage, rd_ks, set ^ 1, 2 * c + 1);
-      }
+      if (loads && c < kLoads) load_one(load_kt, load_stage, c);
+      read_frag(rd_stage, rd_ks, set ^ 1, 2 * c);
+      read_frag(rd_stage, rd_ks, set ^ 1, 2 * c + 1);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = (2 * c + e) >> 2, j = (2 * c + e) & 3;
+      for (int e = 0; e < P; ++e) {
+        const int i = (P * c + e) / TN, j = (P * c + e) % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // A bf16 output that is added to: its old values are loaded now, ahead of the
+  // first stage's direct loads (so the wait for tile 0 also covers them), and
+  // held through the k loop, instead of one dependent load per tile in the
+  // epilogue.  Lane: row lane / 2, 16 columns from 16 (lane % 2) of each tile.
+  constexpr bool kPrefetch = sizeof(OutT) == 2;
+  uint4 prev[4][TN][2];
+  const bool prefetch = kPrefetch && !g.partial && g.accumulate;
+  if (kPrefetch && prefetch) {
 #pragma unroll
-  for (int s = 0; s < kBigNst - 1; ++s)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 2 * kBigInstPerWave; ++i) load_one(s, s, i);
-  wait_vmcnt<kInFlight>();  // tile 0 is in LDS ...
+      for (int j = 0; j < TN; ++j) {
+        const long long row = m0 + wm * 128 + i * 32 + (lane >> 1);
+        const int col = n0 + wn * (BN / 2) + j * 32 + 16 * (lane & 1);
+        const uint4* q = reinterpret_cast<const uint4*>(static_cast<const OutT*>(g.C) + row * g.ldc + col);
+        prev[i][j][0] = col < g.N ? q[0] : make_uint4(0, 0, 0, 0);
+        prev[i][j][1] = col < g.N ? q[1] : make_uint4(0, 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int s = 0; s < Cfg::kNst - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_one(s, s, i);
+  wait_vmcnt<kInFlight>();  // tile 0 is in LDS (and so is the constant tile) ...
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   big_barrier();            // ... for every wave
 #pragma unroll
-  for (int f = 0; f < 8; ++f) read_frag(lds, 0, 0, f);
+  for (int f = 0; f < 4 + TN; ++f) read_frag(lds, 0, 0, f);
   // One k step per iteration, with no branch inside, so the accumulators stay
   // in their registers across iterations.  Software pipelined over the two k
   // slices of a step: slice 1's operand reads and the direct loads of tile kt +
-  // kBigNst - 1 run under slice 0's products, and after the barrier the next
+  // stages - 1 run under slice 0's products, and after the barrier the next
   // step's slice-0 reads run under slice 1's.  The stage those loads refill was
   // last read before the previous barrier, where every wave arrived only after
   // its own reads had landed.
   int stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = stage == 0 ? kBigNst - 1 : stage - 1;  // (kt + kBigNst - 1) % kBigNst
-    const int next = stage == kBigNst - 1 ? 0 : stage + 1;
+    const int ahead = stage == 0 ? Cfg::kNst - 1 : stage - 1;  // (kt + stages - 1) % stages
+    const int next = stage == Cfg::kNst - 1 ? 0 : stage + 1;
     __builtin_amdgcn_sched_barrier(0);
-    slice(0, lds + stage * kBigStageBytes, 1, kt + kBigNst - 1, ahead, true);
+    slice(0, lds + stage * Cfg::kStageBytes, 1, kt + Cfg::kNst - 1, ahead, true);
     // tile kt + 1 is in LDS (later tiles may still be in flight) and this
     // wave's reads of the stage are done; after the barrier, for every wave
     wait_vmcnt<kInFlight, true>();
     big_barrier();
     // (past the last step this reads a stage that nothing uses)
-    slice(1, lds + next * kBigStageBytes, 0, 0, 0, false);
+    slice(1, lds + next * Cfg::kStageBytes, 0, 0, 0, false);
     stage = next;
   }
   wait_vmcnt<0, true>();  // the loads past the end and the unused last reads have landed
@@ -589,7 +649,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0,
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) stage_f[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = acc[i][j][r];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -603,38 +663,58 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0,
       }
       __builtin_amdgcn_wave_barrier();
       const long long row = m0 + wm * 128 + i * 32 + (lane >> 1);
-      const int col = n0 + wn * 128 + j * 32 + 16 * (lane & 1);
-      if (out_f)
-        write_row16_vec<float>(out_f + row * ldo + col, v, false);
-      else
-        write_row16_vec<OutT>(static_cast<OutT*>(g.C) + row * ldo + col, v, g.accumulate != 0);
+      const int col = n0 + wn * (BN / 2) + j * 32 + 16 * (lane & 1);
+      if (col < g.N) {
+        if (out_f) {
+          write_row16_vec<float>(out_f + row * ldo + col, v, false);
+        } else if (kPrefetch && prefetch) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t pw[4] = {prev[i][j][q].x, prev[i][j][q].y, prev[i][j][q].z, prev[i][j][q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[8 * q + 2 * e] += __uint_as_float(pw[e] << 16);
+              v[8 * q + 2 * e + 1] += __uint_as_float(pw[e] & 0xffff0000u);
+            }
+          }
+          write_row16_vec<OutT>(static_cast<OutT*>(g.C) + row * ldo + col, v, false);
+        } else {
+          write_row16_vec<OutT>(static_cast<OutT*>(g.C) + row * ldo + col, v, g.accumulate != 0);
+        }
+      } else if (j == ones_t && col == g.N) {
+        float* cs = g.colsum + (long long)split * g.M + row;
+        *cs = (g.partial || !g.accumulate) ? v[0] : *cs + v[0];
+      }
     }
 }
 
 // grid (column tiles x row tiles x k splits), linear; tiles of one split go
 // to the XCDs in contiguous runs as in gemm_bf16_kernel
-template <bool A_K, bool B_K, typename OutT>
+template <bool A_K, bool B_K, typename OutT, int BN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_kernel(GemmArgs g, int gx, int ntile) {
-  __shared__ __align__(1024) char lds[kBigLdsBytes];
+  __shared__ __align__(1024) char lds[BigCfg<BN>::kLdsBytes];
   const int split = blockIdx.x / ntile;
   const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
-  gemm_big_tile<A_K, B_K, OutT>(g, (tile / gx) * kBigT, (tile % gx) * kBigT, split, lds);
+  gemm_big_tile<A_K, B_K, OutT, BN>(g, (tile / gx) * kBigT, (tile % gx) * BN, split, lds);
 }
 
-// dX and dW of one linear layer in one launch with big tiles: blocks [0, nb1)
-// take product 1's tiles (one k split), the rest product 2's over its splits
-template <bool A1, bool B1, typename O1, bool A2, bool B2, typename O2>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_pair_kernel(GemmArgs g1, GemmArgs g2, int gx1, int nb1,
-                                                                        int gx2, int nt2) {
-  __shared__ __align__(1024) char lds[kBigLdsBytes];
+// Two products in one launch (a linear layer's dX and dW): blocks [0, nb1)
+// take product 1's tiles over its k splits (nt1 tiles per split), the rest
+// product 2's (nt2 per split)
+template <bool A1, bool B1, typename O1, int BN1, bool A2, bool B2, typename O2, int BN2>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_pair_kernel(GemmArgs g1, GemmArgs g2, int gx1, int nt1,
+                                                                        int nb1, int gx2, int nt2) {
+  constexpr int L1 = BigCfg<BN1>::kLdsBytes, L2 = BigCfg<BN2>::kLdsBytes;
+  __shared__ __align__(1024) char lds[L1 > L2 ? L1 : L2];
   const int id = blockIdx.x;
   if (id < nb1) {
-    const int tile = xcd_tile(id, nb1);
-    gemm_big_tile<A1, B1, O1>(g1, (tile / gx1) * kBigT, (tile % gx1) * kBigT, 0, lds);
+    const int split = id / nt1;
+    const int tile = xcd_tile(id - split * nt1, nt1);
+    gemm_big_tile<A1, B1, O1, BN1>(g1, (tile / gx1) * kBigT, (tile % gx1) * BN1, split, lds);
   } else {
     const int local = id - nb1, split = local / nt2;
     const int tile = xcd_tile(local - split * nt2, nt2);
-    gemm_big_tile<A2, B2, O2>(g2, (tile / gx2) * kBigT, (tile % gx2) * kBigT, split, lds);
+    gemm_big_tile<A2, B2, O2, BN2>(g2, (tile / gx2) * kBigT, (tile % gx2) * BN2, split, lds);
   }
 }
 
@@ -698,6 +778,34 @@ __global__ __launch_bounds__(256) void splitk_reduce1(const float* __restrict__ 
   for (int s = 0; s < splits; ++s) acc += part[(long long)s * M * N + idx];
   OutT* c = C + (long long)row * ldc + col;
   *c = from_f32<OutT>((accumulate ? to_f32(*c) : 0.f) + acc);
+}
+
+// the same for a partial plane [splits, M, N] whose sum lands transposed:
+// C[n * ldc + m] (+)= sum_s part[s][m][n], through a 32 x 32 LDS tile so that
+// both the partial reads and the output writes are row-contiguous
+__global__ __launch_bounds__(256) void splitk_reduce_t(const float* __restrict__ part, float* __restrict__ C,
+                                                       long long ldc, int M, int N, int splits, int accumulate) {
+  __shared__ float t[32][33];
+  const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8 threads
+  const long long plane = (long long)M * N;
+#pragma unroll
+  for (int r = ty; r < 32; r += 8) {
+    const int m = m0 + r, n = n0 + tx;
+    float a = 0.f;
+    if (m < M && n < N)
+      for (int s = 0; s < splits; ++s) a += part[s * plane + (long long)m * N + n];
+    t[r][tx] = a;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = ty; r < 32; r += 8) {
+    const int n = n0 + r, m = m0 + tx;
+    if (m < M && n < N) {
+      float* c = C + (long long)n * ldc + m;
+      *c = (accumulate ? *c : 0.f) + t[tx][r];
+    }
+  }
 }
 
 // column sums of a [M, N] matrix (bias gradient) in two fixed-order passes:
@@ -766,8 +874,7 @@ struct TilePick {
   bool big;
 };
 
-// the 256 x 256 x 64 kernel takes the product: whole tiles in m and n, whole k
-// steps in k
+// the 256 x 256 tiles take the product: whole tiles in m and n, whole k steps in k
 bool big_fits(int M, int N, int K) { return M % kBigT == 0 && N % kBigT == 0 && K % kBigK == 0 && K > 0; }
 
 constexpr double kRate128 = 500e12, kRate256 = 650e12, kRateBig = 1000e12;  // flop/s of the whole chip per tile size
@@ -836,7 +943,7 @@ int launch_gemm(const GemmArgs& g0, int splits, float* partial, hipStream_t st) 
   // to the 256 x 128 tiles with the same k split
   if (tp.big && (nsplit > 1 || g.vec_out)) {
     const int gx = g.N / kBigT, ntile = gx * (g.M / kBigT);
-    hipLaunchKernelGGL((gemm_big_kernel<A_K, B_K, OutT>), dim3((unsigned)(ntile * nsplit)), dim3(kGemmThreads), 0,
+    hipLaunchKernelGGL((gemm_big_kernel<A_K, B_K, OutT, 256>), dim3((unsigned)(ntile * nsplit)), dim3(kGemmThreads), 0,
                        st, g, gx, ntile);
     gemm_reduce<OutT>(g, nsplit, partial, st);
     return SSM_OK;
@@ -970,6 +1077,144 @@ PairPick pair_dw_splits(int m, int K, int N) {
   return PairPick{best, big};
 }
 
+// Both products of a linear layer whose input width K is narrow (at most 128,
+// a multiple of 16: dt_proj's rank) over many rows m and a wide output N, on
+// 256 x 128 tiles in one launch: dX [m, K] over k = N and dW [N, K] over k =
+// m, each split over k, every block streaming a 256 x 32 slice of dY per step.
+// The bias gradient rides along as dW's column K (a column of ones in X) when K
+// < 128.  Splits are picked for the two products' blocks together, one block
+// per CU: the modelled finish time of the block schedule, in k steps of equal
+// cost, plus the split-k partial traffic.
+struct SkinnyPlan {
+  int s1, s2;   // k splits of dX and dW (0: the shape does not take this path)
+  bool colsum;  // db as dW's extra column
+};
+
+SkinnyPlan skinny_plan(int m, int K, int N, bool need_db) {
+  SkinnyPlan p{0, 0, false};
+  if (K > 128 || K % 16 || m % kBigT || N % kBigT || m < 4 * kBigK || N < 4 * kBigK) return p;
+  const long slots = gemm_device_cus();
+  const double step_s = 1.3e-6;  // one k step of every CU's block, streaming 24 KB each
+  double best_t = -1.0;
+  for (int s1 : {1, 2, 3, 4, 6, 8}) {
+    const int ks1 = ((N + s1 - 1) / s1 + kBigK - 1) / kBigK * kBigK;
+    if ((N + ks1 - 1) / ks1 != s1) continue;
+    for (int s2 = 1; s2 <= 32; ++s2) {
+      const int ks2 = ((m + s2 - 1) / s2 + kBigK - 1) / kBigK * kBigK;
+      if ((m + ks2 - 1) / ks2 != s2) continue;
+      const long n1 = (long)(m / kBigT) * s1, n2 = (long)(N / kBigT) * s2;
+      const double ms = pair_makespan(slots, n1, ks1 / kBigK + 4.0, n2, ks2 / kBigK + 4.0);
+      if (ms < 0) continue;
+      const double part = (s1 > 1 ? (double)s1 * m * K : 0.0) + (s2 > 1 ? (double)s2 * N * K : 0.0);
+      const double t = ms * step_s + 2.0 * part * 4.0 / 3e12;
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        p = SkinnyPlan{s1, s2, need_db && K < 128};
+      }
+    }
+  }
+  return p;
+}
+
+// the skinny plan for these operands: a product written without a k split
+// needs 16-byte vectors in its output rows
+SkinnyPlan skinny_plan_for(int m, int K, int N, bool need_db, const void* dX, long long lddx, const void* dW) {
+  SkinnyPlan p = skinny_plan(m, K, N, need_db);
+  if (p.s1 && ((p.s1 == 1 && !(aligned16(dX) && lddx % 8 == 0)) || (p.s2 == 1 && !aligned16(dW))))
+    p = SkinnyPlan{0, 0, false};
+  return p;
+}
+
+// workspace of the skinny pair: dX partials, dW partials, db partials
+size_t skinny_workspace_bytes(const SkinnyPlan& p, int m, int K, int N) {
+  if (!p.s1) return 0;
+  return (p.s1 > 1 ? align_up((size_t)p.s1 * m * K * 4) : 0) + (p.s2 > 1 ? align_up((size_t)p.s2 * N * K * 4) : 0) +
+         (p.colsum ? align_up((size_t)p.s2 * N * 4) : 0);
+}
+
+void launch_skinny_pair(const SkinnyPlan& p, const void* X, long long ldx, const void* W, const void* dY,
+                        long long lddy, void* dX, long long lddx, float* dW, float* db, int m, int K, int N, int acc_x,
+                        int acc_w, void* workspace, hipStream_t st) {
+  char* ws = static_cast<char*>(workspace);
+  float* part1 = nullptr;
+  float* part2 = nullptr;
+  float* part_db = nullptr;
+  if (p.s1 > 1) { part1 = reinterpret_cast<float*>(ws); ws += align_up((size_t)p.s1 * m * K * 4); }
+  if (p.s2 > 1) { part2 = reinterpret_cast<float*>(ws); ws += align_up((size_t)p.s2 * N * K * 4); }
+  if (p.colsum) part_db = reinterpret_cast<float*>(ws);
+  const uint16_t* y16 = static_cast<const uint16_t*>(dY);
+  // dX[m, K] = dY[m, N] W[N, K]: A = dY (k = n contiguous), B(k = n, j) = W[n * K + j]
+  GemmArgs g1{y16, static_cast<const uint16_t*>(W), dX, nullptr, lddy, K, lddx, m, K, N, 0, acc_x,
+              aligned16(dX) && lddx % 8 == 0, nullptr};
+  // dW[N, K] = dY^T X: A(i = n, k = row) = dY[row * lddy + n], B(k = row, j) = X[row * ldx + j]
+  GemmArgs g2{y16, static_cast<const uint16_t*>(X), dW, nullptr, lddy, ldx, K, N, K, m, 0, acc_w,
+              aligned16(dW) && K % 4 == 0, nullptr};
+  const int ns1 = gemm_prep(g1, p.s1, part1, kBigK), ns2 = gemm_prep(g2, p.s2, part2, kBigK);
+  if (p.colsum) g2.colsum = p.s2 > 1 ? part_db : db;
+  const int nt1 = m / kBigT, nt2 = N / kBigT;
+  hipLaunchKernelGGL((gemm_big_pair_kernel<true, false, bf16, 128, false, false, float, 128>),
+                     dim3((unsigned)(nt1 * ns1 + nt2 * ns2)), dim3(kGemmThreads), 0, st, g1, g2, 1, nt1, nt1 * ns1, 1,
+                     nt2);
+  gemm_reduce<bf16>(g1, ns1, part1, st);
+  gemm_reduce<float>(g2, ns2, part2, st);
+  if (p.colsum && ns2 > 1)
+    hipLaunchKernelGGL(column_sum_final, dim3((N + 255) / 256), dim3(256), 0, st, part_db, ns2, N, db, acc_w);
+}
+
+// Both products of a linear layer with a narrow output N (at most 128, a
+// multiple of 32: x_proj) over many rows m and a wide input K, in one launch:
+// dW's transpose [K, N] = X^T dY on 256 x 128 tiles split over k = m (its
+// partials summed into dW transposed), and dX [m, K] = dY W on 256 x 256
+// tiles with its 32 k steps.  dW's long blocks come first and dX's short ones
+// fill in behind them.  The split is picked for the two products' blocks
+// together: the modelled finish time of the block schedule (a dX block costing
+// its k steps plus 8 for the read-modify-write of its tile) plus the partial
+// traffic.
+int wide_plan(int m, int K, int N, const void* dX, long long lddx) {
+  if (N > 128 || N % 32 || m % kBigT || K % kBigT || m < 8 * kBigK || !(aligned16(dX) && lddx % 8 == 0)) return 0;
+  const long slots = gemm_device_cus();
+  const double step_s = 1.3e-6;
+  const long n2 = (long)(m / kBigT) * (K / kBigT);
+  int best = 0;
+  double best_t = -1.0;
+  for (int s1 = 2; s1 <= 32; ++s1) {
+    const int ks1 = ((m + s1 - 1) / s1 + kBigK - 1) / kBigK * kBigK;
+    if ((m + ks1 - 1) / ks1 != s1) continue;
+    const long n1 = (long)(K / kBigT) * s1;
+    const double ms = pair_makespan(slots, n1, ks1 / kBigK + 4.0, n2, N / kBigK + 8.0);
+    if (ms < 0) continue;
+    const double t = ms * step_s + 2.0 * s1 * (double)K * N * 4.0 / 3e12;
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = s1;
+    }
+  }
+  return best;
+}
+
+size_t wide_workspace_bytes(int s1, int K, int N) { return s1 ? align_up((size_t)s1 * K * N * 4) : 0; }
+
+void launch_wide_pair(int s1, const void* X, long long ldx, const void* W, const void* dY, long long lddy, void* dX,
+                      long long lddx, float* dW, int m, int K, int N, int acc_x, int acc_w, void* workspace,
+                      hipStream_t st) {
+  float* part = static_cast<float*>(workspace);
+  // dW^T[K, N] = X^T dY: A(i = j, k = row) = X[row * ldx + j], B(k = row, n) = dY[row * lddy + n]
+  GemmArgs g1{static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(dY), nullptr, nullptr, ldx, lddy, N,
+              K, N, m, 0, 0, 1, nullptr};
+  // dX[m, K] = dY[m, N] W[N, K]: A = dY (k = n contiguous), B(k = n, j) = W[n * K + j]
+  GemmArgs g2{static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(W), dX, nullptr, lddy, K, lddx, m, K, N,
+              0, acc_x, 1, nullptr};
+  const int ns1 = gemm_prep(g1, s1, part, kBigK);
+  gemm_prep(g2, 1, nullptr, kBigK);
+  g1.partial = part;  // always through partials: the sum lands transposed
+  const int nt1 = K / kBigT, gx2 = K / kBigT, nt2 = gx2 * (m / kBigT);
+  hipLaunchKernelGGL((gemm_big_pair_kernel<false, false, float, 128, true, false, bf16, 256>),
+                     dim3((unsigned)(nt1 * ns1 + nt2)), dim3(kGemmThreads), 0, st, g1, g2, 1, nt1, nt1 * ns1, gx2,
+                     nt2);
+  hipLaunchKernelGGL(splitk_reduce_t, dim3((K + 31) / 32, (N + 31) / 32), dim3(256), 0, st, part, dW, (long long)K,
+                     K, N, ns1, acc_w);
+}
+
 // dX[M, K] = dY W and dW[N, K] = dY^T X of one linear layer: one launch for both
 // when pair_dw_splits allows (dW's split-k partials then own the workspace),
 // otherwise one launch each.
@@ -995,8 +1240,8 @@ void linear_bwd_products(const void* X, long long ldx, const void* W, const void
   const int nsplit2 = gemm_prep(g2, pp.splits, part, kstep);
   if (pp.big) {
     const int gx = K / kBigT, nb1 = gx * (m / kBigT), nt2 = gx * (N / kBigT);
-    hipLaunchKernelGGL((gemm_big_pair_kernel<true, false, bf16, false, false, float>),
-                       dim3((unsigned)(nb1 + nt2 * nsplit2)), dim3(kGemmThreads), 0, st, g1, g2, gx, nb1, gx, nt2);
+    hipLaunchKernelGGL((gemm_big_pair_kernel<true, false, bf16, 256, false, false, float, 256>),
+                       dim3((unsigned)(nb1 + nt2 * nsplit2)), dim3(kGemmThreads), 0, st, g1, g2, gx, nb1, nb1, gx, nt2);
   } else {
     const int bm = pick_bm(m, K, N);
     const int gx = (K + 127) / 128;
@@ -1039,6 +1284,11 @@ extern "C" size_t linear_bwd_workspace_size(int64_t M, int K, int N) {
   // dX = dY W (M x K, reduction N), dW = dY^T X (N x K, reduction M) and the db
   // column sums run one after another and share the space
   size_t a = gemm_workspace_bytes((int)M, K, N), b = gemm_workspace_bytes(N, K, (int)M);
+  const size_t sk = skinny_workspace_bytes(skinny_plan((int)M, K, N, true), (int)M, K, N);  // both products at once
+  a = sk > a ? sk : a;
+  // the wide pair's plan with an aligned dX (a dX it cannot take runs the other paths)
+  const size_t wd = wide_workspace_bytes(wide_plan((int)M, K, N, reinterpret_cast<const void*>(256), 8), K, N);
+  a = wd > a ? wd : a;
   const int s2 = pair_dw_splits((int)M, K, N).splits;  // dW's split when paired with dX
   if (s2 > 1) {
     const size_t bp = align_up((size_t)s2 * N * K * sizeof(float));
@@ -1071,7 +1321,13 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   if (dX && (rc = gemm_check(dY, lddy, W, K, dX, m, K, N, ws_bytes, workspace)) != SSM_OK) return rc;
   // dW[N, K] = dY^T X: A(i = n, k = m) = dY[m * lddy + n], B(k = m, j) = X[m * ldx + j]
   if (dW && (rc = gemm_check(dY, lddy, X, ldx, dW, N, K, m, ws_bytes, workspace)) != SSM_OK) return rc;
-  if (dX && dW) {  // dX and dW in one launch: dW's split-k partials for the paired split
+  const SkinnyPlan sp = (dX && dW) ? skinny_plan_for(m, K, N, db != nullptr, dX, lddx, dW) : SkinnyPlan{0, 0, false};
+  const int wp = (dX && dW && !sp.s1) ? wide_plan(m, K, N, dX, lddx) : 0;
+  const size_t sk = skinny_workspace_bytes(sp, m, K, N) + wide_workspace_bytes(wp, K, N);
+  if (sk && (!workspace || ws_bytes < sk || !aligned256(workspace)))
+    return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the split-k partials missing, too small or not "
+                                   "256-byte aligned");
+  if (dX && dW && !sp.s1 && !wp) {  // dX and dW in one launch: dW's split-k partials for the paired split
     const int s2 = pair_dw_splits(m, K, N).splits;
     if (s2 > 1 && (!workspace || ws_bytes < align_up((size_t)s2 * N * K * sizeof(float)) || !aligned256(workspace)))
       return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the split-k partials missing, too small or not "
@@ -1079,8 +1335,13 @@ extern "C" int linear_bwd(const void* X, int64_t ldx, const void* W, const void*
   }
   if (db && (!workspace || ws_bytes < column_sum_workspace_bytes(m, N) || !aligned256(workspace)))
     return fail(SSM_ERR_WORKSPACE, "linear_bwd: workspace for the bias sums missing, too small or not 256-byte aligned");
-  linear_bwd_products(X, ldx, W, dY, lddy, dX, lddx, dW, m, K, N, acc_x, acc_w, workspace, st);
-  if (db) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, acc_w, workspace, st);
+  if (sp.s1)
+    launch_skinny_pair(sp, X, ldx, W, dY, lddy, dX, lddx, dW, db, m, K, N, acc_x, acc_w, workspace, st);
+  else if (wp)
+    launch_wide_pair(wp, X, ldx, W, dY, lddy, dX, lddx, dW, m, K, N, acc_x, acc_w, workspace, st);
+  else
+    linear_bwd_products(X, ldx, W, dY, lddy, dX, lddx, dW, m, K, N, acc_x, acc_w, workspace, st);
+  if (db && !sp.colsum) column_sum_launch(dY, lddy, m, N, SSM_BF16, db, acc_w, workspace, st);
   return check_launch("linear_bwd");
 }
 

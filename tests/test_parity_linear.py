@@ -154,6 +154,52 @@ def test_whole_tile_products_accumulate_into_views(M, K, N, offset):
     assert norm_err(_np(Y), orc.linear_fwd(X, W)) < TOL_BF16
 
 
+# (M, K, N): a narrow input K (at most 128) against whole 256-row tiles in M and N
+# takes the paired 256 x 128 tiles (dX and dW split over k, db as dW's extra
+# column when K < 128); a narrow output N (at most 128) against whole tiles in M
+# and K takes dW's transpose on 256 x 128 tiles beside dX on 256 x 256 tiles.
+NARROW = [
+    (256, 96, 256, True),      # narrow input, one row tile, db in the product
+    (1024, 64, 768, True),
+    (4096, 128, 512, True),    # K = 128: no room for the bias column, db summed apart
+    (2048, 96, 3072, False),   # dt_proj's shape, no db
+    (2048, 512, 128, False),   # narrow output (x_proj's shape at fewer rows)
+    (1024, 768, 64, False),
+    (2048, 512, 96, True),     # narrow output ending inside the 128-wide tile
+]
+
+
+@pytest.mark.parametrize("M,K,N,need_db", NARROW)
+def test_narrow_products_accumulate(M, K, N, need_db):
+    """dX added into a column slice of a wider buffer, dW and db accumulated into given buffers."""
+    X, W, dY = _mats(M, K, N, seed=7 * M + K + 3 * N)
+    rng = np.random.default_rng(K + N)
+    base = round_bf16(rng.standard_normal((M, K + 128)))
+    w0 = rng.standard_normal((N, K)).astype(np.float32)
+    b0 = rng.standard_normal(N).astype(np.float32)
+    print(f"case: narrow linear_bwd M {M} K {K} N {N} db {need_db}", flush=True)
+    dXbuf = _bf(base)
+    dWg = torch.from_numpy(w0).to(DEV)
+    dbg = torch.from_numpy(b0).to(DEV) if need_db else None
+    _ssm().linear_bwd(_bf(X), _bf(W), _bf(dY), need_db=need_db, dX=dXbuf[:, 64:64 + K], accumulate_dx=True,
+                      dW=dWg, db=dbg, accumulate=True)
+    torch.cuda.synchronize()
+    rx, rw, rb = orc.linear_bwd(X, W, dY)
+    got = _np(dXbuf)
+    assert norm_err(got[:, 64:64 + K], base[:, 64:64 + K] + rx) < TOL_BF16
+    assert np.array_equal(got[:, :64], base[:, :64]) and np.array_equal(got[:, 64 + K:], base[:, 64 + K:])
+    assert norm_err(_np(dWg), w0 + rw) < TOL_F32
+    if need_db:
+        assert norm_err(_np(dbg), b0 + rb) < TOL_F32
+    # and written fresh, without accumulation
+    dX2, dW2, db2 = _ssm().linear_bwd(_bf(X), _bf(W), _bf(dY), need_db=need_db)
+    torch.cuda.synchronize()
+    assert norm_err(_np(dX2), rx) < TOL_BF16
+    assert norm_err(_np(dW2), rw) < TOL_F32
+    if need_db:
+        assert norm_err(_np(db2), rb) < TOL_F32
+
+
 def test_linear_bwd_empty_rows():
     """M = 0: dW and db are zero (sums over no rows)."""
     W = _bf(np.ones((24, 16)))
