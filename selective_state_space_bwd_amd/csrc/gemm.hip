@@ -688,13 +688,32 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs& g, int m0, int n0,
     }
 }
 
+// Tile of block pid among ntile tiles (gx columns) for the big tiles: XCD x
+// takes the x-th contiguous run of tiles as in xcd_tile, and when the run is
+// whole rows of tiles it walks them in groups of four rows, column by column,
+// so the blocks an XCD holds at once cover about four row tiles and eight
+// column tiles instead of one or two rows of every column.  That roughly
+// halves the distinct operand slices the XCD's L2 must hold per k step (a
+// wide product's weight was otherwise streamed through every L2 once per
+// row of tiles).
+__device__ __forceinline__ int grouped_tile(int pid, int ntile, int gx) {
+  if (ntile % 8 != 0) return pid;
+  const int per = ntile / 8, xcd = pid % 8, local = pid / 8;
+  if (per % gx != 0) return xcd * per + local;
+  constexpr int G = 4;
+  const int nr = per / gx, r0 = xcd * nr;
+  const int g = local / (G * gx), gl = min(G, nr - g * G);  // the group's rows
+  const int idx = local - g * G * gx;
+  return (r0 + g * G + idx % gl) * gx + idx / gl;
+}
+
 // grid (column tiles x row tiles x k splits), linear; tiles of one split go
-// to the XCDs in contiguous runs as in gemm_bf16_kernel
+// to the XCDs in contiguous runs (grouped_tile)
 template <bool A_K, bool B_K, typename OutT, int BN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_kernel(GemmArgs g, int gx, int ntile) {
   __shared__ __align__(1024) char lds[BigCfg<BN>::kLdsBytes];
   const int split = blockIdx.x / ntile;
-  const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
+  const int tile = grouped_tile(blockIdx.x - split * ntile, ntile, gx);
   gemm_big_tile<A_K, B_K, OutT, BN>(g, (tile / gx) * kBigT, (tile % gx) * BN, split, lds);
 }
 
@@ -709,11 +728,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_big_pair_kernel(GemmArgs
   const int id = blockIdx.x;
   if (id < nb1) {
     const int split = id / nt1;
-    const int tile = xcd_tile(id - split * nt1, nt1);
+    const int tile = grouped_tile(id - split * nt1, nt1, gx1);
     gemm_big_tile<A1, B1, O1, BN1>(g1, (tile / gx1) * kBigT, (tile % gx1) * BN1, split, lds);
   } else {
     const int local = id - nb1, split = local / nt2;
-    const int tile = xcd_tile(local - split * nt2, nt2);
+    const int tile = grouped_tile(local - split * nt2, nt2, gx2);
     gemm_big_tile<A2, B2, O2, BN2>(g2, (tile / gx2) * kBigT, (tile % gx2) * BN2, split, lds);
   }
 }
