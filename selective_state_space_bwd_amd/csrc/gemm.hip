@@ -1057,43 +1057,50 @@ double pair_makespan(long slots, long n1, double d1, long n2, double d2) {
 // dW's k split in the paired launch of linear_bwd_products (splits 0: the
 // products are not paired), for an m x N output gradient and an N x K weight.
 // With big tiles when both products are made of whole 256 x 256 tiles and
-// 64-wide k steps; otherwise the products pair when dX needs no k split and
+// 32-wide k steps; otherwise the products pair when dX needs no k split and
 // both pick the same tile height.  The split is picked for the two products'
 // blocks together: the modelled finish time of the block schedule (a k step
 // per block costing the same in both, a fixed set-up per block, the tile rate
-// of the single-product model) plus the split-k partial traffic.
+// of the single-product model) plus the split-k partial traffic.  Big tiles
+// also try dW's blocks first: its long blocks then start together and dX's
+// short ones fill in behind them.
 struct PairPick {
   int splits;
   bool big;
+  bool dw_first;
 };
 
 PairPick pair_dw_splits(int m, int K, int N) {
   const bool big = big_fits(m, K, N) && big_fits(N, K, m);
   const int bm = big ? kBigT : pick_bm(m, K, N), bn = big ? kBigT : 128;
   const int kstep = big ? kBigK : kBK;
-  if (!big && (pick_splits(m, K, N) != 1 || pick_bm(N, K, m) != bm)) return PairPick{0, false};
+  if (!big && (pick_splits(m, K, N) != 1 || pick_bm(N, K, m) != bm)) return PairPick{0, false, false};
   const int gx = (K + bn - 1) / bn;
   const long nb1 = (long)gx * ((m + bm - 1) / bm), nt2 = (long)gx * ((N + bm - 1) / bm);
   const long slots = gemm_device_cus() * (big ? 1 : bm == 256 ? 2 : 3);
   const double rate = big ? kRateBig : bm == 256 ? kRate256 : kRate128;
   const double kstep_s = (double)bm * bn * kstep * 2 / (rate / slots);
-  const double setup = big ? 4.0 : 8.0;  // k steps' worth of prologue and epilogue per block
-  int best = big ? 1 : pick_splits(N, K, m);
+  const double setup = big ? 6.0 : 8.0;  // k steps' worth of prologue and epilogue per block
+  PairPick best{big ? 1 : pick_splits(N, K, m), big, false};
   double best_t = -1.0;
-  for (int sp : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
-    if (sp > 1 && m / sp < 4 * kBK) break;
-    const int ks = ((m + sp - 1) / sp + kstep - 1) / kstep * kstep;
-    const int used = (m + ks - 1) / ks;
-    const double ms = pair_makespan(slots, nb1, (N + kstep - 1) / kstep + setup, nt2 * used, ks / kstep + setup);
-    if (ms < 0) continue;
-    double t = ms * kstep_s;
-    if (used > 1) t += 2.0 * used * (double)N * K * 4.0 / 3e12;
-    if (best_t < 0 || t < best_t) {
-      best_t = t;
-      best = sp;
+  for (int order = 0; order < (big ? 2 : 1); ++order) {
+    for (int sp : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
+      if (sp > 1 && m / sp < 4 * kBK) break;
+      const int ks = ((m + sp - 1) / sp + kstep - 1) / kstep * kstep;
+      const int used = (m + ks - 1) / ks;
+      const double d1 = (N + kstep - 1) / kstep + setup, d2 = ks / kstep + setup;
+      const double ms = order == 0 ? pair_makespan(slots, nb1, d1, nt2 * used, d2)
+                                   : pair_makespan(slots, nt2 * used, d2, nb1, d1);
+      if (ms < 0) continue;
+      double t = ms * kstep_s;
+      if (used > 1) t += 2.0 * used * (double)N * K * 4.0 / 3e12;
+      if (best_t < 0 || t < best_t) {
+        best_t = t;
+        best = PairPick{sp, big, order == 1};
+      }
     }
   }
-  return PairPick{best, big};
+  return best;
 }
 
 // Both products of a linear layer whose input width K is narrow (at most 128,
@@ -1240,7 +1247,7 @@ void launch_wide_pair(int s1, const void* X, long long ldx, const void* W, const
 void linear_bwd_products(const void* X, long long ldx, const void* W, const void* dY, long long lddy, void* dX,
                          long long lddx, float* dW, int m, int K, int N, int acc_x, int acc_w, void* workspace,
                          hipStream_t st) {
-  PairPick pp = (dX && dW) ? pair_dw_splits(m, K, N) : PairPick{0, false};
+  PairPick pp = (dX && dW) ? pair_dw_splits(m, K, N) : PairPick{0, false, false};
   // the big tiles write 16-byte vectors only (dW's partials always take them)
   if (pp.big && !((aligned16(dX) && lddx % 8 == 0) && (pp.splits > 1 || aligned16(dW)))) pp.splits = 0;
   if (pp.splits == 0) {
@@ -1257,7 +1264,12 @@ void linear_bwd_products(const void* X, long long ldx, const void* W, const void
   const int kstep = pp.big ? kBigK : kBK;
   gemm_prep(g1, 1, nullptr, kstep);
   const int nsplit2 = gemm_prep(g2, pp.splits, part, kstep);
-  if (pp.big) {
+  if (pp.big && pp.dw_first) {
+    const int gx = K / kBigT, nt1 = gx * (N / kBigT), nt2 = gx * (m / kBigT);
+    hipLaunchKernelGGL((gemm_big_pair_kernel<false, false, float, 256, true, false, bf16, 256>),
+                       dim3((unsigned)(nt1 * nsplit2 + nt2)), dim3(kGemmThreads), 0, st, g2, g1, gx, nt1,
+                       nt1 * nsplit2, gx, nt2);
+  } else if (pp.big) {
     const int gx = K / kBigT, nb1 = gx * (m / kBigT), nt2 = gx * (N / kBigT);
     hipLaunchKernelGGL((gemm_big_pair_kernel<true, false, bf16, 256, false, false, float, 256>),
                        dim3((unsigned)(nb1 + nt2 * nsplit2)), dim3(kGemmThreads), 0, st, g1, g2, gx, nb1, nb1, gx, nt2);
