@@ -6,16 +6,19 @@
 //   opA(m, k) = A[m * lda + k]  (A_K: k contiguous)  or  A[k * lda + m]
 //   opB(k, n) = B[n * ldb + k]  (B_K: k contiguous)  or  B[k * ldb + n]
 //
-// Block tile BM x BN x 32 (256 x 128 for large products, 128 x 128 otherwise),
-// four waves in a 2 x 2 grid, each wave (BM/2) x (BN/2) as
-// v_mfma_f32_32x32x16_bf16 tiles.  Every operand tile sits in LDS in the layout
-// it has in memory, so global loads and LDS stores are 16 bytes either way:
-// [row][k] when k is contiguous, read as MFMA operands with ds_read_b128, or
-// [k][row] when k is the row index, read with the gfx950 transposing
-// ds_read_b64_tr_b16 (two per operand).  Double buffered: the next tile's
-// global loads are in flight while the matrix cores work on the current one,
-// one barrier per k step.  Split-k writes fp32 partial tiles that a second
-// kernel sums in a fixed order.
+// Two tile families on v_mfma_f32_32x32x16_bf16, both with every operand tile
+// in LDS in the layout it has in memory ([row][k] read with ds_read_b128 when k
+// is contiguous, [k][row] read with the transposing ds_read_b64_tr_b16
+// otherwise):
+// - Register-staged tiles (gemm_tile): BM x BN x 32 (256 x 128 for large
+//   products, 128 x 128 otherwise), four waves in a 2 x 2 grid, two waves per
+//   SIMD, the next tiles' global loads held in registers, edge tiles checked;
+//   they take any shape.
+// - Direct-load tiles (gemm_big_tile): 256 x 256 or 256 x 128 x 32, one wave
+//   per SIMD with the accumulators in AGPRs, operand tiles brought into a ring
+//   of LDS stages by global -> LDS loads; they take whole tiles, and the
+//   layer's products in pairs (dX and dW of one layer in one launch).
+// Split-k writes fp32 partial tiles that a second kernel sums in a fixed order.
 #include <math.h>
 
 #include <atomic>
