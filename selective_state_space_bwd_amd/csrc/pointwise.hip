@@ -148,15 +148,47 @@ __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_kernel(
 
 // Vector form for rows of 16-byte vectors (d_inner, the strides and the bases
 // multiples of 16 bytes): a block's four waves take one vector of channels per
-// lane and four consecutive chunks of kConvTV steps, one chunk per wave.  Each
+// lane and four consecutive chunks of tv steps, one chunk per wave.  Each
 // wave issues the loads of kConvLoad steps together, then runs them; the waves'
 // weight and bias sums combine in LDS in a fixed order into one partial per
 // block.  The K-1 steps after a chunk, needed for its last d_x outputs, are
 // recomputed by the wave (with zero gradient past the sequence end).
-constexpr int kConvTV = 32;
 constexpr int kConvWaves = kPwBlock / kWave;
 constexpr int kConvLoad = 4;
-constexpr int kConvBlockSteps = kConvTV * kConvWaves;
+constexpr int kConvMinTV = 16;  // the workspace is sized for 4 x 16 steps per block (kConvT)
+static_assert(kConvWaves * kConvMinTV >= 64, "conv partials per sequence");
+// Blocks a CU holds at once, from the kernels' register use (the backward's
+// window, weight sums and load buffers take two waves per SIMD, the forward's
+// four).
+constexpr int kConvBwdBlocksPerCU = 2;
+constexpr int kConvFwdBlocksPerCU = 4;
+
+// Steps per wave of the vector conv kernels: the grid is (channel vectors /
+// 64) x (seqlen / 4 tv) x batch blocks, and each wave also recomputes the K - 1
+// steps after its chunk.  Picks tv, a multiple of the load group, that
+// minimises (rounds of resident blocks) x (tv + K - 1); ties go to the longer
+// chunk (fewer weight-sum partials).
+int conv_steps_per_wave(int seqlen, int nx, int batch, int K, int blocks_per_cu) {
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  const long slots = (long)cus * blocks_per_cu;
+  int best = kConvMinTV;
+  long best_cost = -1;
+  for (int tv = kConvMinTV; tv <= 256; tv += kConvLoad) {
+    const long blocks = (long)nx * ((seqlen + kConvWaves * tv - 1) / (kConvWaves * tv)) * batch;
+    const long cost = (blocks + slots - 1) / slots * (tv + K - 1);
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = tv;
+    }
+    if (kConvWaves * tv >= seqlen) break;
+  }
+  return best;
+}
 
 template <typename T, int K>
 struct ConvWindow {
@@ -193,14 +225,14 @@ template <typename T, int K>
 __global__ __launch_bounds__(kPwBlock) void conv1d_bwd_vec(
     const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     const T* __restrict__ d_u, T* __restrict__ d_x, float* __restrict__ part, int Tn, int Di,
-    int ld_x, int ld_du, int ld_dx) {
+    int ld_x, int ld_du, int ld_dx, int tv) {
   constexpr int V = Vec16<T>::N;
   __shared__ float red[kConvWaves - 1][(K + 1) * V][kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d0 = (blockIdx.x * kWave + lane) * V;
   const bool on = d0 < Di;
-  const int t0 = (blockIdx.y * kConvWaves + wave) * kConvTV;
-  const int t1 = min(Tn, t0 + kConvTV);
+  const int t0 = (blockIdx.y * kConvWaves + wave) * tv;
+  const int t1 = min(Tn, t0 + tv);
   const size_t rx = (size_t)blockIdx.z * Tn;
   float dw[K + 1][V];  // K weight sums, then the bias sum
 #pragma unroll
@@ -608,19 +640,19 @@ __global__ __launch_bounds__(kPwBlock) void rmsnorm_fwd_kernel(const bf16* __res
 }
 
 // u[b,t,d] = SiLU(bias[d] + sum_k w[d,k] x[b, t-(K-1)+k, d]), on 8-channel
-// vectors: a lane per vector and a wave per chunk of kConvTV steps, as in the
+// vectors: a lane per vector and a wave per chunk of tv steps, as in the
 // vector conv backward
 template <int K>
 __global__ __launch_bounds__(kPwBlock) void conv_silu_fwd_vec(const bf16* __restrict__ x, int ld_x,
                                                               const float* __restrict__ w,
                                                               const float* __restrict__ bias, bf16* __restrict__ u,
-                                                              int ld_u, int Tn, int Di) {
+                                                              int ld_u, int Tn, int Di, int tv) {
   constexpr int V = Vec16<bf16>::N;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d0 = (blockIdx.x * kWave + lane) * V;
-  const int t0 = (blockIdx.y * kConvWaves + wave) * kConvTV;
+  const int t0 = (blockIdx.y * kConvWaves + wave) * tv;
   if (d0 >= Di || t0 >= Tn) return;
-  const int t1 = min(Tn, t0 + kConvTV);
+  const int t1 = min(Tn, t0 + tv);
   const size_t rx = (size_t)blockIdx.z * Tn;
   ConvWindow<bf16, K> win;
   win.init(w, bias, d0);
@@ -772,10 +804,12 @@ void launch_rmsnorm_fwd(const bf16* x, const float* w, bf16* xn, int64_t rows, i
 void launch_conv_silu_fwd(const bf16* x, int ld_x, const float* w, const float* bias, bf16* u, int ld_u, int Bt,
                           int Tn, int Di, int K, hipStream_t st) {
   if ((int64_t)Bt * Tn == 0) return;
-  const dim3 grid((Di / 8 + kWave - 1) / kWave, (Tn + kConvBlockSteps - 1) / kConvBlockSteps, Bt);
-#define CONV_FWD(KV)                                                                                         \
-  case KV:                                                                                                   \
-    hipLaunchKernelGGL(conv_silu_fwd_vec<KV>, grid, dim3(kPwBlock), 0, st, x, ld_x, w, bias, u, ld_u, Tn, Di); \
+  const int nx = (Di / 8 + kWave - 1) / kWave;
+  const int tv = conv_steps_per_wave(Tn, nx, Bt, K, kConvFwdBlocksPerCU);
+  const dim3 grid(nx, (Tn + kConvWaves * tv - 1) / (kConvWaves * tv), Bt);
+#define CONV_FWD(KV)                                                                                              \
+  case KV:                                                                                                        \
+    hipLaunchKernelGGL(conv_silu_fwd_vec<KV>, grid, dim3(kPwBlock), 0, st, x, ld_x, w, bias, u, ld_u, Tn, Di, tv); \
     break;
   switch (K) { CONV_FWD(1) CONV_FWD(2) CONV_FWD(3) CONV_FWD(4) CONV_FWD(5) CONV_FWD(6) CONV_FWD(7) CONV_FWD(8) }
 #undef CONV_FWD
@@ -860,15 +894,16 @@ extern "C" int conv1d_bwd(const void* x, const float* w, const float* bias, cons
   const int V = dtype == SSM_F32 ? 4 : 8;
   const bool vec = d_inner % V == 0 && ld_x % V == 0 && ld_du % V == 0 && ld_dx % V == 0 && aligned16(x) &&
                    aligned16(d_u) && aligned16(d_x) && aligned16(workspace);
-  const int nchunk = vec ? (seqlen + kConvBlockSteps - 1) / kConvBlockSteps : (seqlen + kConvT - 1) / kConvT;
-  const dim3 grid = vec ? dim3((d_inner / V + kWave - 1) / kWave, nchunk, batch)
-                        : dim3((d_inner + kPwBlock - 1) / kPwBlock, nchunk, batch);
+  const int nx = vec ? (d_inner / V + kWave - 1) / kWave : (d_inner + kPwBlock - 1) / kPwBlock;
+  const int tv = vec ? conv_steps_per_wave(seqlen, nx, batch, d_conv, kConvBwdBlocksPerCU) : 0;
+  const int nchunk = vec ? (seqlen + kConvWaves * tv - 1) / (kConvWaves * tv) : (seqlen + kConvT - 1) / kConvT;
+  const dim3 grid(nx, nchunk, batch);
   const dim3 fgrid(((d_conv + 1) * d_inner + kWave - 1) / kWave);
 #define CONV_CASE(TY, KV)                                                                                      \
   case KV:                                                                                                     \
     if (vec)                                                                                                   \
       hipLaunchKernelGGL((conv1d_bwd_vec<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,        \
-                         (const TY*)d_u, (TY*)d_x, part, seqlen, d_inner, ld_x, ld_du, ld_dx);                \
+                         (const TY*)d_u, (TY*)d_x, part, seqlen, d_inner, ld_x, ld_du, ld_dx, tv);            \
     else                                                                                                       \
       hipLaunchKernelGGL((conv1d_bwd_kernel<TY, KV>), grid, dim3(kPwBlock), 0, st, (const TY*)x, w, bias,     \
                          (const TY*)d_u, (TY*)d_x, part, batch, seqlen, d_inner, ld_x, ld_du, ld_dx, nchunk); \
