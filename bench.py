@@ -50,7 +50,7 @@ FP32_NONPACKED_CEILING_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 #          d_u's sum g B 2, d_B = sum_d g delta u 2, d_C = sum_d dy h 2        -> 14
 FLOPS_PER_SE = 21
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
-CHANNEL_BLOCK = 1024  # channels per CPU-baseline shard (the oracle's own block size)
+CHANNEL_BLOCK = 1024  # most channels per CPU-baseline shard (the oracle's own block size)
 
 
 def parse():
@@ -184,8 +184,15 @@ def _pool_workers() -> int:
 MIN_CPU_SECONDS = 10.0
 
 
+def _channel_block(cfg, n: int) -> int:
+    """Channels per CPU-baseline shard: at most CHANNEL_BLOCK, a multiple of 256, and small enough
+    that each of the n workers gets at least two shards when the shape allows."""
+    per_b = -(-2 * n // cfg.batch)  # channel blocks per batch element for 2n shards
+    return max(256, min(CHANNEL_BLOCK, cfg.d_inner // per_b // 256 * 256))
+
+
 def cpu_baseline_scan(cfg):
-    """The fp64 oracle over the whole workload, sharded over (batch element, 256-channel block) on a
+    """The fp64 oracle over the whole workload, sharded over (batch element, channel block) on a
     fork pool of all host cores (BLAS threads 1 per worker).  The shards' partial sums of d_B, d_C
     (over channel blocks) and d_A_log, d_D (over batch) are added in shard order.  The whole workload
     is repeated until the workers have spent MIN_CPU_SECONDS of CPU time."""
@@ -194,9 +201,9 @@ def cpu_baseline_scan(cfg):
     from synth import scan_inputs
     global _POOL_INPUTS
     _POOL_INPUTS = scan_inputs(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, cfg.seed)
-    tasks = [(b, d0, min(d0 + CHANNEL_BLOCK, cfg.d_inner)) for b in range(cfg.batch)
-             for d0 in range(0, cfg.d_inner, CHANNEL_BLOCK)]
     n = _pool_workers()
+    blk = _channel_block(cfg, n)
+    tasks = [(b, d0, min(d0 + blk, cfg.d_inner)) for b in range(cfg.batch) for d0 in range(0, cfg.d_inner, blk)]
     passes, wall, cpu = 0, 0.0, 0.0
     with mp.get_context("fork").Pool(n, initializer=_pool_init) as pool:
         while cpu < MIN_CPU_SECONDS and passes < 8:
@@ -219,7 +226,7 @@ def cpu_baseline_scan(cfg):
     return {"value": se / wall, "unit": "state-elements/s", "cores": n, "kind": "oracle",
             "cpu_model": _cpu_model(),
             "sample": f"the whole workload x {passes} ({se} state elements) as {len(tasks)} shards of "
-                      f"(batch element, {CHANNEL_BLOCK} channels) on {n} worker processes, fp64 NumPy, "
+                      f"(batch element, {blk} channels) on {n} worker processes, fp64 NumPy, "
                       f"1 BLAS thread each; {wall:.2f} s wall, {cpu:.1f} s CPU"}
 
 
@@ -259,6 +266,7 @@ def cpu_baseline_layer(cfg):
 # timing
 
 STAGE_SAMPLES = 4  # timed steps that also record the per-stage HIP events
+ROTATE = 3         # copies of each workload's tensors that the steps take in turn (Infinity Cache)
 
 
 def timed(step, n_events: int, steps: int, warmup: int):
@@ -302,7 +310,8 @@ def step_stats(step, steps: int):
     return {"ms_median": round(float(np.median(ms)), 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
             "ms_p90": round(float(np.percentile(ms, 90)), 4), "steps": steps,
             "note": "per-step HIP events in a second pass of the same length after the timed region; "
-                    "the Infinity Cache is not flushed between steps"}
+                    f"steps take {ROTATE} copies of their input and output tensors in turn, so no step finds "
+                    "its tensors in the Infinity Cache from the step before"}
 
 
 # ---------------------------------------------------------------------------
@@ -330,6 +339,8 @@ def scan_roofline(cfg, main_ms, ms_step, main_bytes, call_bytes, traffic_main, t
     return {
         "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_main,
+        "traffic_GBps": round(traffic_main / (main_ms * 1e-3) / 1e9, 1) if traffic_main else None,
+        "traffic_frac_of_peak": round(traffic_main / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if traffic_main else None,
         "kernel": "scan_bwd_main", "kernel_ms": round(main_ms, 4), "algorithmic_bytes": main_bytes,
         "alu": {"flops_per_state_element": FLOPS_PER_SE, "achieved_TFLOPs": round(tflops, 3),
                 "published_fp32_peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
@@ -339,6 +350,9 @@ def scan_roofline(cfg, main_ms, ms_step, main_bytes, call_bytes, traffic_main, t
         "step": {"algorithmic_bytes": call_bytes,
                  "frac_of_hbm_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                  "counted_bytes": traffic_call,
+                 "counted_GBps": round(traffic_call / (ms_step * 1e-3) / 1e9, 1) if traffic_call else None,
+                 "counted_frac_of_peak": round(traffic_call / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                 if traffic_call else None,
                  "counted_over_algorithmic": round(traffic_call / call_bytes, 3) if traffic_call else None},
     }
 
@@ -361,20 +375,34 @@ def prepare_scan(args, cfg):
     out["d_A_log"] = torch.empty_like(t["A_log"])
     out["d_D"] = torch.empty_like(t["D"])
     dims = ssm.scan_dims(t["u"], t["B"], seg_len=args.seg_len)
+    # ROTATE copies of the inputs and outputs, used in turn: a step finds none of its
+    # tensors in the Infinity Cache from the step before
+    sets = [(t, out)] + [({k: v.clone() for k, v in t.items()}, {k: torch.empty_like(v) for k, v in out.items()})
+                         for _ in range(ROTATE - 1)]
+    turn = [0]
+
+    def next_set():
+        i = turn[0]
+        turn[0] = (i + 1) % ROTATE
+        return sets[i]
     if args.ckpt:
-        h_ckpt = ssm.ssm_scan_fwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], want_y=False,
-                                  want_out=False, ckpt_every=8)["h_ckpt"]
+        h_ckpts = [ssm.ssm_scan_fwd(ti["u"], ti["delta"], ti["A_log"], ti["B"], ti["C"], ti["D"], want_y=False,
+                                    want_out=False, ckpt_every=8)["h_ckpt"] for ti, _ in sets]
         ws = torch.empty(ssm.ssm_scan_bwd_ckpt_workspace_size(dims, tdt), dtype=torch.uint8, device=dev)
 
         def step(ev):
-            ssm.ssm_scan_bwd_ckpt(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
-                                  h_ckpt, out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
+            i = turn[0]
+            ti, oi = next_set()
+            ssm.ssm_scan_bwd_ckpt(ti["u"], ti["delta"], ti["A_log"], ti["B"], ti["C"], ti["D"], ti["z"],
+                                  ti["d_out"], h_ckpts[i], out=oi, workspace=ws, seg_len=args.seg_len,
+                                  stage_events=ev)
     else:
         ws = torch.empty(ssm.ssm_scan_bwd_workspace_size(dims, tdt), dtype=torch.uint8, device=dev)
 
         def step(ev):
-            ssm.ssm_scan_bwd(t["u"], t["delta"], t["A_log"], t["B"], t["C"], t["D"], t["z"], t["d_out"],
-                             out=out, workspace=ws, seg_len=args.seg_len, stage_events=ev)
+            ti, oi = next_set()
+            ssm.ssm_scan_bwd(ti["u"], ti["delta"], ti["A_log"], ti["B"], ti["C"], ti["D"], ti["z"], ti["d_out"],
+                             out=oi, workspace=ws, seg_len=args.seg_len, stage_events=ev)
     return step
 
 
@@ -450,18 +478,24 @@ def measure_layer(args, cfg, steps, warmup, want_stats=True):
     t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in bf else torch.from_numpy(v)).to(dev) for k, v in p.items()}
     del p
     W = {k: t[k] for k in ssm.LAYER_WEIGHTS}
-    _, saved = ssm.mamba_layer_fwd(t["x"], W, seg_len=args.seg_len, keep_scan_states=args.ckpt)
+    # ROTATE copies of the input, the upstream gradient and the saved activations, used in turn
+    xs = [t["x"]] + [t["x"].clone() for _ in range(ROTATE - 1)]
+    gs = [t["d_out"]] + [t["d_out"].clone() for _ in range(ROTATE - 1)]
+    saves = [ssm.mamba_layer_fwd(x, W, seg_len=args.seg_len, keep_scan_states=args.ckpt)[1] for x in xs]
     ws = torch.empty(ssm.mamba_layer_bwd_workspace_size(t["x"], W, seg_len=args.seg_len), dtype=torch.uint8,
                      device=dev)
-    out = ssm.mamba_layer_bwd(t["x"], W, saved, t["d_out"], workspace=ws, seg_len=args.seg_len)
+    out = ssm.mamba_layer_bwd(xs[0], W, saves[0], gs[0], workspace=ws, seg_len=args.seg_len)
+    turn = [0]
 
     def step(ev):
-        ssm.mamba_layer_bwd(t["x"], W, saved, t["d_out"], workspace=ws, out=out, seg_len=args.seg_len,
+        i = turn[0]
+        turn[0] = (i + 1) % ROTATE
+        ssm.mamba_layer_bwd(xs[i], W, saves[i], gs[i], workspace=ws, out=out, seg_len=args.seg_len,
                             stage_events=ev)
 
     ms_step, stages = timed(step, 11, steps, warmup)
     stats = step_stats(step, steps) if want_stats else None
-    del t, W, saved, ws, out
+    del t, W, xs, gs, saves, ws, out
     torch.cuda.empty_cache()
     return ms_step, {name: float(stages[:, i].mean()) for i, name in enumerate(LAYER_STAGES)}, stats
 
@@ -715,22 +749,31 @@ def run_backbone(args, cfg):
     }
 
 
-def copy_probe(args):
-    """A plain device-to-device copy of 1 GiB, `steps` times: 1 GiB read + 1 GiB written per launch."""
+def copy_rate(warmup: int, steps: int):
+    """A plain device-to-device copy of 1 GiB, `steps` times after `warmup`: 1 GiB read + 1 GiB
+    written per launch.  Returns (ms per copy, GB/s of bytes read + written)."""
     import torch
     n = 1 << 28
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
     b = torch.empty_like(a)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         b.copy_(a)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         b.copy_(a)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    del a, b
+    torch.cuda.empty_cache()
+    return ms, 8 * n / (ms * 1e-3) / 1e9
+
+
+def copy_probe(args):
+    ms, gbps = copy_rate(args.warmup, args.steps)
+    n = 1 << 28
     return {"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "ms_per_copy": round(ms, 4),
-            "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}
+            "GBps": round(gbps, 1)}
 
 
 # Default (warmup, steps) per workload.  The GPU comes to the timed region from
@@ -757,8 +800,13 @@ def main():
         return
     from synth import CONFIGS, BackboneConfig, LayerConfig, RecurrenceConfig
     cfg = CONFIGS[args.workload]
-    # the CPU baseline runs first: its fork pool must not inherit a process that has used the GPU
+    all_configs = args.workload == "mamba370m" and not args.no_configs and not args.ckpt
+    # the CPU baselines run first: their fork pools must not inherit a process that has used the GPU
     cpu = None
+    cpu_configs = {}
+    if not args.no_cpu_baseline and all_configs:
+        cpu_configs = {k: (cpu_baseline_layer if k == "layer" else cpu_baseline_scan)(CONFIGS[k])
+                       for k in ("mamba130m", "mamba2p8b", "layer")}
     if not args.no_cpu_baseline:
         if isinstance(cfg, LayerConfig):
             cpu = cpu_baseline_layer(cfg)
@@ -773,9 +821,9 @@ def main():
     # and timed steps then follow GPU work, not seconds of idling while the host draws inputs.  (After
     # idling, the first ~15 ms of work run slower while the clocks ramp up; a training loop, which
     # keeps the GPU busy, does not see that.)
-    all_configs = args.workload == "mamba370m" and not args.no_configs and not args.ckpt
     head_step = None
     configs = {}
+    copy = None
     if all_configs:
         head_step = prepare_scan(args, cfg)
         small = {k: prepare_scan(args, CONFIGS[k]) for k in ("tiny", "mamba130m")}
@@ -792,7 +840,16 @@ def main():
     if cpu is not None:
         line["cpu_baseline"] = cpu
     if all_configs:
+        # the box's practical HBM rate, beside the published peak (after the headline: a bandwidth-bound
+        # copy leaves the clocks low for the next few milliseconds of compute)
+        copy = copy_rate(5, 10)[1]
+    if copy is not None:
+        line["hbm"]["measured_copy_GBps"] = round(copy, 1)
+        line["hbm"]["frac_of_measured_copy"] = round(line["hbm"]["effective_GBps"] / copy, 4)
+    if all_configs:
         configs.update(run_configs(args, ("mamba2p8b", "layer")))
+        for k, v in cpu_configs.items():
+            configs[k]["cpu_baseline"] = v
         line["configs"] = configs
     print(json.dumps(line), flush=True)
 
