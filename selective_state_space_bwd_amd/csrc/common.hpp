@@ -64,14 +64,48 @@ __device__ __forceinline__ void load_row(const bf16* __restrict__ p, float (&v)[
   }
 }
 
+// ---- raw buffer access ---------------------------------------------------------
+// A gfx9 buffer resource over [base, base + 4 GiB) (no stride; DATA_FORMAT 32 in
+// word 3).  A load or store adds a 32-bit per-lane byte offset (VGPR) and a
+// wave-uniform byte offset (SGPR) to the base, so no 64-bit per-lane address is
+// formed or kept.  The base must be the same in every lane of the wave.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes buf_res(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+// element `i` of the lane at wave-uniform byte offset `soff`
+template <typename T>
+__device__ __forceinline__ float buf_ld(BufRes r, uint32_t i, uint32_t soff);
+template <>
+__device__ __forceinline__ float buf_ld<float>(BufRes r, uint32_t i, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, i * 4u, soff, 0));
+}
+template <>
+__device__ __forceinline__ float buf_ld<bf16>(BufRes r, uint32_t i, uint32_t soff) {
+  return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, i * 2u, soff, 0)) << 16);
+}
+template <typename T>
+__device__ __forceinline__ void buf_st(BufRes r, uint32_t i, uint32_t soff, float v);
+template <>
+__device__ __forceinline__ void buf_st<float>(BufRes r, uint32_t i, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, i * 4u, soff, 0);
+}
+template <>
+__device__ __forceinline__ void buf_st<bf16>(BufRes r, uint32_t i, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16>(v).bits, r, i * 2u, soff, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
 
 // ---- cross-lane moves (DPP and the gfx950 permlane swaps) -----------------
+// Every control used here (quad_perm, row_ror, row_half_mirror) reads a valid
+// lane for every lane, so the "old" value never shows; bound_ctrl lets the
+// compiler skip materialising it.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
@@ -131,6 +165,53 @@ __device__ __forceinline__ void wave_reduce_scatter(float (&v)[V], int lane) {
   if constexpr (V <= 8) v[0] += dpp<kRowHalfMirror>(v[0]);
   v[0] += dpp<kQuadXor1>(v[0]);
   v[0] += dpp<kQuadXor2>(v[0]);
+}
+
+// Reduce-scatter of V values per lane (V = 2, 4 or 8) over the 32 lanes that
+// share lane bit 0 (the two halves of a lane pair hold different values and are
+// never added together).  On return v[0] of lane l holds the sum, over the 32
+// lanes with l's bit 0, of the input element with index pair_index<V>(l); the
+// lanes with pair_writer<V>(l) hold each such sum once.  Steps: lane bits 5 and
+// 4 exchange halves with permlane32/16 swaps, bit 1 (V = 8) with a quad DPP;
+// the bits left once a single value remains are summed with DPP rotations
+// (row_ror 4 then 8 sums over bits 2 and 3 and leaves bits 0 and 1 alone).
+constexpr int kRowRor4 = 0x124;  // lane l <- l + 4 (mod 16) inside a 16-lane row
+template <int V>
+__device__ __forceinline__ void pair_reduce_scatter(float (&v)[V], int lane) {
+  static_assert(V == 2 || V == 4 || V == 8, "V must be 2, 4 or 8");
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {  // lane bit 5
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + V / 2]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (V >= 4) {  // lane bit 4
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + V / 4]), false, false);
+      v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+    v[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (V >= 8) {  // lane bit 1 (partner l ^ 2)
+    const bool hi = lane & 2;
+    const float keep = hi ? v[1] : v[0];
+    const float send = hi ? v[0] : v[1];
+    v[0] = keep + dpp<kQuadXor2>(send);
+  } else {
+    v[0] += dpp<kQuadXor2>(v[0]);
+  }
+  v[0] += dpp<kRowRor4>(v[0]);
+  v[0] += dpp<kRowRor8>(v[0]);
+}
+template <int V>
+__device__ __forceinline__ int pair_index(int lane) {
+  return V == 8 ? (((lane >> 3) & 6) | ((lane >> 1) & 1)) : V == 4 ? ((lane >> 4) & 3) : ((lane >> 5) & 1);
+}
+template <int V>
+__device__ __forceinline__ bool pair_writer(int lane) {
+  return (lane & (V == 8 ? 0x0C : V == 4 ? 0x0E : 0x1E)) == 0;
 }
 
 // ---- error reporting ---------------------------------------------------------

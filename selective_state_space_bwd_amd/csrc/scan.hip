@@ -393,20 +393,20 @@ struct ChunkTile {
   static constexpr int kLdsSteps = kChunk - kRegSteps;
 };
 
-// float asks for two waves per SIMD (B | C staged in LDS take VGPRs the
-// compiler would otherwise spend at the cost of occupancy); bf16 leaves the
-// choice to the compiler.
+// The float sweep (bf16 storage takes the lane-pair sweep below, measured 9 %
+// faster there and 3 % slower here); two waves per SIMD.
 // GCK: `ckpt` holds the exact state before every chunk (the forward's
 // checkpoints) instead of the local ones of the summary pass; seg_h, ckpt_sd
 // are then unused.
 template <typename T, int NS, bool SOFTPLUS, bool GCK>
-__global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
+__global__ __launch_bounds__(kBlock, 2) void scan_bwd_main(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
     const T* __restrict__ z, const T* __restrict__ dout, T* __restrict__ d_u,
     T* __restrict__ d_delta, T* __restrict__ d_z, const float* __restrict__ ckpt,
     const float* __restrict__ ckpt_sd, const float* __restrict__ seg_h, const float* __restrict__ seg_g,
     float* __restrict__ part_bc, float* __restrict__ part_a, ScanShape sh) {
+  static_assert(sizeof(T) == 4, "the one-channel-per-lane sweep is the float path");
   constexpr int kLogNS = NS == 16 ? 4 : NS == 8 ? 3 : NS == 4 ? 2 : NS == 2 ? 1 : 0;
   constexpr int kRep = kWave / NS;  // lanes holding each reduced value
   constexpr int kReg = ChunkTile<NS>::kRegSteps;
@@ -441,28 +441,22 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
   const int c_first = t0 / kChunk, c_last = (t1 - 1) / kChunk;
   const T* __restrict__ Bb = Bm + row0 * sh.ld_bc;
   const T* __restrict__ Cb = Cm + row0 * sh.ld_bc;
-  // float, and bf16 when the chunk states are given: the last chunk's B | C rows
-  // go to LDS before the sweep, and each chunk fetches the next one's while it
-  // computes.  bf16 rebuilding its own states reads them per step with scalar
-  // loads instead (its VGPR budget has no room for the staged rows).
-  constexpr bool kStage = sizeof(T) == 4 || GCK;
-  if (kStage) {
-    if (tid < kChunk * 2 * NS)
-      (&bcs[c_last & 1][0][0])[tid] =
-          bc_element<T, NS>(Bb, Cb, sh.ld_bc, c_last * kChunk, min(kChunk, t1 - c_last * kChunk), tid);
-    __syncthreads();
-  }
+  // the last chunk's B | C rows go to LDS before the sweep, and each chunk
+  // fetches the next one's while it computes
+  if (tid < kChunk * 2 * NS)
+    (&bcs[c_last & 1][0][0])[tid] =
+        bc_element<T, NS>(Bb, Cb, sh.ld_bc, c_last * kChunk, min(kChunk, t1 - c_last * kChunk), tid);
+  __syncthreads();
   // a chunk's loads: its per-step channel values (delta, u, z, d_out) and, when
   // the states are given, its starting state.  With given states the next
   // chunk's loads go out at the end of the current one, before its barrier, into
   // registers it no longer needs (measured: 2-3 % off the sweep); a sweep that
   // rebuilds its states issues them at the chunk's start (earlier costs bf16 a
   // tenth and float nothing).
-  // Per-step rows addressed as scalar row pointer + 32-bit lane offset: fewer
-  // VALU address operations in bf16 and with given states (measured in the ISA:
-  // 6 % and 4 % fewer VALU instructions); the float sweep that rebuilds its
-  // states keeps 64-bit lane addresses, which spill less there.
-  constexpr bool kRowAddr = sizeof(T) == 2 || GCK;
+  // Per-step rows addressed as scalar row pointer + 32-bit lane offset with
+  // given states (measured in the ISA: 4 % fewer VALU instructions); the sweep
+  // that rebuilds its states keeps 64-bit lane addresses, which spill less there.
+  constexpr bool kRowAddr = GCK;
   float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
   float hg[NS];
   const auto load_chunk = [&](int c) {
@@ -497,7 +491,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     const int tc = c * kChunk;
     const int nv = min(kChunk, t1 - tc);
     const int buf = c & 1;
-    const float bc_next = kStage && c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
+    const float bc_next = c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
     // state before the chunk: given, or local checkpoint + decayed carry-in
     float h[NS];
     if (GCK) {
@@ -524,12 +518,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     for (int j = 0; j < kChunk; ++j) {
       if (j < nv) {
         float Bv[NS], Cv[NS];
-        if (kStage) {
-          bc_row<NS>(bcs[buf], j, Bv, Cv);
-        } else {
-          load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
-          load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
-        }
+        bc_row<NS>(bcs[buf], j, Bv, Cv);
         const float sz = sigmoid(zr[j]);
         dy[j] = active ? gr[j] * zr[j] * sz : 0.f;
         const float dzf = gr[j] * sz * (1.f + zr[j] * (1.f - sz));
@@ -572,12 +561,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     for (int j = kChunk - 1; j >= 0; --j) {
       if (j < nv) {
         float Bv[NS], Cv[NS];
-        if (kStage) {
-          bc_row<NS>(bcs[buf], j, Bv, Cv);
-        } else {
-          load_row<NS>(Bm + (row0 + tc + j) * sh.ld_bc, Bv);
-          load_row<NS>(Cm + (row0 + tc + j) * sh.ld_bc, Cv);
-        }
+        bc_row<NS>(bcs[buf], j, Bv, Cv);
         float aj[NS];
         if (j < kLds) {
 #pragma unroll
@@ -628,7 +612,7 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     }
     if (GCK && c > c_first) load_chunk(c - 1);
     // the buffer written here was last read before the previous chunk's barrier
-    if (kStage && c > c_first && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
+    if (c > c_first && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
     __syncthreads();
     for (int q = tid; q < kChunk * 2 * NS; q += kBlock) {
       const int j = q / (2 * NS), k = q - j * (2 * NS);
@@ -644,6 +628,297 @@ __global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
 #pragma unroll
   for (int n = 0; n < NS; ++n) part_a[(sg * (NS + 1) + n) * Di + d] = dA[n];
   part_a[(sg * (NS + 1) + NS) * Di + d] = dD;
+}
+
+
+// 3'. the main sweep on lane pairs (bf16 storage).  Lanes 2i and 2i+1 of a wave share the
+// channels d = 2i and 2i+1: lane l owns channel l (its per-step loads, gate
+// math and outputs) and holds, for both channels, the half of the states with
+// index in [NH q, NH q + NH), q = l & 1.  The d_B | d_C sums over channels then
+// cross only the 32 lanes of one state half (half the values per lane of the
+// one-channel-per-lane layout, so half the cross-lane work), and each
+// per-channel sum over states (y, sum g B, sum A a h g) takes one DPP add
+// across the pair.  The partner channel's delta, delta u and dy come over by
+// DPP.  Register roles: index 0 holds the lane's own channel, index 1 the
+// partner's, so the partner's partial for this lane's channel is always its
+// index-1 value.
+template <int NS>
+__device__ __forceinline__ void bc_half(const float (&bcs)[kChunk][2 * NS], int j, int n0, float (&Bv)[NS / 2],
+                                        float (&Cv)[NS / 2]) {
+  constexpr int NH = NS / 2;
+  if constexpr (NH % 4 == 0) {
+    const float4* pb = reinterpret_cast<const float4*>(&bcs[j][n0]);
+    const float4* pc = reinterpret_cast<const float4*>(&bcs[j][NS + n0]);
+#pragma unroll
+    for (int k = 0; k < NH / 4; ++k) {
+      const float4 b = pb[k], c = pc[k];
+      Bv[4 * k] = b.x; Bv[4 * k + 1] = b.y; Bv[4 * k + 2] = b.z; Bv[4 * k + 3] = b.w;
+      Cv[4 * k] = c.x; Cv[4 * k + 1] = c.y; Cv[4 * k + 2] = c.z; Cv[4 * k + 3] = c.w;
+    }
+  } else {
+    const float2* pb = reinterpret_cast<const float2*>(&bcs[j][n0]);
+    const float2* pc = reinterpret_cast<const float2*>(&bcs[j][NS + n0]);
+#pragma unroll
+    for (int k = 0; k < NH / 2; ++k) {
+      const float2 b = pb[k], c = pc[k];
+      Bv[2 * k] = b.x; Bv[2 * k + 1] = b.y;
+      Cv[2 * k] = c.x; Cv[2 * k + 1] = c.y;
+    }
+  }
+}
+
+template <typename T, int NS, bool SOFTPLUS, bool GCK>
+__global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
+    const T* __restrict__ z, const T* __restrict__ dout, T* __restrict__ d_u,
+    T* __restrict__ d_delta, T* __restrict__ d_z, const float* __restrict__ ckpt,
+    const float* __restrict__ ckpt_sd, const float* __restrict__ seg_h, const float* __restrict__ seg_g,
+    float* __restrict__ part_bc, float* __restrict__ part_a, ScanShape sh) {
+  static_assert(sizeof(T) == 2, "the lane-pair sweep is the bf16 path");
+  constexpr int NH = NS / 2;
+  constexpr int kReg = ChunkTile<NS>::kRegSteps;
+  constexpr int kLds = ChunkTile<NS>::kLdsSteps;
+  static_assert(NS % 4 == 0, "a*h rows move through LDS as float4");
+  __shared__ float red[2][kBlock / kWave][kChunk][2 * NS];
+  __shared__ float4 lds_ah[kLds > 0 ? kLds : 1][NS / 4][kBlock];
+  __shared__ __align__(16) float bcs[2][kChunk][2 * NS];
+  __shared__ float red_sink[kBlock];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int n0 = (lane & 1) * NH;  // first state of this lane's half
+  const int d = blockIdx.x * kBlock + tid, dq = d ^ 1;
+  const int s = blockIdx.y, b = blockIdx.z;
+  const int Di = sh.Di;
+  const bool active = d < Di, active_q = dq < Di;
+  const int dc = active ? d : Di - 1, dqc = active_q ? dq : Di - 1;
+  const size_t row0 = (size_t)b * sh.T;
+  const size_t sg = (size_t)b * sh.nseg + s;
+  const bool last_seg = s == sh.nseg - 1;
+  // [.., N, Di] state blocks: element (n0 + k, channel) at lane element offset
+  // o0 | o1 and wave-uniform byte offset k Di 4 from the block
+  const uint32_t o0 = (uint32_t)(n0 * Di + dc), o1 = (uint32_t)(n0 * Di + dqc);
+  const uint32_t row_bytes = (uint32_t)Di * 4u;
+  const BufRes rsh = buf_res(seg_h + sg * NS * Di);
+
+  float A2[2][NH];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    A2[0][k] = -expf(A_log[(size_t)dc * NS + n0 + k]) * kLog2e;
+    A2[1][k] = -expf(A_log[(size_t)dqc * NS + n0 + k]) * kLog2e;
+  }
+  const float Dd = Dp[dc];
+  float g[2][NH], dA[2][NH];
+  const BufRes rsg = buf_res(seg_g + sg * NS * Di);
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    g[0][k] = last_seg ? 0.f : buf_ld<float>(rsg, o0, k * row_bytes);
+    g[1][k] = last_seg ? 0.f : buf_ld<float>(rsg, o1, k * row_bytes);
+    dA[0][k] = 0.f;
+    dA[1][k] = 0.f;
+  }
+  float dD = 0.f;
+
+  const int t0 = s * sh.seg, t1 = min(sh.T, t0 + sh.seg);
+  const int c_first = t0 / kChunk, c_last = (t1 - 1) / kChunk;
+  const T* __restrict__ Bb = Bm + row0 * sh.ld_bc;
+  const T* __restrict__ Cb = Cm + row0 * sh.ld_bc;
+  // the last chunk's B | C rows go to LDS before the sweep; each chunk fetches
+  // the next one's while it computes
+  if (tid < kChunk * 2 * NS)
+    (&bcs[c_last & 1][0][0])[tid] =
+        bc_element<T, NS>(Bb, Cb, sh.ld_bc, c_last * kChunk, min(kChunk, t1 - c_last * kChunk), tid);
+  __syncthreads();
+  // a chunk's loads: its per-step values of the lane's own channel (delta, u,
+  // z, d_out) and, when the states are given, its starting states.  With given
+  // states the next chunk's loads go out at the end of the current one.  Rows
+  // of a chunk sit at wave-uniform byte offsets from the chunk's first row.
+  const uint32_t step_bytes = (uint32_t)(Di * sizeof(T)), zstep_bytes = (uint32_t)(sh.ld_z * sizeof(T));
+  float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
+  float hg[2][NH];
+  const auto load_chunk = [&](int c) {
+    const int tc = c * kChunk;
+    const int nv = min(kChunk, t1 - tc);
+    if (GCK) {
+      const size_t cc = (size_t)b * sh.nchunk + c;
+      const BufRes rc = buf_res(ckpt + cc * NS * Di);
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        hg[0][k] = buf_ld<float>(rc, o0, k * row_bytes);
+        hg[1][k] = buf_ld<float>(rc, o1, k * row_bytes);
+      }
+    }
+    const size_t rowc = row0 + tc;
+    const BufRes rd = buf_res(delta + rowc * Di), ru = buf_res(u + rowc * Di), rg = buf_res(dout + rowc * Di);
+    const BufRes rz = buf_res(z + rowc * sh.ld_z);
+    // steps past a ragged chunk's end read its last step again (unused)
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const uint32_t jj = (uint32_t)min(j, nv - 1);
+      dl[j] = buf_ld<T>(rd, dc, jj * step_bytes);
+      uu[j] = buf_ld<T>(ru, dc, jj * step_bytes);
+      zr[j] = buf_ld<T>(rz, dc, jj * zstep_bytes);
+      gr[j] = buf_ld<T>(rg, dc, jj * step_bytes);
+    }
+  };
+  if (GCK) load_chunk(c_last);
+  for (int c = c_last; c >= c_first; --c) {
+    const int tc = c * kChunk;
+    const int nv = min(kChunk, t1 - tc);
+    const int buf = c & 1;
+    const float bc_next = c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
+    // states before the chunk: given, or local checkpoint + decayed carry-in
+    float h[2][NH];
+    if (GCK) {
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        h[0][k] = hg[0][k];
+        h[1][k] = hg[1][k];
+      }
+    } else if (c == c_first) {
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        h[0][k] = (s == 0) ? 0.f : buf_ld<float>(rsh, o0, k * row_bytes);
+        h[1][k] = (s == 0) ? 0.f : buf_ld<float>(rsh, o1, k * row_bytes);
+      }
+    } else {
+      // local checkpoint + carry-in decayed over the segment's steps before the chunk
+      const size_t cc = (size_t)b * sh.nchunk + c;
+      const BufRes rsd = buf_res(ckpt_sd + cc * Di), rc = buf_res(ckpt + cc * NS * Di);
+      const float sd0 = buf_ld<float>(rsd, dc, 0), sd1 = buf_ld<float>(rsd, dqc, 0);
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        const float hin0 = (s == 0) ? 0.f : buf_ld<float>(rsh, o0, k * row_bytes);
+        const float hin1 = (s == 0) ? 0.f : buf_ld<float>(rsh, o1, k * row_bytes);
+        h[0][k] = fmaf(fast_exp2(A2[0][k] * sd0), hin0, buf_ld<float>(rc, o0, k * row_bytes));
+        h[1][k] = fmaf(fast_exp2(A2[1][k] * sd1), hin1, buf_ld<float>(rc, o1, k * row_bytes));
+      }
+    }
+    if (!GCK) load_chunk(c);
+    const BufRes rdz = buf_res(d_z + (row0 + tc) * sh.ld_z);
+    const BufRes rdu = buf_res(d_u + (row0 + tc) * Di), rdd = buf_res(d_delta + (row0 + tc) * Di);
+    // forward: rebuild the chunk's states, keep a_t h_{t-1}
+    float ah[kReg][NS];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < nv) {
+        float Bv[NH], Cv[NH];
+        bc_half<NS>(bcs[buf], j, n0, Bv, Cv);
+        const float sz = sigmoid(zr[j]);
+        dy[j] = active ? gr[j] * zr[j] * sz : 0.f;
+        const float dzf = gr[j] * sz * (1.f + zr[j] * (1.f - sz));
+        const float du = dl[j] * uu[j];
+        const float dlq = dpp<kQuadXor1>(dl[j]), duq = dpp<kQuadXor1>(du), dyq = dpp<kQuadXor1>(dy[j]);
+        float y0, y1;
+        float dC[NH], aj[NS];
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+          aj[k] = fast_exp2(dl[j] * A2[0][k]) * h[0][k];
+          h[0][k] = fmaf(du, Bv[k], aj[k]);
+          y0 = k == 0 ? Cv[k] * h[0][k] : fmaf(Cv[k], h[0][k], y0);
+          aj[NH + k] = fast_exp2(dlq * A2[1][k]) * h[1][k];
+          h[1][k] = fmaf(duq, Bv[k], aj[NH + k]);
+          y1 = k == 0 ? Cv[k] * h[1][k] : fmaf(Cv[k], h[1][k], y1);
+          dC[k] = fmaf(dyq, h[1][k], dy[j] * h[0][k]);
+        }
+        // this lane's channel: its own half of the states plus the partner's
+        // partial over the other half
+        const float y = fmaf(Dd, uu[j], y0 + dpp<kQuadXor1>(y1));
+        if (j < kLds) {
+#pragma unroll
+          for (int v = 0; v < NS / 4; ++v)
+            lds_ah[j < kLds ? j : 0][v][tid] = make_float4(aj[4 * v], aj[4 * v + 1], aj[4 * v + 2], aj[4 * v + 3]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < NS; ++k) ah[j >= kLds ? j - kLds : 0][k] = aj[k];
+        }
+        if (active) buf_st<T>(rdz, d, j * zstep_bytes, y * dzf);
+        pair_reduce_scatter<NH>(dC, lane);
+        *(pair_writer<NH>(lane) ? &red[buf][wave][j][NS + n0 + pair_index<NH>(lane)] : &red_sink[tid]) = dC[0];
+      }
+    }
+    // The reverse walk reads B | C again rather than keeping the forward's
+    // values live across the walks.
+    asm volatile("" ::: "memory");
+    // reverse: adjoint through the chunk
+#pragma unroll
+    for (int j = kChunk - 1; j >= 0; --j) {
+      if (j < nv) {
+        float Bv[NH], Cv[NH];
+        bc_half<NS>(bcs[buf], j, n0, Bv, Cv);
+        float aj[NS];
+        if (j < kLds) {
+#pragma unroll
+          for (int v = 0; v < NS / 4; ++v) {
+            const float4 w4 = lds_ah[j < kLds ? j : 0][v][tid];
+            aj[4 * v] = w4.x;
+            aj[4 * v + 1] = w4.y;
+            aj[4 * v + 2] = w4.z;
+            aj[4 * v + 3] = w4.w;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < NS; ++k) aj[k] = ah[j >= kLds ? j - kLds : 0][k];
+        }
+        // deltas of the step, opaque to the compiler: a_t is recomputed here
+        // rather than kept from the forward walk
+        float dlr = dl[j], dlqr = dpp<kQuadXor1>(dl[j]);
+        asm volatile("" : "+v"(dlr), "+v"(dlqr));
+        const float du = active ? dlr * uu[j] : 0.f;
+        const float duq = dpp<kQuadXor1>(du), dyq = dpp<kQuadXor1>(dy[j]);
+        float sgb0, sgb1, saw0, saw1;
+        float dB[NH];
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+          const float gn0 = fmaf(dy[j], Cv[k], g[0][k]);
+          const float w0 = gn0 * aj[k];
+          saw0 = k == 0 ? A2[0][k] * w0 : fmaf(A2[0][k], w0, saw0);
+          dA[0][k] = fmaf(dlr, w0, dA[0][k]);
+          sgb0 = k == 0 ? gn0 * Bv[k] : fmaf(gn0, Bv[k], sgb0);
+          g[0][k] = fast_exp2(dlr * A2[0][k]) * gn0;
+          const float gn1 = fmaf(dyq, Cv[k], g[1][k]);
+          const float w1 = gn1 * aj[NH + k];
+          saw1 = k == 0 ? A2[1][k] * w1 : fmaf(A2[1][k], w1, saw1);
+          dA[1][k] = fmaf(dlqr, w1, dA[1][k]);
+          sgb1 = k == 0 ? gn1 * Bv[k] : fmaf(gn1, Bv[k], sgb1);
+          g[1][k] = fast_exp2(dlqr * A2[1][k]) * gn1;
+          dB[k] = fmaf(gn1, duq, gn0 * du);
+        }
+        const float sgb = sgb0 + dpp<kQuadXor1>(sgb1);
+        const float saw = saw0 + dpp<kQuadXor1>(saw1);
+        float ddl = fmaf(saw, kLn2, uu[j] * sgb);
+        if (SOFTPLUS) ddl = dl[j] > 20.f ? ddl : ddl * (1.f - fast_exp2(-dl[j] * kLog2e));
+        dD = fmaf(dy[j], uu[j], dD);
+        if (active) {
+          buf_st<T>(rdu, d, j * step_bytes, fmaf(Dd, dy[j], dl[j] * sgb));
+          buf_st<T>(rdd, d, j * step_bytes, ddl);
+        }
+        pair_reduce_scatter<NH>(dB, lane);
+        *(pair_writer<NH>(lane) ? &red[buf][wave][j][n0 + pair_index<NH>(lane)] : &red_sink[tid]) = dB[0];
+      }
+    }
+    if (GCK && c > c_first) load_chunk(c - 1);
+    // the buffer written here was last read before the previous chunk's barrier
+    if (c > c_first && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
+    __syncthreads();
+    for (int v = tid; v < kChunk * 2 * NS; v += kBlock) {
+      const int j = v / (2 * NS), k = v - j * (2 * NS);
+      if (j < nv) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kBlock / kWave; ++w) acc += red[buf][w][j][k];
+        part_bc[(((size_t)blockIdx.x * sh.Bt + b) * sh.T + tc + j) * 2 * NS + k] = acc;
+      }
+    }
+  }
+  // each (channel, state) of the lane pair is written by exactly one lane
+  const BufRes rpa = buf_res(part_a + sg * (NS + 1) * Di);
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    if (active) buf_st<float>(rpa, o0, k * row_bytes, dA[0][k]);
+    if (active_q) buf_st<float>(rpa, o1, k * row_bytes, dA[1][k]);
+  }
+  if (active) buf_st<float>(rpa, d, NS * row_bytes, dD);
 }
 
 // ---------------------------------------------------------------------------
@@ -973,10 +1248,18 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
                          w.seg_sd, sh);
   }
   mark(2);
-#define SSM_MAIN(SP, GCK)                                                                                     \
-  hipLaunchKernelGGL((scan_bwd_main<T, NS, SP, GCK>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz, \
-                     tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),                 \
-                     GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh)
+  // float sweeps one channel per lane, bf16 on lane pairs
+#define SSM_MAIN(SP, GCK)                                                                                        \
+  do {                                                                                                           \
+    if constexpr (sizeof(T) == 4)                                                                                \
+      hipLaunchKernelGGL((scan_bwd_main<T, NS, SP, GCK>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz, \
+                         tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),               \
+                         GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);            \
+    else                                                                                                         \
+      hipLaunchKernelGGL((scan_bwd_pair<T, NS, SP, GCK>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz, \
+                         tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),               \
+                         GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);            \
+  } while (0)
   if (h_ckpt) {
     if (flags & SSM_BWD_SOFTPLUS) SSM_MAIN(true, true);
     else SSM_MAIN(false, true);
