@@ -441,16 +441,16 @@ def run_scan(args, cfg, step=None):
     return line
 
 
-def config_entry_scan(args, key, cfg, step=None):
+def config_entry_scan(args, key, cfg, warmup, step=None):
     """One other scan workload of the benchmark, timed in the same run."""
-    ms_step, stages, stats = measure_scan(args, cfg, args.steps, args.warmup, step=step)
+    ms_step, stages, stats = measure_scan(args, cfg, args.steps, warmup, step=step)
     call_bytes, main_bytes = scan_bytes(cfg, False)
     main_ms = float(stages[:, 2].mean())
     med = stats["ms_median"]
     roof = scan_roofline(cfg, main_ms, med, main_bytes, call_bytes, recorded_traffic(key, "scan_bwd_main"),
                          recorded_traffic(key, "ssm_scan_bwd"))
-    return {"workload": cfg.name, "dtype": cfg.dtype, "ms_per_step": round(ms_step, 4), **{k: stats[k] for k in
-            ("ms_median", "ms_p10", "ms_p90")},
+    return {"workload": cfg.name, "dtype": cfg.dtype, "steps": args.steps, "warmup": warmup,
+            "ms_per_step": round(ms_step, 4), **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
             "state_elements_per_s": round(cfg.state_elements / (med * 1e-3), 1),
             "hbm_effective_frac": round(call_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "stages_ms": {"summary": round(float(stages[:, 0].mean()), 4),
@@ -541,8 +541,8 @@ def run_layer(args, cfg):
     return line
 
 
-def config_entry_layer(args, cfg):
-    ms_step, st, stats = measure_layer(args, cfg, args.steps, args.warmup)
+def config_entry_layer(args, cfg, warmup):
+    ms_step, st, stats = measure_layer(args, cfg, args.steps, warmup)
     gemm_flops = layer_gemm_flops(cfg)
     med = stats["ms_median"]
     dom = max(st, key=st.get)
@@ -558,7 +558,7 @@ def config_entry_layer(args, cfg):
                  "algorithmic_bytes": nbytes}
     droof.update({"kernel": f"{dom} stage" + (" (summary, carry, main sweep, finalize)" if dom == "scan_bwd" else ""),
                   "kernel_ms": round(st[dom], 4)})
-    return {"workload": cfg.name, "dtype": "bf16", "ms_per_step": round(ms_step, 4),
+    return {"workload": cfg.name, "dtype": "bf16", "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
             **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
             "state_elements_per_s": round(cfg.state_elements / (med * 1e-3), 1),
             "stages_ms": {k: round(v, 4) for k, v in st.items()},
@@ -566,17 +566,19 @@ def config_entry_layer(args, cfg):
             "dominant_kernel": droof}
 
 
-def config_entry_tiny(args, cfg, step=None):
-    ms_step, _, stats = measure_scan(args, cfg, args.steps, args.warmup, step=step)
-    return {"workload": cfg.name, "dtype": cfg.dtype,
+def config_entry_tiny(args, cfg, warmup, step=None):
+    ms_step, _, stats = measure_scan(args, cfg, args.steps, warmup, step=step)
+    return {"workload": cfg.name, "dtype": cfg.dtype, "steps": args.steps, "warmup": warmup,
             "role": "parity case (checked against the fp64 oracle and finite differences by the tests); "
                     "launch-bound, timed here only for completeness",
             "ms_per_step": round(ms_step, 4), **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")}}
 
 
 def run_configs(args, keys, steps=None):
-    """The benchmark's other workloads, timed in this run (same steps and warm-up); `steps` may hold
-    step functions of scan workloads whose inputs are already on the GPU."""
+    """The benchmark's other workloads, timed in this run with the same number of timed steps; each
+    warms up for the run's warm-up steps or its own default, whichever is more (the two small ones run
+    before the headline, so this also brings the clocks up before the headline's warm-up).  `steps`
+    may hold step functions of scan workloads whose inputs are already on the GPU."""
     from synth import CONFIGS
     out = {}
     steps = steps or {}
@@ -584,13 +586,14 @@ def run_configs(args, keys, steps=None):
         if key == args.workload:
             continue
         cfg = CONFIGS[key]
+        warmup = max(args.warmup, DEFAULT_STEPS[key][0])
         print(f"bench: timing {cfg.name}", file=sys.stderr, flush=True)
         if key == "tiny":
-            out[key] = config_entry_tiny(args, cfg, step=steps.pop(key, None))
+            out[key] = config_entry_tiny(args, cfg, warmup, step=steps.pop(key, None))
         elif key == "layer":
-            out[key] = config_entry_layer(args, cfg)
+            out[key] = config_entry_layer(args, cfg, warmup)
         else:
-            out[key] = config_entry_scan(args, key, cfg, step=steps.pop(key, None))
+            out[key] = config_entry_scan(args, key, cfg, warmup, step=steps.pop(key, None))
     return out
 
 
