@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--recompute", action="store_true",
                     help="backbone: keep only the layer inputs (SSM_KEEP_INPUTS); the backward reruns each layer's "
                          "forward")
+    ap.add_argument("--recompute-inputs", action="store_true",
+                    help="layer and backbone: the forward keeps y instead of the products' inputs (gated, u, xn) "
+                         "and the backward recomputes the gate, the conv + SiLU and the RMSNorm forward")
     ap.add_argument("--ckpt", action="store_true",
                     help="time the backward that takes the scan's state before every 8-step chunk from the "
                          "forward (scan workloads: ssm_scan_bwd_ckpt after one ssm_scan_fwd; layer and backbone: "
@@ -466,7 +469,14 @@ LAYER_STAGES = ("gate_fwd", "out_proj", "conv_silu_fwd", "scan_bwd", "dt_proj", 
                 "rmsnorm_fwd", "in_proj", "rmsnorm_bwd")
 
 
-def measure_layer(args, cfg, steps, warmup, want_stats=True):
+# what the layer forward keeps for the backward: the products' inputs (gated, u, xn, as the page's
+# MambaLayerFlat keeps gated, u and post_norm), or only y (the backward recomputes the gate, the conv + SiLU
+# and the RMSNorm forward, 0.25 GB less activation memory per layer of the full layer shape)
+LAYER_SAVED_KEPT = "xz, xdbl, delta and the products' inputs gated, u, xn (the page's acts keep gated, u, post_norm)"
+LAYER_SAVED_LEAN = "xz, xdbl, delta, y; the gate, conv + SiLU and RMSNorm forward recomputed in the backward"
+
+
+def measure_layer(args, cfg, steps, warmup, want_stats=True, keep_inputs=True):
     import torch
 
     import selective_state_space_bwd_amd as ssm
@@ -481,7 +491,8 @@ def measure_layer(args, cfg, steps, warmup, want_stats=True):
     # ROTATE copies of the input, the upstream gradient and the saved activations, used in turn
     xs = [t["x"]] + [t["x"].clone() for _ in range(ROTATE - 1)]
     gs = [t["d_out"]] + [t["d_out"].clone() for _ in range(ROTATE - 1)]
-    saves = [ssm.mamba_layer_fwd(x, W, seg_len=args.seg_len, keep_scan_states=args.ckpt)[1] for x in xs]
+    saves = [ssm.mamba_layer_fwd(x, W, seg_len=args.seg_len, keep_scan_states=args.ckpt,
+                                 keep_gemm_inputs=keep_inputs)[1] for x in xs]
     ws = torch.empty(ssm.mamba_layer_bwd_workspace_size(t["x"], W, seg_len=args.seg_len), dtype=torch.uint8,
                      device=dev)
     out = ssm.mamba_layer_bwd(xs[0], W, saves[0], gs[0], workspace=ws, seg_len=args.seg_len)
@@ -515,7 +526,8 @@ def layer_scan_bytes(cfg):
 
 
 def run_layer(args, cfg):
-    ms_step, st, stats = measure_layer(args, cfg, args.steps, args.warmup)
+    keep = not args.recompute_inputs
+    ms_step, st, stats = measure_layer(args, cfg, args.steps, args.warmup, keep_inputs=keep)
     gemm_flops = layer_gemm_flops(cfg)
     in_tf = gemm_flops["in_proj"] / (st["in_proj"] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(in_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -530,7 +542,8 @@ def run_layer(args, cfg):
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "d_model": cfg.d_model,
                    "d_inner": cfg.d_inner, "d_state": cfg.d_state, "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv,
                    "seg_len": args.seg_len or "auto", "storage": "bf16",
-                   "scan_states": "kept by the forward" if args.ckpt else "rebuilt"},
+                   "scan_states": "kept by the forward" if args.ckpt else "rebuilt",
+                   "saved": LAYER_SAVED_KEPT if keep else LAYER_SAVED_LEAN},
         "timing": stats,
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "gemm": {"TFLOP": round(sum(gemm_flops.values()) / 1e12, 4), "ms": round(gemm_ms, 4),
@@ -543,6 +556,7 @@ def run_layer(args, cfg):
 
 def config_entry_layer(args, cfg, warmup):
     ms_step, st, stats = measure_layer(args, cfg, args.steps, warmup)
+    lean_ms, lean_st, lean_stats = measure_layer(args, cfg, args.steps, warmup, keep_inputs=False)
     gemm_flops = layer_gemm_flops(cfg)
     med = stats["ms_median"]
     dom = max(st, key=st.get)
@@ -558,12 +572,15 @@ def config_entry_layer(args, cfg, warmup):
                  "algorithmic_bytes": nbytes}
     droof.update({"kernel": f"{dom} stage" + (" (summary, carry, main sweep, finalize)" if dom == "scan_bwd" else ""),
                   "kernel_ms": round(st[dom], 4)})
-    return {"workload": cfg.name, "dtype": "bf16", "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
-            **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
+    return {"workload": cfg.name, "dtype": "bf16", "steps": args.steps, "warmup": warmup, "saved": LAYER_SAVED_KEPT,
+            "ms_per_step": round(ms_step, 4), **{k: stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
             "state_elements_per_s": round(cfg.state_elements / (med * 1e-3), 1),
             "stages_ms": {k: round(v, 4) for k, v in st.items()},
             "gemm_TFLOPs": {k: round(v / (st[k] * 1e-3) / 1e12, 1) for k, v in gemm_flops.items()},
-            "dominant_kernel": droof}
+            "dominant_kernel": droof,
+            "recompute_inputs": {"saved": LAYER_SAVED_LEAN, "ms_per_step": round(lean_ms, 4),
+                                 **{k: lean_stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
+                                 "stages_ms": {k: round(v, 4) for k, v in lean_st.items()}}}
 
 
 def config_entry_tiny(args, cfg, warmup, step=None):
@@ -705,8 +722,9 @@ def run_backbone(args, cfg):
     tl = [{k: cv(k, v) for k, v in p.items()} for p in layers]
     del bp, layers
     keep = "inputs" if args.recompute else "all"
+    keep_in = keep == "all" and not args.recompute_inputs
     _, kept = ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, seg_len=args.seg_len,
-                                     keep=keep, keep_scan_states=args.ckpt)
+                                     keep=keep, keep_scan_states=args.ckpt, keep_gemm_inputs=keep_in)
     ws = torch.empty(ssm.mamba_backbone_bwd_workspace_size(tb["inp"], tb["W_ip"], tl, seg_len=args.seg_len, keep=keep),
                      dtype=torch.uint8, device=dev)
     out = ssm.mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"], workspace=ws,
@@ -742,7 +760,8 @@ def run_backbone(args, cfg):
                    "seqlen": cfg.seqlen, "d_model": dm, "d_inner": di, "d_state": cfg.d_state,
                    "dt_rank": cfg.dt_rank, "d_conv": cfg.d_conv, "seg_len": args.seg_len or "auto",
                    "scan_states": "kept by the forward" if args.ckpt else "rebuilt",
-                   "kept": "layer inputs only (activations recomputed)" if args.recompute else "all activations"},
+                   "kept": "layer inputs only (activations recomputed)" if args.recompute else
+                   "every layer's saved activations: " + (LAYER_SAVED_KEPT if keep_in else LAYER_SAVED_LEAN)},
         "timing": stats,
         "memory": {"kept_activations_bytes": kept_bytes, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -335,16 +335,26 @@ typedef struct ssm_layer_weights {
   const void* W_out;   /* [d_model, d_inner] */
 } ssm_layer_weights;
 
-/* what the forward keeps for the backward (everything else is recomputed) */
+/* what the forward keeps for the backward (everything else is recomputed).
+ * The last three, the inputs of the out_proj, x_proj and in_proj products, are
+ * the activations mamba-rs's MambaLayerFlat keeps as gated, u and post_norm
+ * (cpu/backward.rs, backward_mamba_layer_batched, Phases B1, B5 and B7 read
+ * them); each is nullable: when given, the forward writes it and the backward
+ * reads it instead of recomputing it (the gate, the conv + SiLU and the
+ * RMSNorm forward), at 2 bytes per element of extra activation memory. */
 typedef struct ssm_layer_saved {
   void* xz;    /* [batch, seqlen, 2 d_inner] in_proj output */
   void* xdbl;  /* [batch, seqlen, dt_rank + 2 d_state] x_proj output */
   void* delta; /* [batch, seqlen, d_inner] softplus output */
-  void* y;     /* [batch, seqlen, d_inner] scan output before the gate */
+  void* y;     /* [batch, seqlen, d_inner] scan output before the gate; may be
+                  null when gated is given (only the gate recompute reads it) */
   float* h_ckpt; /* nullable: [batch, ceil(seqlen / 8), d_state, d_inner] float, the
                     scan's state before every 8-step chunk; when given, the forward
                     writes it and the backward starts its scan chunks from it
                     (ssm_scan_bwd_ckpt) instead of rebuilding the states */
+  void* gated; /* nullable: [batch, seqlen, d_inner] y * SiLU(z), out_proj's input */
+  void* u;     /* nullable: [batch, seqlen, d_inner] SiLU(conv(x_b)), x_proj's and the scan's input */
+  void* xn;    /* nullable: [batch, seqlen, d_model] RMSNorm(x), in_proj's input */
 } ssm_layer_saved;
 
 typedef struct ssm_layer_grads {
@@ -363,7 +373,7 @@ typedef struct ssm_layer_grads {
 } ssm_layer_grads;
 
 /* mamba_layer_fwd — out [batch, seqlen, d_model] and the saved activations
- * (all four buffers of `saved` are written).  Workspace:
+ * (every non-null buffer of `saved` is written).  Workspace:
  * mamba_layer_fwd_workspace_size(). */
 size_t mamba_layer_fwd_workspace_size(const ssm_layer_dims* dims);
 int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* out, const ssm_layer_saved* saved,
@@ -373,12 +383,14 @@ int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* out, const 
  * d_out = dL/d out, writes d_x = dL/dx (bf16, including the residual path) and
  * every parameter gradient (float; overwritten, or added into when
  * grads->accumulate is set, to sum micro-batches).  Recomputes RMSNorm, the conv
- * + SiLU output, the gate and the scan states on the way.  Workspace:
+ * + SiLU output and the gate unless `saved` holds them (xn, u, gated), and the
+ * scan states unless it holds h_ckpt.  Workspace:
  * mamba_layer_bwd_workspace_size().
  * mamba_layer_bwd_timed: same, recording caller-created hipEvent_t handles
  * (11, each nullable) around its ten stages: [0] start, then after the gate
  * recompute, out_proj, conv recompute, scan, dt_proj, x_proj, conv, RMSNorm
- * recompute, in_proj and RMSNorm backward. */
+ * recompute, in_proj and RMSNorm backward (a recompute that `saved` makes
+ * unnecessary is an empty stage). */
 size_t mamba_layer_bwd_workspace_size(const ssm_layer_dims* dims);
 int mamba_layer_bwd(const void* x, const ssm_layer_weights* w, const ssm_layer_saved* saved,
                     const void* d_out, void* d_x, const ssm_layer_grads* grads, void* workspace,

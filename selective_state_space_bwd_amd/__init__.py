@@ -38,6 +38,8 @@ class ssm_layer_dims(ctypes.Structure):
 
 LAYER_WEIGHTS = ("norm_w", "W_in", "conv_w", "conv_b", "W_x", "W_dt", "b_dt", "A_log", "D", "W_out")
 LAYER_SAVED = ("xz", "xdbl", "delta", "y")
+# optional: the inputs of the out_proj, x_proj and in_proj products (ssm_layer_saved's last fields)
+LAYER_KEPT_INPUTS = ("gated", "u", "xn")
 LAYER_GRADS = tuple("d_" + k for k in LAYER_WEIGHTS)  # same order as ssm_layer_grads
 
 
@@ -46,11 +48,26 @@ class ssm_layer_weights(ctypes.Structure):
 
 
 class ssm_layer_saved(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_SAVED] + [("h_ckpt", ctypes.c_void_p)]
+    _fields_ = ([(name, ctypes.c_void_p) for name in LAYER_SAVED] + [("h_ckpt", ctypes.c_void_p)]
+                + [(name, ctypes.c_void_p) for name in LAYER_KEPT_INPUTS])
 
 
 def _saved_struct(saved: dict) -> ssm_layer_saved:
-    return ssm_layer_saved(*[ctypes.c_void_p(saved[k].data_ptr()) for k in LAYER_SAVED], _ptr(saved.get("h_ckpt")))
+    return ssm_layer_saved(*[_ptr(saved.get(k)) for k in LAYER_SAVED], _ptr(saved.get("h_ckpt")),
+                           *[_ptr(saved.get(k)) for k in LAYER_KEPT_INPUTS])
+
+
+def _new_saved(B_, T_, dims, device, keep_gemm_inputs: bool) -> dict:
+    """The saved activations a layer forward writes: {xz, xdbl, delta, y}, or with ``keep_gemm_inputs``
+    {xz, xdbl, delta, gated, u, xn} (y is then not needed: only the gate recompute reads it)."""
+    di, R2 = dims.d_inner, dims.dt_rank + 2 * dims.d_state
+    e = lambda *shp: torch.empty(shp, dtype=torch.bfloat16, device=device)
+    saved = {"xz": e(B_, T_, 2 * di), "xdbl": e(B_, T_, R2), "delta": e(B_, T_, di)}
+    if keep_gemm_inputs:
+        saved.update(gated=e(B_, T_, di), u=e(B_, T_, di), xn=e(B_, T_, dims.d_model))
+    else:
+        saved["y"] = e(B_, T_, di)
+    return saved
 
 
 def _scan_states(batch, seqlen, d_state, d_inner, device):
@@ -536,17 +553,15 @@ def _layer_weights(weights: dict, dims: ssm_layer_dims):
 
 
 def mamba_layer_fwd(x, weights: dict, *, eps: float = 1e-5, seg_len: int = 0, keep_scan_states: bool = False,
-                    workspace=None):
+                    keep_gemm_inputs: bool = False, workspace=None):
     """Layer forward on bf16 activations: returns (out, saved) with saved = {xz, xdbl, delta, y}
-    (and h_ckpt, the scan's chunk states, with ``keep_scan_states``: the backward then skips rebuilding them)."""
+    (and h_ckpt, the scan's chunk states, with ``keep_scan_states``: the backward then skips rebuilding them;
+    with ``keep_gemm_inputs``, gated, u and xn in place of y: the backward then skips recomputing them)."""
     _need(x.dtype == torch.bfloat16 and x.dim() == 3 and x.is_contiguous(), "x must be contiguous bf16 [B, T, d_model]")
     dims = layer_dims(x, weights, eps=eps, seg_len=seg_len)
     w = _layer_weights(weights, dims)
-    B_, T_, di, R2 = dims.batch, dims.seqlen, dims.d_inner, dims.dt_rank + 2 * dims.d_state
-    saved = {"xz": torch.empty((B_, T_, 2 * di), dtype=torch.bfloat16, device=x.device),
-             "xdbl": torch.empty((B_, T_, R2), dtype=torch.bfloat16, device=x.device),
-             "delta": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=x.device),
-             "y": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=x.device)}
+    B_, T_, di = dims.batch, dims.seqlen, dims.d_inner
+    saved = _new_saved(B_, T_, dims, x.device, keep_gemm_inputs)
     if keep_scan_states:
         saved["h_ckpt"] = _scan_states(B_, T_, dims.d_state, di, x.device)
     out = torch.empty_like(x)
@@ -571,12 +586,7 @@ def mamba_layer_bwd(x, weights: dict, saved: dict, d_out, *, eps: float = 1e-5, 
     _need(d_out.shape == x.shape and d_out.dtype == x.dtype and d_out.is_contiguous(), "d_out must match x")
     dims = layer_dims(x, weights, eps=eps, seg_len=seg_len)
     w = _layer_weights(weights, dims)
-    B_, T_, di, R2 = dims.batch, dims.seqlen, dims.d_inner, dims.dt_rank + 2 * dims.d_state
-    want = {"xz": (B_, T_, 2 * di), "xdbl": (B_, T_, R2), "delta": (B_, T_, di), "y": (B_, T_, di)}
-    for k, shp in want.items():
-        t = saved[k]
-        _need(tuple(t.shape) == shp and t.dtype == torch.bfloat16 and t.is_contiguous(), f"saved {k} must be {shp}")
-    _check_scan_states(saved, dims)
+    _check_saved(saved, dims)
     sv = _saved_struct(saved)
     o = dict(out or {})
     _need(not accumulate or all(k in o for k in LAYER_GRADS), "accumulate needs every gradient buffer in out")
@@ -617,6 +627,22 @@ def backbone_dims(inp, W_ip, layers: list, *, eps: float = 1e-5, seg_len: int = 
                              SSM_KEEP_ALL if keep == "all" else SSM_KEEP_INPUTS)
 
 
+def _check_saved(saved: dict, dims: ssm_layer_dims):
+    """Shapes of a layer's saved activations: xz, xdbl, delta always; y unless gated is kept; gated, u, xn
+    and h_ckpt when present."""
+    B_, T_, di, R2 = dims.batch, dims.seqlen, dims.d_inner, dims.dt_rank + 2 * dims.d_state
+    want = {"xz": (B_, T_, 2 * di), "xdbl": (B_, T_, R2), "delta": (B_, T_, di), "y": (B_, T_, di),
+            "gated": (B_, T_, di), "u": (B_, T_, di), "xn": (B_, T_, dims.d_model)}
+    _need(saved.get("y") is not None or saved.get("gated") is not None, "saved needs y or gated")
+    for k, shp in want.items():
+        t = saved.get(k)
+        if t is None:
+            _need(k not in ("xz", "xdbl", "delta"), f"saved {k} is required")
+            continue
+        _need(tuple(t.shape) == shp and t.dtype == torch.bfloat16 and t.is_contiguous(), f"saved {k} must be {shp}")
+    _check_scan_states(saved, dims)
+
+
 def _check_scan_states(saved: dict, dims: ssm_layer_dims):
     h = saved.get("h_ckpt")
     if h is not None:
@@ -632,27 +658,27 @@ def _backbone_arrays(bd, layers, xs, saved):
     if saved is None:
         return W, X, None
     for sv in saved:
-        _check_scan_states(sv, bd.layer)
+        _check_saved(sv, bd.layer)
     S = (ssm_layer_saved * L)(*[_saved_struct(sv) for sv in saved])
     return W, X, S
 
 
 def mamba_backbone_fwd(inp, W_ip, b_ip, norm_f_w, layers: list, *, eps: float = 1e-5, seg_len: int = 0,
-                       keep: str = "all", keep_scan_states: bool = False, workspace=None):
+                       keep: str = "all", keep_scan_states: bool = False, keep_gemm_inputs: bool = False,
+                       workspace=None):
     """Backbone forward on bf16 activations: returns (out, kept) with kept = {"xs": [n_layers + 1 tensors],
-    "saved": [per-layer {xz, xdbl, delta, y}] (None with keep="inputs"), "keep": keep}, what the backward reads."""
+    "saved": [per-layer {xz, xdbl, delta, y}] (None with keep="inputs"), "keep": keep}, what the backward reads.
+    ``keep_scan_states`` and ``keep_gemm_inputs`` add to every layer's saved set as in mamba_layer_fwd."""
     _need(inp.dtype == torch.bfloat16 and inp.dim() == 3 and inp.is_contiguous(), "inp must be contiguous bf16")
     _need(W_ip.dtype == torch.bfloat16 and W_ip.is_contiguous() and W_ip.shape[1] == inp.shape[2], "W_ip [d_model, in]")
-    _need(not (keep == "inputs" and keep_scan_states), "scan states are kept only with keep=\"all\"")
+    _need(keep == "all" or not (keep_scan_states or keep_gemm_inputs),
+          "scan states and product inputs are kept only with keep=\"all\"")
     bd = backbone_dims(inp, W_ip, layers, eps=eps, seg_len=seg_len, keep=keep)
     d = bd.layer
     dev = inp.device
-    B_, T_, dm, di, R2 = d.batch, d.seqlen, d.d_model, d.d_inner, d.dt_rank + 2 * d.d_state
+    B_, T_, dm, di = d.batch, d.seqlen, d.d_model, d.d_inner
     xs = [torch.empty((B_, T_, dm), dtype=torch.bfloat16, device=dev) for _ in range(bd.n_layers + 1)]
-    saved = [{"xz": torch.empty((B_, T_, 2 * di), dtype=torch.bfloat16, device=dev),
-              "xdbl": torch.empty((B_, T_, R2), dtype=torch.bfloat16, device=dev),
-              "delta": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=dev),
-              "y": torch.empty((B_, T_, di), dtype=torch.bfloat16, device=dev)} for _ in range(bd.n_layers)]
+    saved = [_new_saved(B_, T_, d, dev, keep_gemm_inputs) for _ in range(bd.n_layers)]
     if keep_scan_states:
         for sv in saved:
             sv["h_ckpt"] = _scan_states(B_, T_, d.d_state, di, dev)

@@ -72,10 +72,12 @@ int check_weights(const ssm_layer_weights* w) {
 }
 
 int check_saved(const ssm_layer_saved* s) {
-  if (!s || !s->xz || !s->xdbl || !s->delta || !s->y) return fail(SSM_ERR_INVALID_ARG, "a saved activation is null");
-  if (!aligned16(s->xz) || !aligned16(s->xdbl) || !aligned16(s->delta) || !aligned16(s->y) ||
-      (s->h_ckpt && !aligned16(s->h_ckpt)))
-    return fail(SSM_ERR_UNSUPPORTED, "activations must be 16-byte aligned");
+  if (!s || !s->xz || !s->xdbl || !s->delta || (!s->y && !s->gated))
+    return fail(SSM_ERR_INVALID_ARG, "a saved activation is null (y may be null only when gated is given)");
+  const void* opt[] = {s->y, s->h_ckpt, s->gated, s->u, s->xn};
+  bool ok = aligned16(s->xz) && aligned16(s->xdbl) && aligned16(s->delta);
+  for (const void* p : opt) ok = ok && (!p || aligned16(p));
+  if (!ok) return fail(SSM_ERR_UNSUPPORTED, "activations must be 16-byte aligned");
   return SSM_OK;
 }
 
@@ -189,25 +191,29 @@ extern "C" int mamba_layer_fwd(const void* x, const ssm_layer_weights* w, void* 
   bf16* xz = static_cast<bf16*>(saved->xz);
   bf16* xdbl = static_cast<bf16*>(saved->xdbl);
   bf16* delta = static_cast<bf16*>(saved->delta);
+  // the products' inputs go to the caller's buffers when it keeps them, else to the workspace
+  bf16* xn = saved->xn ? static_cast<bf16*>(saved->xn) : b.xn;
+  bf16* u = saved->u ? static_cast<bf16*>(saved->u) : b.u;
+  bf16* gated = saved->gated ? static_cast<bf16*>(saved->gated) : b.gated;
   // every product's arguments are checked before the first launch
-  TRY(gemm_check(b.xn, dm, w->W_in, dm, xz, (int)M, 2 * di, dm, b.scratch_bytes, b.scratch));
-  TRY(gemm_check(b.u, di, w->W_x, di, xdbl, (int)M, R2, di, b.scratch_bytes, b.scratch));
+  TRY(gemm_check(xn, dm, w->W_in, dm, xz, (int)M, 2 * di, dm, b.scratch_bytes, b.scratch));
+  TRY(gemm_check(u, di, w->W_x, di, xdbl, (int)M, R2, di, b.scratch_bytes, b.scratch));
   TRY(gemm_check(xdbl, R2, w->W_dt, R, delta, (int)M, di, R, b.scratch_bytes, b.scratch));
-  TRY(gemm_check(b.gated, di, w->W_out, di, out, (int)M, dm, di, b.scratch_bytes, b.scratch));
+  TRY(gemm_check(gated, di, w->W_out, di, out, (int)M, dm, di, b.scratch_bytes, b.scratch));
 
-  launch_rmsnorm_fwd(static_cast<const bf16*>(x), w->norm_w, b.xn, M, dm, d.eps, st);
-  gemm_bf16(b.xn, true, dm, w->W_in, true, dm, xz, 2 * di, SSM_BF16, (int)M, 2 * di, dm, 0, b.scratch, st);
-  launch_conv_silu_fwd(xz, 2 * di, w->conv_w, w->conv_b, b.u, di, d.batch, d.seqlen, di, d.d_conv, st);
-  gemm_bf16(b.u, true, di, w->W_x, true, di, xdbl, R2, SSM_BF16, (int)M, R2, di, 0, b.scratch, st);
+  launch_rmsnorm_fwd(static_cast<const bf16*>(x), w->norm_w, xn, M, dm, d.eps, st);
+  gemm_bf16(xn, true, dm, w->W_in, true, dm, xz, 2 * di, SSM_BF16, (int)M, 2 * di, dm, 0, b.scratch, st);
+  launch_conv_silu_fwd(xz, 2 * di, w->conv_w, w->conv_b, u, di, d.batch, d.seqlen, di, d.d_conv, st);
+  gemm_bf16(u, true, di, w->W_x, true, di, xdbl, R2, SSM_BF16, (int)M, R2, di, 0, b.scratch, st);
   gemm_bf16(xdbl, true, R2, w->W_dt, true, R, delta, di, SSM_BF16, (int)M, di, R, 0, b.scratch, st);
   launch_bias_softplus(delta, w->b_dt, M, di, st);
   const ssm_dims sd = scan_dims_of(d);
-  TRY(ssm_scan_fwd(b.u, delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, saved->y, b.gated, saved->h_ckpt,
+  TRY(ssm_scan_fwd(u, delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, saved->y, gated, saved->h_ckpt,
                    saved->h_ckpt ? 8 : 0, b.scratch, b.scratch_bytes, &sd, SSM_BF16, stream));
   // residual: out = x, then out += gated W_out^T
   if (hipMemcpyAsync(out, x, (size_t)M * dm * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
     return fail(SSM_ERR_LAUNCH, "residual copy failed");
-  gemm_bf16(b.gated, true, di, w->W_out, true, di, out, dm, SSM_BF16, (int)M, dm, di, 1, b.scratch, st);
+  gemm_bf16(gated, true, di, w->W_out, true, di, out, dm, SSM_BF16, (int)M, dm, di, 1, b.scratch, st);
   return check_launch("mamba_layer_fwd");
 }
 
@@ -244,24 +250,28 @@ extern "C" int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, 
   const ssm_dims sd = scan_dims_of(d);
   void* sc = b.scratch;
   const size_t scb = b.scratch_bytes;
+  // the products' inputs: kept by the forward, or recomputed into the workspace below
+  const bf16* gated = saved->gated ? static_cast<const bf16*>(saved->gated) : b.gated;
+  const bf16* u = saved->u ? static_cast<const bf16*>(saved->u) : b.u;
+  const bf16* xn = saved->xn ? static_cast<const bf16*>(saved->xn) : b.xn;
 
   mark(ev, 0, st);
-  launch_gate_fwd(static_cast<const bf16*>(saved->y), xz + di, 2 * di, b.gated, M, di, st);
+  if (!saved->gated) launch_gate_fwd(static_cast<const bf16*>(saved->y), xz + di, 2 * di, b.gated, M, di, st);
   mark(ev, 1, st);
   // B1: out = gated W_out^T (+ x)
   const int acc = g->accumulate ? SSM_BWD_ACCUMULATE : 0;
-  TRY(linear_bwd(b.gated, di, w->W_out, d_out, dm, b.d_gated, di, acc, g->d_W_out, nullptr, M, di, dm, sc, scb,
+  TRY(linear_bwd(gated, di, w->W_out, d_out, dm, b.d_gated, di, acc, g->d_W_out, nullptr, M, di, dm, sc, scb,
                  SSM_BF16, stream));
   mark(ev, 2, st);
-  launch_conv_silu_fwd(xz, 2 * di, w->conv_w, w->conv_b, b.u, di, d.batch, d.seqlen, di, d.d_conv, st);
+  if (!saved->u) launch_conv_silu_fwd(xz, 2 * di, w->conv_w, w->conv_b, b.u, di, d.batch, d.seqlen, di, d.d_conv, st);
   mark(ev, 3, st);
   // B2 + B3 (+ softplus backward): d_z lands in the second half of d_xz, d_B | d_C in d_xdbl
   if (saved->h_ckpt)
-    TRY(ssm_scan_bwd_ckpt(b.u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated,
+    TRY(ssm_scan_bwd_ckpt(u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated,
                           saved->h_ckpt, b.d_u, b.d_raw, g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D,
                           b.d_xz + di, SSM_BWD_SOFTPLUS | acc, sc, scb, &sd, SSM_BF16, stream, nullptr));
   else
-    TRY(ssm_scan_bwd(b.u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated, b.d_u, b.d_raw,
+    TRY(ssm_scan_bwd(u, saved->delta, w->A_log, xdbl + R, xdbl + R + N, w->D, xz + di, b.d_gated, b.d_u, b.d_raw,
                      g->d_A_log, b.d_xdbl + R, b.d_xdbl + R + N, g->d_D, b.d_xz + di, SSM_BWD_SOFTPLUS | acc, sc, scb,
                      &sd, SSM_BF16, stream));
   mark(ev, 4, st);
@@ -270,7 +280,7 @@ extern "C" int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, 
                  SSM_BF16, stream));
   mark(ev, 5, st);
   // B5: xdbl = u W_x^T; d_u collects the scan's and this product's parts
-  TRY(linear_bwd(b.u, di, w->W_x, b.d_xdbl, R2, b.d_u, di, SSM_BWD_ACCUMULATE_DX | acc, g->d_W_x, nullptr, M, di,
+  TRY(linear_bwd(u, di, w->W_x, b.d_xdbl, R2, b.d_u, di, SSM_BWD_ACCUMULATE_DX | acc, g->d_W_x, nullptr, M, di,
                  R2, sc, scb, SSM_BF16,
                  stream));
   mark(ev, 6, st);
@@ -278,10 +288,10 @@ extern "C" int mamba_layer_bwd_timed(const void* x, const ssm_layer_weights* w, 
   TRY(conv1d_bwd(xz, w->conv_w, w->conv_b, b.d_u, b.d_xz, g->d_conv_w, g->d_conv_b, d.batch, d.seqlen, di,
                  d.d_conv, 2 * di, di, 2 * di, acc, sc, scb, SSM_BF16, stream));
   mark(ev, 7, st);
-  launch_rmsnorm_fwd(static_cast<const bf16*>(x), w->norm_w, b.xn, M, dm, d.eps, st);
+  if (!saved->xn) launch_rmsnorm_fwd(static_cast<const bf16*>(x), w->norm_w, b.xn, M, dm, d.eps, st);
   mark(ev, 8, st);
   // B7: xz = xn W_in^T
-  TRY(linear_bwd(b.xn, dm, w->W_in, b.d_xz, 2 * di, b.d_xn, dm, acc, g->d_W_in, nullptr, M, dm, 2 * di, sc, scb,
+  TRY(linear_bwd(xn, dm, w->W_in, b.d_xz, 2 * di, b.d_xn, dm, acc, g->d_W_in, nullptr, M, dm, 2 * di, sc, scb,
                  SSM_BF16, stream));
   mark(ev, 9, st);
   // B8: RMSNorm backward plus the residual path

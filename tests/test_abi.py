@@ -233,6 +233,12 @@ def test_layer_entry_points_validate():
     assert bwd(_layer_dims(seqlen=1 << 20, d_inner=4096)) == ssm.SSM_ERR_UNSUPPORTED   # rows past 2^32 elements
     misaligned = ssm.ssm_layer_saved(FAKE.value, 0x1008, FAKE.value, FAKE.value)
     assert bwd(_layer_dims(), sv=misaligned) == ssm.SSM_ERR_UNSUPPORTED
+    # y may be null only when the gate's output is kept; kept inputs are alignment-checked too
+    assert bwd(_layer_dims(), sv=ssm.ssm_layer_saved(FAKE.value, FAKE.value, FAKE.value, None)) == ssm.SSM_ERR_INVALID_ARG
+    kept = ssm.ssm_layer_saved(FAKE.value, FAKE.value, FAKE.value, None, None, FAKE.value, FAKE.value, FAKE.value)
+    assert bwd(_layer_dims(), sv=kept, ws_bytes=1024) == ssm.SSM_ERR_WORKSPACE   # saved accepted, workspace not
+    kept_bad = ssm.ssm_layer_saved(FAKE.value, FAKE.value, FAKE.value, None, None, FAKE.value, 0x1004, FAKE.value)
+    assert bwd(_layer_dims(), sv=kept_bad) == ssm.SSM_ERR_UNSUPPORTED
     assert L.mamba_layer_fwd(FAKE, ctypes.byref(w), FAKE, ctypes.byref(sv), FAKE, 16, ctypes.byref(_layer_dims()),
                              None) == ssm.SSM_ERR_WORKSPACE
 

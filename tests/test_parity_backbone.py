@@ -92,15 +92,16 @@ def test_backbone_bwd_from_oracle_activations(shape):
     _check(got, ref, "backward", TOL)
 
 
-@pytest.mark.parametrize("keep", [False, True], ids=["rebuilt-states", "kept-states"])
+@pytest.mark.parametrize("keep", [(False, False), (True, False), (False, True)],
+                         ids=["rebuilt-states", "kept-states", "kept-gemm-inputs"])
 @pytest.mark.parametrize("shape", SHAPES[:1])
 def test_backbone_end_to_end(shape, keep):
     L, Bt, T, mid, dm, di, N, R, K = shape
     bp, layers = _inputs(shape, seed=3 + sum(shape))
     tb, tl = _dev(bp, layers)
-    print(f"case: backbone fwd + bwd {shape} keep_scan_states {keep}", flush=True)
+    print(f"case: backbone fwd + bwd {shape} keep_scan_states, keep_gemm_inputs {keep}", flush=True)
     out, kept = _ssm().mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl,
-                                          keep_scan_states=keep)
+                                          keep_scan_states=keep[0], keep_gemm_inputs=keep[1])
     g = _ssm().mamba_backbone_bwd(tb["inp"], tb["W_ip"], tb["norm_f_w"], tl, kept, tb["d_out"])
     torch.cuda.synchronize()
     f = orc.backbone_forward(bp, layers, N, R)
@@ -182,3 +183,6 @@ def test_backbone_keep_inputs_accumulates_like_keep_all():
     with pytest.raises(Exception):
         ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, keep="inputs",
                                keep_scan_states=True)
+    with pytest.raises(Exception):
+        ssm.mamba_backbone_fwd(tb["inp"], tb["W_ip"], tb["b_ip"], tb["norm_f_w"], tl, keep="inputs",
+                               keep_gemm_inputs=True)

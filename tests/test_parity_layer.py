@@ -118,6 +118,34 @@ def test_layer_end_to_end_with_scan_states(shape):
     _check({k: _np(v) for k, v in g.items()}, {k: _np(v) for k, v in h.items()}, GRADS, "vs rebuilt states", tol=1e-2)
 
 
+@pytest.mark.parametrize("shape", SHAPES[:2])
+def test_layer_end_to_end_keeping_gemm_inputs(shape):
+    """The forward keeps the products' inputs (gated, u, xn: the page's gated, u and
+    post_norm) in place of y, and the backward reads them instead of recomputing them:
+    the kept values against the oracle's activations, the gradients at the oracle's bar
+    and close to the recomputing backward (whose gate is rebuilt from the bf16-rounded y,
+    where the kept gated comes from the scan's float y: only bf16 rounding differs), and
+    the forward's output bitwise equal to the forward that keeps y."""
+    Bt, T, dm, di, N, R, K = shape
+    p = _inputs(shape, seed=9 + sum(shape))
+    t = _dev(p)
+    print(f"case: layer fwd (keeping the products' inputs) + bwd {shape}", flush=True)
+    out, saved = _ssm().mamba_layer_fwd(t["x"], _weights(t), seg_len=16, keep_gemm_inputs=True)
+    assert "y" not in saved and all(k in saved for k in ("gated", "u", "xn"))
+    g = _ssm().mamba_layer_bwd(t["x"], _weights(t), saved, t["d_out"], seg_len=16)
+    out2, saved2 = _ssm().mamba_layer_fwd(t["x"], _weights(t), seg_len=16)
+    h = _ssm().mamba_layer_bwd(t["x"], _weights(t), saved2, t["d_out"], seg_len=16)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    act = orc.layer_forward(p, N, R)
+    keys = ("xz", "xdbl", "delta", "gated", "u", "xn")
+    _check({k: _np(saved[k]) for k in keys}, act, keys, "kept forward values")
+    ref = orc.layer_bwd(p, p["d_out"], N, R)
+    _check({k: _np(v) for k, v in g.items()}, ref, GRADS, "backward from kept inputs", tol=TOL_END_TO_END)
+    _check({k: _np(v) for k, v in g.items()}, {k: _np(v) for k, v in h.items()}, GRADS, "vs recomputed inputs",
+           tol=1e-2)
+
+
 @pytest.mark.parametrize("variant", ["default", "perturbed"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_layer_bwd_from_oracle_activations(shape, variant):
