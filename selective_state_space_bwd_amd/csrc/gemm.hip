@@ -1072,6 +1072,7 @@ struct PairPick {
   bool big;
   bool dw_first;
 };
+constexpr double kSplitSumLaunch = 20e-6;
 
 PairPick pair_dw_splits(int m, int K, int N) {
   const bool big = big_fits(m, K, N) && big_fits(N, K, m);
@@ -1096,7 +1097,11 @@ PairPick pair_dw_splits(int m, int K, int N) {
                                    : pair_makespan(slots, nt2 * used, d2, nb1, d1);
       if (ms < 0) continue;
       double t = ms * kstep_s;
-      if (used > 1) t += 2.0 * used * (double)N * K * 4.0 / 3e12;
+      // a k split adds its partials' traffic and the split-k sum's own launch,
+      // which starts only after the pair's last block (20 us in the model's
+      // units, fitted to the measured order of the layer's in_proj and out_proj
+      // plans: in_proj 0.529 ms unsplit against 0.558 ms with two dW splits)
+      if (used > 1) t += 2.0 * used * (double)N * K * 4.0 / 3e12 + kSplitSumLaunch;
       if (best_t < 0 || t < best_t) {
         best_t = t;
         best = PairPick{sp, big, order == 1};
