@@ -5,7 +5,7 @@
 // h_curr, each [T, d_inner*d_state]).  Here nothing per step and per state
 // goes to memory.  One lane owns one channel (b, d) and keeps its d_state
 // states in registers; B_t and C_t are the same for every lane of a block and
-// sit in scalar registers.  Time is cut into segments that run in parallel,
+// are read from scalar registers or a block-wide LDS copy.  Time is cut into segments that run in parallel,
 // and each segment into chunks of kChunk steps:
 //
 //   1. summary  (per segment, forward in t): the segment's local states from a
@@ -22,7 +22,9 @@
 //      d_C (sums over channels) are reduced inside the wave with permlane swaps
 //      and DPP, across the block's waves in LDS, and across blocks as
 //      fixed-order partials; d_A_log and d_D (sums over batch and time) are kept
-//      per lane over the segment and written as partials.
+//      per lane over the segment and written as partials.  Float storage runs
+//      it one channel per lane; bf16 storage on lane pairs that share two
+//      channels, each lane holding half the states of both (3').
 //   4. finalize: fixed-order sums of the partials.
 // Nothing uses atomics, so results are bitwise repeatable.
 #include <stdarg.h>
