@@ -679,8 +679,12 @@ __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
     float* __restrict__ part_bc, float* __restrict__ part_a, ScanShape sh) {
   static_assert(sizeof(T) == 2, "the lane-pair sweep is the bf16 path");
   constexpr int NH = NS / 2;
-  constexpr int kReg = ChunkTile<NS>::kRegSteps;
-  constexpr int kLds = ChunkTile<NS>::kLdsSteps;
+  // with d_state 16 one more step of a_t h_{t-1} stays in registers than in the
+  // float sweep (the half-row B | C leave room: 249 VGPRs, no spills; measured
+  // 0.5-0.8 % faster); with given states it would spill, so that variant keeps
+  // the float sweep's split
+  constexpr int kReg = ChunkTile<NS>::kRegSteps + (NS == 16 && !GCK ? 1 : 0);
+  constexpr int kLds = kChunk - kReg;
   static_assert(NS % 4 == 0, "a*h rows move through LDS as float4");
   __shared__ float red[2][kBlock / kWave][kChunk][2 * NS];
   __shared__ float4 lds_ah[kLds > 0 ? kLds : 1][NS / 4][kBlock];
