@@ -279,13 +279,14 @@ def timed(step, n_events: int, steps: int, warmup: int):
     microseconds of idle GPU, so only STAGE_SAMPLES evenly spaced steps of the
     timed region carry the events; the others run as a caller would."""
     import torch
-    for _ in range(warmup):
-        step(None)
-    torch.cuda.synchronize()
+    # the events are created before the warm-up, so that the GPU goes from the warm-up steps to the
+    # timed ones with no host-side work between them but the synchronisation
     hip = HipEvents()
     every = max(1, steps // STAGE_SAMPLES)
     sampled = [k for k in range(steps) if k % every == every - 1][:STAGE_SAMPLES]
     evs = {k: hip.create(n_events) for k in sampled}
+    for _ in range(warmup):
+        step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
