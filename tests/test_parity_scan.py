@@ -11,7 +11,7 @@ import torch
 
 from oracle import layer as orc_layer
 from oracle import ssm as orc
-from synth import CONFIGS, scan_inputs
+from synth import CONFIGS, round_bf16, scan_inputs
 from tests._util import SCAN_OUTPUTS, norm_err
 
 pytestmark = pytest.mark.gpu
@@ -150,6 +150,24 @@ def test_softplus_epilogue():
     g = gpu_bwd(p, "f32", softplus_epilogue=True)
     assert norm_err(g["d_delta"], want) < TOL["f32"]
     _check(g, r, TOL["f32"], keys=("d_u", "d_A_log", "d_B", "d_C", "d_D", "d_z"), label="softplus")
+
+
+def test_softplus_epilogue_bf16():
+    """The bf16 sweep (lane pairs) with the softplus epilogue.  delta is stored as the bf16-rounded
+    softplus of raw, so the oracle's softplus derivative is taken at the raw value that maps to the
+    rounded delta.  d_inner 67 is odd: the last lane pair has an idle partner."""
+    nb, T, di, N = 2, 100, 67, 16
+    p = scan_inputs(nb, T, di, N, "bf16", seed=22)
+    rng = np.random.default_rng(5)
+    raw = rng.standard_normal((nb, T, di)) * 3.0
+    raw[0, :5, :3] = 25.0                         # above the threshold: pass-through
+    p["delta"] = round_bf16(orc_layer.softplus_fwd(raw)).astype(np.float32)
+    r = oracle_bwd(p)
+    want = orc_layer.softplus_bwd(orc_layer.softplus_inv(p["delta"]), r["d_delta"])
+    print("case: softplus epilogue bf16 B2 T100 Di67 N16", flush=True)
+    g = gpu_bwd(p, "bf16", softplus_epilogue=True)
+    assert norm_err(g["d_delta"], want) < TOL["bf16"]
+    _check(g, r, TOL["bf16"], keys=("d_u", "d_A_log", "d_B", "d_C", "d_D", "d_z"), label="softplus bf16")
 
 
 def test_strided_B_C_inside_xdbl_rows():
