@@ -221,6 +221,14 @@ def test_linear_fwd(M, K, N):
     assert norm_err(_np(Y), orc.linear_fwd(X, W)) < TOL_BF16
 
 
+# rows of dX checked at the layer's size: the last nine 256-row tiles in full
+# (the blocks the paired launch hands out last) plus a random sample of the
+# others
+def _full_size_rows(M, n_random, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.union1d(rng.choice(M - 2304, n_random, replace=False), np.arange(M - 2304, M))
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("which", ["in_proj", "out_proj"])
 def test_linear_bwd_full_layer_sampled(which):
@@ -233,10 +241,37 @@ def test_linear_bwd_full_layer_sampled(which):
     dX, dW, db = _ssm().linear_bwd(_bf(X), _bf(W), _bf(dY), need_db=True)
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(M, 64, replace=False))
+    rows = _full_size_rows(M, 64)
     cols = np.sort(rng.choice(K, 16, replace=False))
     rx, _, _ = orc.linear_bwd(X[rows], W, dY[rows])
     _, rw, rb = orc.linear_bwd(X[:, cols], W[:, cols], dY)
     assert norm_err(_np(dX[rows]), rx) < TOL_BF16
     assert norm_err(_np(dW[:, cols]), rw) < TOL_F32
     assert norm_err(_np(db), rb) < TOL_F32
+
+
+@pytest.mark.timeout(600)
+def test_linear_bwd_full_layer_accumulate_dx():
+    """in_proj at full size with dX added into a column slice of a wider buffer
+    and dW accumulated: every checked row adds to its old values, and the
+    columns outside the slice keep theirs."""
+    M, K, N = 8 * 2048, 1536, 6144
+    X, W, dY = _mats(M, K, N, seed=77)
+    rng = np.random.default_rng(7)
+    base = round_bf16(rng.standard_normal((M, K + 256)))
+    w0 = rng.standard_normal((N, K)).astype(np.float32)
+    print(f"case: linear_bwd full-size in_proj M {M} K {K} N {N}, dX accumulated into a view", flush=True)
+    dXbuf = _bf(base)
+    dWg = torch.from_numpy(w0).to(DEV)
+    _ssm().linear_bwd(_bf(X), _bf(W), _bf(dY), dX=dXbuf[:, 128:128 + K], accumulate_dx=True, dW=dWg,
+                      accumulate=True)
+    torch.cuda.synchronize()
+    rows = _full_size_rows(M, 32, seed=1)
+    cols = np.sort(rng.choice(K, 8, replace=False))
+    rx, _, _ = orc.linear_bwd(X[rows], W, dY[rows])
+    _, rw, _ = orc.linear_bwd(X[:, cols], W[:, cols], dY)
+    got = _np(dXbuf)[rows]
+    assert norm_err(got[:, 128:128 + K], base[rows, 128:128 + K] + rx) < TOL_BF16
+    assert np.array_equal(got[:, :128], base[rows, :128])
+    assert np.array_equal(got[:, 128 + K:], base[rows, 128 + K:])
+    assert norm_err(_np(dWg)[:, cols], w0[:, cols] + rw) < TOL_F32
