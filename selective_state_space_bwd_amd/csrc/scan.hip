@@ -395,20 +395,24 @@ struct ChunkTile {
   static constexpr int kLdsSteps = kChunk - kRegSteps;
 };
 
-// The float sweep (bf16 storage takes the lane-pair sweep below, measured 9 %
-// faster there and 3 % slower here); two waves per SIMD.
+// The float sweep, and the bf16 one when the chunk states are given.  bf16
+// rebuilding its own states takes the lane-pair sweep below: measured 9 %
+// faster there (1.19 against 1.30 ms on batch 2, 8192 steps, 5120 channels),
+// while from given states the lane pairs run 4-6 % slower (1.09 against 1.05
+// ms on that shape, 0.67 against 0.63 ms on batch 8, 2048 steps, 3072
+// channels) and on float storage 3 % slower.  Two waves per SIMD.
 // GCK: `ckpt` holds the exact state before every chunk (the forward's
 // checkpoints) instead of the local ones of the summary pass; seg_h, ckpt_sd
 // are then unused.
 template <typename T, int NS, bool SOFTPLUS, bool GCK>
-__global__ __launch_bounds__(kBlock, 2) void scan_bwd_main(
+__global__ __launch_bounds__(kBlock, sizeof(T) == 4 ? 2 : 1) void scan_bwd_main(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
     const T* __restrict__ z, const T* __restrict__ dout, T* __restrict__ d_u,
     T* __restrict__ d_delta, T* __restrict__ d_z, const float* __restrict__ ckpt,
     const float* __restrict__ ckpt_sd, const float* __restrict__ seg_h, const float* __restrict__ seg_g,
     float* __restrict__ part_bc, float* __restrict__ part_a, ScanShape sh) {
-  static_assert(sizeof(T) == 4, "the one-channel-per-lane sweep is the float path");
+  static_assert(sizeof(T) == 4 || GCK, "bf16 rebuilding its states takes the lane-pair sweep");
   constexpr int kLogNS = NS == 16 ? 4 : NS == 8 ? 3 : NS == 4 ? 2 : NS == 2 ? 1 : 0;
   constexpr int kRep = kWave / NS;  // lanes holding each reduced value
   constexpr int kReg = ChunkTile<NS>::kRegSteps;
@@ -669,7 +673,7 @@ __device__ __forceinline__ void bc_half(const float (&bcs)[kChunk][2 * NS], int 
   }
 }
 
-template <typename T, int NS, bool SOFTPLUS, bool GCK>
+template <typename T, int NS, bool SOFTPLUS>
 __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A_log,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dp,
@@ -680,10 +684,9 @@ __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
   static_assert(sizeof(T) == 2, "the lane-pair sweep is the bf16 path");
   constexpr int NH = NS / 2;
   // with d_state 16 one more step of a_t h_{t-1} stays in registers than in the
-  // float sweep (the half-row B | C leave room: 249 VGPRs, no spills; measured
-  // 0.5-0.8 % faster); with given states it would spill, so that variant keeps
-  // the float sweep's split
-  constexpr int kReg = ChunkTile<NS>::kRegSteps + (NS == 16 && !GCK ? 1 : 0);
+  // one-channel sweep (the half-row B | C leave room: 249 VGPRs, no spills;
+  // measured 0.5-0.8 % faster)
+  constexpr int kReg = ChunkTile<NS>::kRegSteps + (NS == 16 ? 1 : 0);
   constexpr int kLds = kChunk - kReg;
   static_assert(NS % 4 == 0, "a*h rows move through LDS as float4");
   __shared__ float red[2][kBlock / kWave][kChunk][2 * NS];
@@ -736,24 +739,13 @@ __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
         bc_element<T, NS>(Bb, Cb, sh.ld_bc, c_last * kChunk, min(kChunk, t1 - c_last * kChunk), tid);
   __syncthreads();
   // a chunk's loads: its per-step values of the lane's own channel (delta, u,
-  // z, d_out) and, when the states are given, its starting states.  With given
-  // states the next chunk's loads go out at the end of the current one.  Rows
-  // of a chunk sit at wave-uniform byte offsets from the chunk's first row.
+  // z, d_out), issued at the chunk's start.  Rows of a chunk sit at
+  // wave-uniform byte offsets from the chunk's first row.
   const uint32_t step_bytes = (uint32_t)(Di * sizeof(T)), zstep_bytes = (uint32_t)(sh.ld_z * sizeof(T));
   float dl[kChunk], uu[kChunk], zr[kChunk], gr[kChunk], dy[kChunk];
-  float hg[2][NH];
   const auto load_chunk = [&](int c) {
     const int tc = c * kChunk;
     const int nv = min(kChunk, t1 - tc);
-    if (GCK) {
-      const size_t cc = (size_t)b * sh.nchunk + c;
-      const BufRes rc = buf_res(ckpt + cc * NS * Di);
-#pragma unroll
-      for (int k = 0; k < NH; ++k) {
-        hg[0][k] = buf_ld<float>(rc, o0, k * row_bytes);
-        hg[1][k] = buf_ld<float>(rc, o1, k * row_bytes);
-      }
-    }
     const size_t rowc = row0 + tc;
     const BufRes rd = buf_res(delta + rowc * Di), ru = buf_res(u + rowc * Di), rg = buf_res(dout + rowc * Di);
     const BufRes rz = buf_res(z + rowc * sh.ld_z);
@@ -767,21 +759,14 @@ __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
       gr[j] = buf_ld<T>(rg, dc, jj * step_bytes);
     }
   };
-  if (GCK) load_chunk(c_last);
   for (int c = c_last; c >= c_first; --c) {
     const int tc = c * kChunk;
     const int nv = min(kChunk, t1 - tc);
     const int buf = c & 1;
     const float bc_next = c > c_first ? bc_element<T, NS>(Bb, Cb, sh.ld_bc, tc - kChunk, kChunk, tid) : 0.f;
-    // states before the chunk: given, or local checkpoint + decayed carry-in
+    // states before the chunk: local checkpoint + decayed carry-in
     float h[2][NH];
-    if (GCK) {
-#pragma unroll
-      for (int k = 0; k < NH; ++k) {
-        h[0][k] = hg[0][k];
-        h[1][k] = hg[1][k];
-      }
-    } else if (c == c_first) {
+    if (c == c_first) {
 #pragma unroll
       for (int k = 0; k < NH; ++k) {
         h[0][k] = (s == 0) ? 0.f : buf_ld<float>(rsh, o0, k * row_bytes);
@@ -800,7 +785,7 @@ __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
         h[1][k] = fmaf(fast_exp2(A2[1][k] * sd1), hin1, buf_ld<float>(rc, o1, k * row_bytes));
       }
     }
-    if (!GCK) load_chunk(c);
+    load_chunk(c);
     const BufRes rdz = buf_res(d_z + (row0 + tc) * sh.ld_z);
     const BufRes rdu = buf_res(d_u + (row0 + tc) * Di), rdd = buf_res(d_delta + (row0 + tc) * Di);
     // forward: rebuild the chunk's states, keep a_t h_{t-1}
@@ -903,7 +888,6 @@ __global__ __launch_bounds__(kBlock, 2) void scan_bwd_pair(
         *(pair_writer<NH>(lane) ? &red[buf][wave][j][n0 + pair_index<NH>(lane)] : &red_sink[tid]) = dB[0];
       }
     }
-    if (GCK && c > c_first) load_chunk(c - 1);
     // the buffer written here was last read before the previous chunk's barrier
     if (c > c_first && tid < kChunk * 2 * NS) (&bcs[buf ^ 1][0][0])[tid] = bc_next;
     __syncthreads();
@@ -1254,17 +1238,18 @@ int launch_bwd(const void* u, const void* delta, const float* A_log, const void*
                          w.seg_sd, sh);
   }
   mark(2);
-  // float sweeps one channel per lane, bf16 on lane pairs
+  // float sweeps one channel per lane, and so does bf16 from given states;
+  // bf16 rebuilding its states sweeps on lane pairs
 #define SSM_MAIN(SP, GCK)                                                                                        \
   do {                                                                                                           \
-    if constexpr (sizeof(T) == 4)                                                                                \
+    if constexpr (sizeof(T) == 4 || GCK)                                                                         \
       hipLaunchKernelGGL((scan_bwd_main<T, NS, SP, GCK>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz, \
                          tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),               \
                          GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);            \
     else                                                                                                         \
-      hipLaunchKernelGGL((scan_bwd_pair<T, NS, SP, GCK>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz, \
-                         tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z),               \
-                         GCK ? h_ckpt : w.ckpt, w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);            \
+      hipLaunchKernelGGL((scan_bwd_pair<T, NS, SP>), grid, dim3(kBlock), 0, st, tu, tdl, A_log, tB, tC, D, tz,    \
+                         tdo, static_cast<T*>(d_u), static_cast<T*>(d_delta), static_cast<T*>(d_z), w.ckpt,       \
+                         w.ckpt_sd, w.seg_h, w.seg_g, w.part_bc, w.part_a, sh);                                   \
   } while (0)
   if (h_ckpt) {
     if (flags & SSM_BWD_SOFTPLUS) SSM_MAIN(true, true);
