@@ -112,13 +112,38 @@ class HipEvents:
 KERNEL_SOURCES = {"scan_bwd_main": ("scan.hip", "common.hpp"), "ssm_scan_bwd": ("scan.hip", "common.hpp")}
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments, whitespace runs collapsed to one space: what the compiler sees."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # string or character literal, copied through its closing quote
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_digest(kernel: str) -> str:
-    """Digest of a kernel's sources: recorded counter totals are only valid for the code they came from."""
+    """Digest of a kernel's sources (code only: comments and layout do not count), so that recorded
+    counter totals are used only with the code they came from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_bwd_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -23,8 +23,9 @@
 //      and DPP, across the block's waves in LDS, and across blocks as
 //      fixed-order partials; d_A_log and d_D (sums over batch and time) are kept
 //      per lane over the segment and written as partials.  Float storage runs
-//      it one channel per lane; bf16 storage on lane pairs that share two
-//      channels, each lane holding half the states of both (3').
+//      it one channel per lane, and so does bf16 from given chunk states; bf16
+//      rebuilding its states runs on lane pairs that share two channels, each
+//      lane holding half the states of both (3').
 //   4. finalize: fixed-order sums of the partials.
 // Nothing uses atomics, so results are bitwise repeatable.
 #include <stdarg.h>

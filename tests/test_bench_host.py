@@ -37,6 +37,16 @@ def test_recorded_traffic_lines_parse():
         assert got == (int(m.group(3)) if m.group(4) == bench.source_digest(m.group(2)) else None)
 
 
+def test_source_digest_ignores_comments_and_layout():
+    """A comment or whitespace edit keeps the digest (the compiled code is the same); a code edit
+    changes it.  Comment markers inside string and character literals are code."""
+    src = 'int a = 1;  // note\n/* block */ const char* s = "x//y";\nchar q = \'"\';\n'
+    assert bench.code_text(src) == 'int a = 1; const char* s = "x//y"; char q = \'"\';'
+    assert bench.code_text(src) == bench.code_text(src.replace("// note", "// another note"))
+    assert bench.code_text(src) != bench.code_text(src.replace("1;", "2;"))
+    assert len(bench.source_digest("scan_bwd_main")) == 16
+
+
 def test_roofline_fields_follow_the_published_peaks():
     """The scan roofline: HBM bound against 8 TB/s from the algorithmic bytes and the kernel time;
     the arithmetic against 157.3 TFLOP/s (published fp32) and the 78.6 TFLOP/s non-packed ceiling."""
