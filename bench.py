@@ -502,7 +502,7 @@ LAYER_SAVED_KEPT = "xz, xdbl, delta and the products' inputs gated, u, xn (the p
 LAYER_SAVED_LEAN = "xz, xdbl, delta, y; the gate, conv + SiLU and RMSNorm forward recomputed in the backward"
 
 
-def measure_layer(args, cfg, steps, warmup, want_stats=True, keep_inputs=True):
+def measure_layer(args, cfg, steps, warmup, want_stats=True, keep_inputs=True, scan_states=None):
     import torch
 
     import selective_state_space_bwd_amd as ssm
@@ -517,7 +517,8 @@ def measure_layer(args, cfg, steps, warmup, want_stats=True, keep_inputs=True):
     # ROTATE copies of the input, the upstream gradient and the saved activations, used in turn
     xs = [t["x"]] + [t["x"].clone() for _ in range(ROTATE - 1)]
     gs = [t["d_out"]] + [t["d_out"].clone() for _ in range(ROTATE - 1)]
-    saves = [ssm.mamba_layer_fwd(x, W, seg_len=args.seg_len, keep_scan_states=args.ckpt,
+    keep_states = args.ckpt if scan_states is None else scan_states
+    saves = [ssm.mamba_layer_fwd(x, W, seg_len=args.seg_len, keep_scan_states=keep_states,
                                  keep_gemm_inputs=keep_inputs)[1] for x in xs]
     ws = torch.empty(ssm.mamba_layer_bwd_workspace_size(t["x"], W, seg_len=args.seg_len), dtype=torch.uint8,
                      device=dev)
@@ -583,6 +584,7 @@ def run_layer(args, cfg):
 def config_entry_layer(args, cfg, warmup):
     ms_step, st, stats = measure_layer(args, cfg, args.steps, warmup)
     lean_ms, lean_st, lean_stats = measure_layer(args, cfg, args.steps, warmup, keep_inputs=False)
+    ck_ms, ck_st, ck_stats = measure_layer(args, cfg, args.steps, warmup, scan_states=True)
     gemm_flops = layer_gemm_flops(cfg)
     med = stats["ms_median"]
     dom = max(st, key=st.get)
@@ -606,7 +608,12 @@ def config_entry_layer(args, cfg, warmup):
             "dominant_kernel": droof,
             "recompute_inputs": {"saved": LAYER_SAVED_LEAN, "ms_per_step": round(lean_ms, 4),
                                  **{k: lean_stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
-                                 "stages_ms": {k: round(v, 4) for k, v in lean_st.items()}}}
+                                 "stages_ms": {k: round(v, 4) for k, v in lean_st.items()}},
+            "chunk_states_kept": {"saved": LAYER_SAVED_KEPT + ", and the scan's state before every 8-step chunk "
+                                           "(written by the forward; the backward does not rebuild them)",
+                                  "ms_per_step": round(ck_ms, 4),
+                                  **{k: ck_stats[k] for k in ("ms_median", "ms_p10", "ms_p90")},
+                                  "stages_ms": {k: round(v, 4) for k, v in ck_st.items()}}}
 
 
 def config_entry_tiny(args, cfg, warmup, step=None):

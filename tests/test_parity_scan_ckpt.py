@@ -89,6 +89,7 @@ SHAPES = [
     (2, 130, 520, 8, "bf16", "default", 32),
     (1, 300, 70, 16, "bf16", "long_memory", 24),
     (2, 77, 129, 16, "bf16", "random_A", 0),
+    (2, 45, 67, 4, "bf16", "default", 16),
 ]
 
 
